@@ -1,0 +1,222 @@
+"""CPU oracle of the quantized MoE layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The GPU library never links or calls it, and it
+shares no code with the GPU path.  The arithmetic lives in ``oracle.c`` (plain
+single-threaded C, double precision); this module only marshals arguments.
+
+Pinned by ``tests/test_oracle_pins.py``: every function below has at least one
+pin that does not re-use the oracle's own formula (format tables from the OCP
+specifications, torch's float8 decode, brute-force sorts, closed forms,
+a dense fp64 reference on the tiny layer).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FMT_NVFP4 = 1
+FMT_Q6K = 2
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-fno-fast-math",
+               "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class OracleExperts(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("fmt_down", ctypes.c_int32),
+                ("gate_q", ctypes.c_void_p), ("gate_s", ctypes.c_void_p),
+                ("gate_ts", ctypes.c_void_p),
+                ("up_q", ctypes.c_void_p), ("up_s", ctypes.c_void_p),
+                ("up_ts", ctypes.c_void_p),
+                ("down_q", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
+                ("down_ts", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+        L.oracle_e2m1.restype = ctypes.c_double
+        L.oracle_e2m1.argtypes = [u32]
+        L.oracle_e4m3.restype = ctypes.c_double
+        L.oracle_e4m3.argtypes = [u32]
+        L.oracle_bf16.restype = ctypes.c_double
+        L.oracle_bf16.argtypes = [ctypes.c_uint16]
+        L.oracle_f16.restype = ctypes.c_double
+        L.oracle_f16.argtypes = [ctypes.c_uint16]
+        L.oracle_round_bf16.restype = ctypes.c_uint16
+        L.oracle_round_bf16.argtypes = [ctypes.c_double]
+        L.oracle_nvfp4_weight.restype = ctypes.c_double
+        L.oracle_nvfp4_weight.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64]
+        L.oracle_q6k_weight.restype = ctypes.c_double
+        L.oracle_q6k_weight.argtypes = [vp, i64, i64, i64]
+        L.oracle_router_logits.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp]
+        L.oracle_topk.argtypes = [vp, i64, i64, i64, i32, vp, vp]
+        L.oracle_bucket.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.oracle_hist.argtypes = [vp, i64, i32, i32, vp]
+        L.oracle_expert.argtypes = [ctypes.POINTER(OracleExperts), i64, vp, vp]
+        L.oracle_ffn_combine.argtypes = [ctypes.POINTER(OracleExperts), vp, i64, i64, vp, vp,
+                                         vp, vp, i64, vp, vp]
+        L.oracle_decode_nvfp4.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp]
+        L.oracle_decode_q6k.argtypes = [vp, i64, i64, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+# ---- formats -------------------------------------------------------------
+
+def e2m1(code: int) -> float:
+    return lib().oracle_e2m1(code)
+
+
+def e4m3(b: int) -> float:
+    return lib().oracle_e4m3(b)
+
+
+def bf16(bits: int) -> float:
+    return lib().oracle_bf16(bits)
+
+
+def f16(bits: int) -> float:
+    return lib().oracle_f16(bits)
+
+
+def round_bf16(v: float) -> int:
+    return int(lib().oracle_round_bf16(v))
+
+
+def decode_nvfp4(codes: np.ndarray, scales: np.ndarray, ts: float) -> np.ndarray:
+    N = codes.shape[0]
+    K = codes.shape[1] * 2
+    out = np.empty((N, K), np.float64)
+    lib().oracle_decode_nvfp4(_p(np.ascontiguousarray(codes)), _p(np.ascontiguousarray(scales)),
+                              ts, N, K, _p(out))
+    return out
+
+
+def decode_q6k(blocks: np.ndarray, K: int) -> np.ndarray:
+    N = blocks.shape[0]
+    out = np.empty((N, K), np.float64)
+    lib().oracle_decode_q6k(_p(np.ascontiguousarray(blocks)), N, K, _p(out))
+    return out
+
+
+# ---- layer steps ---------------------------------------------------------
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None, order: int = 0) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.uint16)
+    T, H = x.shape
+    E = w_router.shape[0]
+    out = np.empty((T, E), np.float32)
+    lib().oracle_router_logits(_p(x), T, H, _p(np.ascontiguousarray(w_router, np.float32)),
+                               _p(None if bias is None else np.ascontiguousarray(bias, np.float32)),
+                               E, order, _p(out))
+    return out
+
+
+def topk(logits: np.ndarray, k: int, renormalize: int = 1):
+    logits = np.ascontiguousarray(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    lib().oracle_topk(_p(logits), T, E, k, renormalize, _p(idx), _p(w))
+    return idx, w
+
+
+def bucket(idx: np.ndarray, E: int):
+    idx = np.ascontiguousarray(idx, np.int32).reshape(-1)
+    A = idx.size
+    counts = np.empty(E, np.uint32)
+    offsets = np.empty(E + 1, np.int32)
+    sorted_asg = np.empty(A, np.int32)
+    pos = np.empty(A, np.int32)
+    active = np.empty(E, np.int32)
+    n_active = np.zeros(1, np.int32)
+    lib().oracle_bucket(_p(idx), A, E, _p(counts), _p(offsets), _p(sorted_asg), _p(pos),
+                        _p(active), _p(n_active))
+    return dict(counts=counts, offsets=offsets, sorted_asg=sorted_asg, asg_pos=pos,
+                active=active[: int(n_active[0])].copy(), n_active=int(n_active[0]))
+
+
+def hist(counts: np.ndarray, hist_in: np.ndarray, decay_shift: int, unit_shift: int) -> np.ndarray:
+    h = np.ascontiguousarray(hist_in, np.uint32).copy()
+    c = np.ascontiguousarray(counts, np.uint32)
+    lib().oracle_hist(_p(c), c.size, decay_shift, unit_shift, _p(h))
+    return h
+
+
+def experts_struct(L):
+    """OracleExperts view of a moegen.LayerWeights (keeps references alive)."""
+    s = OracleExperts(L.E, L.H, L.I, L.fmt_down,
+                      _p(L.gate_q), _p(L.gate_s), _p(L.gate_ts),
+                      _p(L.up_q), _p(L.up_s), _p(L.up_ts),
+                      _p(L.down_q), _p(L.down_s), _p(L.down_ts))
+    s._keep = L
+    return s
+
+
+def expert(L, e: int, x_row: np.ndarray) -> np.ndarray:
+    s = experts_struct(L)
+    y = np.empty(L.H, np.float64)
+    lib().oracle_expert(ctypes.byref(s), e, _p(np.ascontiguousarray(x_row, np.uint16)), _p(y))
+    return y
+
+
+def ffn_combine(L, x: np.ndarray, idx: np.ndarray, w: np.ndarray, residual=None,
+                tokens=None, want_y: bool = False):
+    """Layer output bf16 bits [T][H] (rows of unlisted tokens are zero)."""
+    s = experts_struct(L)
+    x = np.ascontiguousarray(x, np.uint16)
+    T = x.shape[0]
+    k = idx.shape[1]
+    out = np.zeros((T, L.H), np.uint16)
+    y = np.zeros((T * k, L.H), np.float64) if want_y else None
+    tok = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
+    lib().oracle_ffn_combine(ctypes.byref(s), _p(x), T, k,
+                             _p(np.ascontiguousarray(idx, np.int32)),
+                             _p(np.ascontiguousarray(w, np.float32)),
+                             _p(None if residual is None else np.ascontiguousarray(residual, np.uint16)),
+                             _p(tok), 0 if tok is None else tok.size, _p(out), _p(y))
+    return (out, y) if want_y else out
+
+
+def route(x, L, order: int = 0):
+    logits = router_logits(x, L.w_router, L.bias, order)
+    idx, w = topk(logits, L.k, L.renormalize)
+    return logits, idx, w
+
+
+def layer(x, L, residual=None, tokens=None):
+    """Full layer: route, bucket, experts and combine for the given tokens."""
+    logits, idx, w = route(x, L)
+    b = bucket(idx, L.E)
+    out = ffn_combine(L, x, idx, w, residual, tokens)
+    return dict(logits=logits, idx=idx, w=w, buckets=b, out=out)

@@ -1,0 +1,333 @@
+/*
+ * oracle.c -- plain, slow CPU reference of the quantized mixture-of-experts
+ * layer.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and the benchmark's
+ * CPU-baseline leg call it; the GPU library never does, and the two share no
+ * code, header or table.
+ *
+ * What the layer computes is taken from the Basalt pages:
+ *   - "Each token uses only a few experts" and the busiest experts are kept in
+ *     VRAM (basalt.jgulfo.com, section "Expert tiers"); a mixture-of-experts
+ *     model "selects a subset as it processes tokens" (aiopssre.com, "What
+ *     Basalt changes in a Blackwell local inference stack", section "Experts
+ *     can move without becoming free").
+ *   - Routed experts are stored as NVIDIA's NVFP4, and packs such as
+ *     NVFP4-DQ6_K carry GGUF Q6_K tensors (basalt.jgulfo.com, sections
+ *     "Models", "Quick start" and "All the numbers" / engine notes).
+ * The pages give no formula; the readings used here (all listed in the design
+ * notes) are: router logits in fp64 accumulation rounded once to fp32;
+ * selection on logits by (logit desc, index asc); softmax renormalised over the
+ * selected k; SwiGLU experts h = silu(gate) * up; combine as the gate-weighted
+ * sum in j order; output rounded once to bf16.
+ *
+ * Everything here is evaluated in double precision from exactly decoded
+ * weights, so it is the definition's value up to fp64 rounding.  Parity of
+ * every function is pinned by the CPU tests (format tables, brute force,
+ * closed forms, a dense reference on the tiny layer).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                       */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 (4-bit float of the OCP microscaling spec, used by NVFP4):
+ * bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
+ * Exponent 0 is subnormal: value = m * 0.5. Otherwise (1 + m/2) * 2^(e-1). */
+double oracle_e2m1(uint32_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double v = (e == 0) ? m * 0.5 : (1.0 + m * 0.5) * ldexp(1.0, e - 1);
+  return s ? -v : v;
+}
+
+/* E4M3 "fn" (OCP 8-bit float): bit 7 sign, bits 6..3 exponent (bias 7),
+ * bits 2..0 mantissa; exponent 0 subnormal = m/8 * 2^-6; 0x7f / 0xff NaN. */
+double oracle_e4m3(uint32_t b) {
+  int s = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = (e == 0) ? (m / 8.0) * ldexp(1.0, -6) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+  return s ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* IEEE binary16. */
+double oracle_f16(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else v = e ? ldexp(1.0 + m / 1024.0, e - 15) : ldexp(m / 1024.0, -14);
+  return s ? -v : v;
+}
+
+/* Round a double to the nearest bfloat16 (ties to even), returning its bits.
+ * Finite inputs; overflow saturates to infinity like an IEEE conversion. */
+uint16_t oracle_round_bf16(double v) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0) return sign;
+  int e;
+  frexp(a, &e);          /* a = f * 2^e, f in [0.5, 1) */
+  int ue = e - 1;        /* a in [2^ue, 2^(ue+1)) */
+  if (ue < -126) ue = -126;
+  double q = ldexp(a, 7 - ue);  /* 8-bit significand units */
+  double r = nearbyint(q);      /* ties to even */
+  uint32_t mant = (uint32_t)r;
+  int biased = ue + 127;
+  if (mant >= 256) { mant >>= 1; biased += 1; }
+  if (mant < 128) return (uint16_t)(sign | mant);       /* subnormal */
+  if (biased >= 255) return (uint16_t)(sign | 0x7f80);  /* inf */
+  return (uint16_t)(sign | ((uint32_t)biased << 7) | (mant - 128));
+}
+
+/* Decoded-value tables built from the functions above (speed only). */
+static double T_E2M1[16], T_E4M3[256];
+static int tables_ready = 0;
+static void tables_init(void) {
+  if (tables_ready) return;
+  for (int c = 0; c < 16; ++c) T_E2M1[c] = oracle_e2m1((uint32_t)c);
+  for (int b = 0; b < 256; ++b) T_E4M3[b] = oracle_e4m3((uint32_t)b);
+  tables_ready = 1;
+}
+
+/* NVFP4 weight (n, k) of an N x K matrix, canonical row-major layout:
+ * code nibble (k & 1) of byte codes[n*K/2 + k/2]; scale byte scales[n*K/16 + k/16];
+ * value = e2m1(code) * e4m3(scale) * ts (exact in double). */
+double oracle_nvfp4_weight(const uint8_t* codes, const uint8_t* scales, float ts,
+                           int64_t K, int64_t n, int64_t k) {
+  tables_init();
+  uint8_t byte = codes[n * (K / 2) + k / 2];
+  uint32_t code = (k & 1) ? (byte >> 4) : (byte & 15);
+  return T_E2M1[code] * T_E4M3[scales[n * (K / 16) + k / 16]] * (double)ts;
+}
+
+/* Q6_K-style weight (n, k): superblock s = k/256 of row n is 210 bytes:
+ * ql[128] | qh[64] | sc int8[16] | d fp16[2]; i = k % 256;
+ * q = (nibble (i&1) of ql[i/2]) | (bits 2*(i&3).. of qh[i/4]) << 4;
+ * value = d * sc[i/16] * (q - 32). */
+double oracle_q6k_weight(const uint8_t* blocks, int64_t K, int64_t n, int64_t k) {
+  const uint8_t* b = blocks + (n * (K / 256) + k / 256) * 210;
+  int i = (int)(k % 256);
+  int lo = (b[i >> 1] >> (4 * (i & 1))) & 15;
+  int hi = (b[128 + (i >> 2)] >> (2 * (i & 3))) & 3;
+  int q = lo | (hi << 4);
+  int8_t sc = (int8_t)b[192 + i / 16];
+  uint16_t dbits = (uint16_t)(b[208] | (b[209] << 8));
+  return oracle_f16(dbits) * (double)sc * (double)(q - 32);
+}
+
+/* ------------------------------------------------------------------ */
+/* Router                                                               */
+/* ------------------------------------------------------------------ */
+
+/* Router logits l[t][e] = fp32( sum_h x[t][h] * Wr[e][h] + b[e] ).
+ * Every product of a bf16 and an fp32 is exact in double; the sum is taken in
+ * double and rounded to fp32 once.
+ *   order 0 (the documented order): 64 interleaved partial sums, partial j
+ *     adding the terms h = j, j+64, j+128, ... in ascending h; the partials are
+ *     then combined pairwise, p[j] += p[j+w] for w = 32, 16, 8, 4, 2, 1;
+ *     the bias is added to the total.
+ *   order 1: one running sum over h ascending, then the bias (cross-check). */
+void oracle_router_logits(const uint16_t* x, int64_t T, int64_t H, const float* Wr,
+                          const float* bias, int64_t E, int order, float* logits) {
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t e = 0; e < E; ++e) {
+      double s;
+      if (order == 0) {
+        double p[64];
+        for (int j = 0; j < 64; ++j) {
+          p[j] = 0.0;
+          for (int64_t h = j; h < H; h += 64)
+            p[j] += oracle_bf16(x[t * H + h]) * (double)Wr[e * H + h];
+        }
+        for (int w = 32; w >= 1; w /= 2)
+          for (int j = 0; j < w; ++j) p[j] = p[j] + p[j + w];
+        s = p[0];
+      } else {
+        s = 0.0;
+        for (int64_t h = 0; h < H; ++h) s += oracle_bf16(x[t * H + h]) * (double)Wr[e * H + h];
+      }
+      if (bias) s += (double)bias[e];
+      logits[t * E + e] = (float)s;
+    }
+  }
+}
+
+static const float* g_sort_logits;
+static int cmp_desc_then_index(const void* a, const void* b) {
+  int32_t i = *(const int32_t*)a, j = *(const int32_t*)b;
+  float li = g_sort_logits[i], lj = g_sort_logits[j];
+  if (li > lj) return -1;
+  if (li < lj) return 1;
+  return (i < j) ? -1 : (i > j);
+}
+
+/* Top-k and gate weights from fp32 logits [T][E]:
+ * idx[t][0..k) = the k experts first in the order (logit desc, index asc);
+ * renormalize != 0: w_j = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ *   (the softmax over all E restricted to the selected k and renormalised --
+ *   the full denominator cancels);
+ * renormalize == 0: w_j = exp(l_j - l_max) / sum_e exp(l_e - l_max).
+ * Weights are computed in double and rounded to fp32. */
+void oracle_topk(const float* logits, int64_t T, int64_t E, int64_t k, int renormalize,
+                 int32_t* idx, float* w) {
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    for (int64_t e = 0; e < E; ++e) order[e] = (int32_t)e;
+    g_sort_logits = l;
+    qsort(order, (size_t)E, sizeof(int32_t), cmp_desc_then_index);
+    double top = (double)l[order[0]];
+    double den = 0.0;
+    if (renormalize) {
+      for (int64_t i = 0; i < k; ++i) den += exp((double)l[order[i]] - top);
+    } else {
+      for (int64_t e = 0; e < E; ++e) den += exp((double)l[e] - top);
+    }
+    for (int64_t j = 0; j < k; ++j) {
+      idx[t * k + j] = order[j];
+      w[t * k + j] = (float)(exp((double)l[order[j]] - top) / den);
+    }
+  }
+  free(order);
+}
+
+/* ------------------------------------------------------------------ */
+/* Bucketing and histogram                                              */
+/* ------------------------------------------------------------------ */
+
+/* Stable counting sort of the A = T*k assignments a = t*k + j by expert:
+ * counts[e] = #{a : idx[a] == e}; offsets = exclusive prefix sum (E+1 entries);
+ * sorted[offsets[e] ..] = the assignments of e in ascending a;
+ * pos = inverse of sorted; active = experts with counts > 0, ascending. */
+void oracle_bucket(const int32_t* idx, int64_t A, int64_t E, uint32_t* counts,
+                   int32_t* offsets, int32_t* sorted, int32_t* pos, int32_t* active,
+                   int32_t* n_active) {
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t a = 0; a < A; ++a) counts[idx[a]]++;
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + (int32_t)counts[e];
+  int64_t fill = 0;
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t a = 0; a < A; ++a)
+      if (idx[a] == e) sorted[fill++] = (int32_t)a;
+  for (int64_t p = 0; p < A; ++p) pos[sorted[p]] = (int32_t)p;
+  int32_t na = 0;
+  for (int64_t e = 0; e < E; ++e)
+    if (counts[e] > 0) active[na++] = (int32_t)e;
+  *n_active = na;
+}
+
+/* Running usage histogram, unsigned 32-bit wrap-around arithmetic:
+ * hist[e] <- hist[e] - (hist[e] >> decay_shift) + (counts[e] << unit_shift). */
+void oracle_hist(const uint32_t* counts, int64_t E, int decay_shift, int unit_shift,
+                 uint32_t* hist) {
+  for (int64_t e = 0; e < E; ++e)
+    hist[e] = hist[e] - (hist[e] >> decay_shift) + (counts[e] << unit_shift);
+}
+
+/* ------------------------------------------------------------------ */
+/* Expert FFN and combine                                               */
+/* ------------------------------------------------------------------ */
+
+enum { ORACLE_FMT_NVFP4 = 1, ORACLE_FMT_Q6K = 2 };
+
+/* Expert weights in the canonical layouts, stacked over experts. */
+typedef struct oracle_experts {
+  int32_t E, H, I, fmt_down;
+  const uint8_t* gate_q;   /* [E][I][H/2] */
+  const uint8_t* gate_s;   /* [E][I][H/16] */
+  const float* gate_ts;    /* [E] */
+  const uint8_t* up_q;
+  const uint8_t* up_s;
+  const float* up_ts;
+  const uint8_t* down_q;   /* NVFP4 [E][H][I/2], or Q6_K [E][H][I/256*210] */
+  const uint8_t* down_s;   /* NVFP4 [E][H][I/16], NULL for Q6_K */
+  const float* down_ts;    /* NVFP4 [E], NULL for Q6_K */
+} oracle_experts;
+
+static double down_weight(const oracle_experts* X, int64_t e, int64_t n, int64_t i) {
+  int64_t H = X->H, I = X->I;
+  if (X->fmt_down == ORACLE_FMT_Q6K)
+    return oracle_q6k_weight(X->down_q + e * H * (I / 256) * 210, I, n, i);
+  return oracle_nvfp4_weight(X->down_q + e * H * (I / 2), X->down_s + e * H * (I / 16),
+                             X->down_ts[e], I, n, i);
+}
+
+/* SwiGLU expert e applied to one bf16 token x[H]:
+ *   g_i = sum_h x_h Wg[i][h],  u_i = sum_h x_h Wu[i][h],
+ *   h_i = silu(g_i) * u_i,  silu(z) = z / (1 + exp(-z)),
+ *   y_n = sum_i h_i Wd[n][i];  all in double, y written as double [H]. */
+void oracle_expert(const oracle_experts* X, int64_t e, const uint16_t* x, double* y) {
+  int64_t H = X->H, I = X->I;
+  double* hv = (double*)malloc(sizeof(double) * (size_t)I);
+  const uint8_t* gq = X->gate_q + e * I * (H / 2);
+  const uint8_t* gs = X->gate_s + e * I * (H / 16);
+  const uint8_t* uq = X->up_q + e * I * (H / 2);
+  const uint8_t* us = X->up_s + e * I * (H / 16);
+  for (int64_t i = 0; i < I; ++i) {
+    double g = 0.0, u = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      double xv = oracle_bf16(x[h]);
+      g += xv * oracle_nvfp4_weight(gq, gs, X->gate_ts[e], H, i, h);
+      u += xv * oracle_nvfp4_weight(uq, us, X->up_ts[e], H, i, h);
+    }
+    hv[i] = g / (1.0 + exp(-g)) * u;
+  }
+  for (int64_t n = 0; n < H; ++n) {
+    double s = 0.0;
+    for (int64_t i = 0; i < I; ++i) s += hv[i] * down_weight(X, e, n, i);
+    y[n] = s;
+  }
+  free(hv);
+}
+
+/* Layer output for the listed tokens (all T when tokens == NULL):
+ *   out[t] = bf16( residual[t] + sum_{j<k} w[t][j] * y_{t,j} ),
+ * y_{t,j} = expert idx[t][j] applied to x[t]; sum in j order, in double.
+ * residual may be NULL.  out is indexed by token (only listed rows written);
+ * y_out (nullable) receives y_{t,j} as double [T*k][H] for listed tokens. */
+void oracle_ffn_combine(const oracle_experts* X, const uint16_t* x, int64_t T, int64_t k,
+                        const int32_t* idx, const float* w, const uint16_t* residual,
+                        const int32_t* tokens, int64_t n_tokens, uint16_t* out,
+                        double* y_out) {
+  int64_t H = X->H;
+  double* y = (double*)malloc(sizeof(double) * (size_t)H);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+  int64_t n_list = tokens ? n_tokens : T;
+  for (int64_t q = 0; q < n_list; ++q) {
+    int64_t t = tokens ? tokens[q] : q;
+    for (int64_t n = 0; n < H; ++n) acc[n] = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      oracle_expert(X, idx[t * k + j], x + t * H, y);
+      if (y_out) memcpy(y_out + (t * k + j) * H, y, sizeof(double) * (size_t)H);
+      for (int64_t n = 0; n < H; ++n) acc[n] += (double)w[t * k + j] * y[n];
+    }
+    for (int64_t n = 0; n < H; ++n) {
+      double r = residual ? oracle_bf16(residual[t * H + n]) : 0.0;
+      out[t * H + n] = oracle_round_bf16(r + acc[n]);
+    }
+  }
+  free(y);
+  free(acc);
+}
+
+/* Decoded matrix helpers, used by tests to build independent references. */
+void oracle_decode_nvfp4(const uint8_t* codes, const uint8_t* scales, float ts, int64_t N,
+                         int64_t K, double* out) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) out[n * K + k] = oracle_nvfp4_weight(codes, scales, ts, K, n, k);
+}
+
+void oracle_decode_q6k(const uint8_t* blocks, int64_t N, int64_t K, double* out) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) out[n * K + k] = oracle_q6k_weight(blocks, K, n, k);
+}

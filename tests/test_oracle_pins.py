@@ -1,0 +1,326 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test ties one oracle function to something other than its own formula:
+format tables of the OCP specifications (tests/golden), torch's float8 /
+bfloat16 / numpy float16 decoders, exact rational arithmetic, brute-force
+sorting, numpy's stable argsort, scipy's softmax and expit, and a dense fp64
+reference of the whole layer on the tiny workload.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import moegen
+import oracle
+from conftest import load_golden
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e2m1_matches_ocp_table():
+    rows = load_golden("e2m1_values.txt")
+    assert len(rows) == 16
+    for code, val in rows:
+        got = oracle.e2m1(int(code))
+        assert got == float(val)
+        assert math.copysign(1.0, got) == math.copysign(1.0, float(val))
+
+
+def test_e4m3_matches_ocp_points_and_torch():
+    for b, val in load_golden("e4m3_points.txt"):
+        got = oracle.e4m3(int(b, 16))
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(256):
+        got = oracle.e4m3(b)
+        if math.isnan(ref[b]):
+            assert math.isnan(got), b
+        else:
+            assert got == ref[b], (b, got, ref[b])
+
+
+def test_f16_bf16_decode_match_numpy_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 65536, size=4000, dtype=np.uint16)
+    f16 = bits.view(np.float16).astype(np.float64)
+    bf = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    for i, b in enumerate(bits):
+        g = oracle.f16(int(b))
+        assert (math.isnan(g) and math.isnan(f16[i])) or g == f16[i]
+        g = oracle.bf16(int(b))
+        assert (math.isnan(g) and math.isnan(bf[i])) or g == bf[i]
+
+
+def test_round_bf16_matches_torch_rne():
+    rng = np.random.default_rng(2)
+    vals = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000),
+                           [1.00390625, 1.005859375, -2.01171875, 3.0e-39, -1.0e-40]])
+    vals = vals.astype(np.float32)  # exactly representable: one rounding in torch too
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for v, r in zip(vals, ref):
+        assert oracle.round_bf16(float(v)) == int(r), v
+
+
+def test_nvfp4_decode_hand_built():
+    e2m1 = {int(c): float(v) for c, v in load_golden("e2m1_values.txt")}
+    e4m3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    rng = np.random.default_rng(3)
+    N, K = 5, 64
+    codes4 = rng.integers(0, 16, size=(N, K))
+    scales = rng.integers(0, 127, size=(N, K // 16)).astype(np.uint8)
+    packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
+    ts = np.float32(0.0123)
+    got = oracle.decode_nvfp4(packed, scales, float(ts))
+    for n in range(N):
+        for k in range(K):
+            exp = e2m1[int(codes4[n, k])] * e4m3[scales[n, k // 16]] * float(ts)
+            assert got[n, k] == exp
+
+
+def test_q6k_decode_closed_form():
+    """Pack random integers by the documented byte layout; decode must equal
+    d * sc * (q - 32) computed from the integers themselves."""
+    rng = np.random.default_rng(4)
+    N, K = 3, 512
+    q = rng.integers(0, 64, size=(N, K))
+    sc = rng.integers(-128, 128, size=(N, K // 16))
+    d = (rng.standard_normal((N, K // 256)) * 1e-3).astype(np.float16)
+    blocks = np.zeros((N, K // 256, 210), np.uint8)
+    for n in range(N):
+        for s in range(K // 256):
+            for i in range(256):
+                v = int(q[n, 256 * s + i])
+                blocks[n, s, i // 2] |= (v & 15) << (4 * (i % 2))
+                blocks[n, s, 128 + i // 4] |= ((v >> 4) & 3) << (2 * (i % 4))
+            blocks[n, s, 192:208] = sc[n, 16 * s:16 * s + 16].astype(np.int8).view(np.uint8)
+            blocks[n, s, 208:210] = np.frombuffer(d[n, s].tobytes(), np.uint8)
+    got = oracle.decode_q6k(blocks.reshape(N, -1), K)
+    for n in range(N):
+        for k in range(K):
+            exp = float(d[n, k // 256]) * float(sc[n, k // 16]) * float(q[n, k] - 32)
+            assert got[n, k] == exp
+
+
+def test_generator_quantizers_roundtrip_on_grid():
+    """Values already on the NVFP4 / Q6_K grids survive quantize->decode."""
+    e2m1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    rng = np.random.default_rng(5)
+    N, K = 4, 64
+    W = rng.choice(np.concatenate([e2m1, -e2m1]), size=(N, K))
+    W[:, 0] = 6.0  # each 16-block then has amax 6 in some rows; force exact scale
+    for b in range(K // 16):
+        W[:, 16 * b] = 6.0
+    W = (W * 0.25).astype(np.float32)  # amax 1.5 -> ts = 1.5/2688
+    codes, scales, ts = moegen.quant_nvfp4(W)
+    dec = oracle.decode_nvfp4(codes, scales, ts)
+    np.testing.assert_allclose(dec, W, rtol=2e-7, atol=0)
+
+
+# ---------------------------------------------------------------- router
+
+def _f32_rne_of_fraction(fr: Fraction) -> np.float32:
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                     int(np.array(c).view(np.uint32)) & 1))
+    return best
+
+
+def test_router_logits_equal_exact_rounding_tiny():
+    W = moegen.WORKLOADS["tiny"]
+    L = moegen.make_layer(W)
+    x = moegen.make_tokens(W, W.T)
+    bias = np.linspace(-0.3, 0.2, W.E).astype(np.float32)
+    for order in (0, 1):
+        got = oracle.router_logits(x, L.w_router, bias, order)
+        xf = moegen.bf16_to_f32(x)
+        for t in range(W.T):
+            for e in range(W.E):
+                s = sum(Fraction(float(a)) * Fraction(float(b))
+                        for a, b in zip(xf[t], L.w_router[e]))
+                s += Fraction(float(bias[e]))
+                assert got[t, e] == _f32_rne_of_fraction(s), (order, t, e)
+
+
+def test_router_orders_agree_at_decode_shape():
+    W = moegen.WORKLOADS["decode"]
+    rng_layer = moegen.make_layer(moegen.Workload("r", E=128, k=8, H=2048, I=128, T=8))
+    x = moegen.make_tokens(W, 64)
+    a = oracle.router_logits(x, rng_layer.w_router, None, 0)
+    b = oracle.router_logits(x, rng_layer.w_router, None, 1)
+    ref = (moegen.bf16_to_f32(x).astype(np.float64) @ rng_layer.w_router.T.astype(np.float64))
+    assert np.array_equal(a, b)
+    assert np.array_equal(a, ref.astype(np.float32))
+
+
+# ---------------------------------------------------------------- top-k
+
+def _brute_topk(l, k):
+    order = sorted(range(len(l)), key=lambda e: (-float(l[e]), e))
+    return order[:k]
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (256, 8), (5, 5), (64, 1)])
+def test_topk_brute_force_with_ties(E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    T = 200
+    logits = (rng.integers(-6, 6, size=(T, E)) * 0.25).astype(np.float32)  # many ties
+    idx, w = oracle.topk(logits, k, 1)
+    for t in range(T):
+        assert list(idx[t]) == _brute_topk(logits[t], k)
+        ref = scipy.special.softmax(logits[t, idx[t]].astype(np.float64))
+        np.testing.assert_allclose(w[t], ref, rtol=0, atol=1e-7)
+        assert abs(float(np.sum(w[t].astype(np.float64))) - 1.0) <= 1e-6
+
+
+def test_topk_special_cases():
+    l = np.zeros((3, 16), np.float32)
+    idx, w = oracle.topk(l, 4, 1)
+    assert (idx == np.arange(4)).all() and np.allclose(w, 0.25, atol=0)
+    rng = np.random.default_rng(7)
+    l = rng.standard_normal((10, 16)).astype(np.float32)
+    idx, w = oracle.topk(l, 1, 1)
+    assert (w == 1.0).all() and (idx[:, 0] == np.argmax(l, axis=1)).all()
+    idx, w = oracle.topk(l, 16, 1)
+    for t in range(10):
+        assert list(idx[t]) == _brute_topk(l[t], 16)
+    idx, w = oracle.topk(l, 3, 0)  # no renormalisation: full softmax probabilities
+    for t in range(10):
+        p = scipy.special.softmax(l[t].astype(np.float64))
+        np.testing.assert_allclose(w[t], p[idx[t]], rtol=0, atol=1e-7)
+
+
+# ---------------------------------------------------------------- bucketing
+
+@pytest.mark.parametrize("T,k,E", [(4, 2, 8), (1, 8, 128), (300, 4, 32), (1000, 8, 256), (0, 8, 16)])
+def test_bucket_matches_stable_argsort(T, k, E):
+    rng = np.random.default_rng(T + E)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32) \
+        if T else np.zeros((0, k), np.int32)
+    b = oracle.bucket(idx, E)
+    flat = idx.reshape(-1)
+    assert (b["counts"] == np.bincount(flat, minlength=E)).all()
+    assert b["offsets"][0] == 0 and (np.diff(b["offsets"]) == b["counts"]).all()
+    assert (b["sorted_asg"] == np.argsort(flat, kind="stable")).all()
+    assert (b["sorted_asg"][b["asg_pos"]] == np.arange(T * k)).all()
+    assert (b["active"] == np.nonzero(b["counts"])[0]).all()
+
+
+# ---------------------------------------------------------------- histogram
+
+def test_hist_steps_and_fixed_point():
+    h = oracle.hist(np.array([3, 0, 1], np.uint32), np.array([1000, 31, 0xFFFFFFFF], np.uint32), 5, 10)
+    assert list(h) == [1000 - 31 + 3072, 31 - 0 + 0, (0xFFFFFFFF - (0xFFFFFFFF >> 5) + 1024) & 0xFFFFFFFF]
+    s, u = 5, 10
+    counts = np.array([0, 1, 2, 7, 8], np.uint32)
+    hv = np.zeros(5, np.uint32)
+    for _ in range(3000):
+        hv = oracle.hist(counts, hv, s, u)
+    for c, v in zip(counts, hv):
+        C = int(c) << u
+        assert C << s <= int(v) <= (C << s) + (1 << s) - 1   # v >> s == C
+    assert (oracle.hist(counts, hv, s, u) == hv).all()
+
+
+# ---------------------------------------------------------------- expert FFN
+
+def _dense_reference(L, x, w_idx, w_val, residual=None):
+    """Every token through every expert in fp64, combined with gate weights
+    that are zero for unselected experts (no bucketing, no gather)."""
+    e2m1 = np.array([float(v) for _, v in load_golden("e2m1_values.txt")])
+    e4m3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    def dq(codes, scales, ts):
+        N, Kh = codes.shape
+        c = np.empty((N, 2 * Kh), np.int64)
+        c[:, 0::2] = codes & 15
+        c[:, 1::2] = codes >> 4
+        return e2m1[c] * np.repeat(e4m3[scales], 16, axis=1) * float(ts)
+
+    xf = moegen.bf16_to_f32(x).astype(np.float64)
+    T = x.shape[0]
+    gates = np.zeros((T, L.E))
+    for t in range(T):
+        gates[t, w_idx[t]] = w_val[t]
+    out = np.zeros((T, L.H))
+    ys = {}
+    for e in range(L.E):
+        Wg = dq(L.gate_q[e], L.gate_s[e], L.gate_ts[e])
+        Wu = dq(L.up_q[e], L.up_s[e], L.up_ts[e])
+        if L.fmt_down == moegen.FMT_NVFP4:
+            Wd = dq(L.down_q[e], L.down_s[e], L.down_ts[e])
+        else:
+            Wd = oracle.decode_q6k(L.down_q[e], L.I)
+        g = xf @ Wg.T
+        u = xf @ Wu.T
+        h = g * scipy.special.expit(g) * u
+        y = h @ Wd.T
+        ys[e] = y
+        out += gates[:, e:e + 1] * y
+    if residual is not None:
+        out += moegen.bf16_to_f32(residual).astype(np.float64)
+    return out, ys
+
+
+def _bf16_close(got_bits, ref, ulps=1):
+    got = moegen.bf16_to_f32(got_bits).astype(np.float64)
+    tol = ulps * np.maximum(np.abs(ref), 1e-30) * 2.0 ** -7
+    assert (np.abs(got - ref) <= tol).all(), np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30))
+
+
+def test_ffn_tiny_dense_fp64_reference():
+    W = moegen.WORKLOADS["tiny"]
+    L = moegen.make_layer(W)
+    x = moegen.make_tokens(W, W.T)
+    res = moegen.make_residual(W, W.T)
+    _, idx, w = oracle.route(x, L)
+    out, y = oracle.ffn_combine(L, x, idx, w, residual=res, want_y=True)
+    ref, ys = _dense_reference(L, x, idx, w, residual=res)
+    for t in range(W.T):
+        for j in range(W.k):
+            np.testing.assert_allclose(y[t * W.k + j], ys[idx[t, j]][t], rtol=1e-12, atol=1e-15)
+    _bf16_close(out, ref)
+
+
+def test_ffn_q6k_down_dense_reference():
+    W = moegen.Workload("q6", E=4, k=2, H=256, I=256, T=3, fmt_down=moegen.FMT_Q6K)
+    L = moegen.make_layer(W)
+    x = moegen.make_tokens(W, W.T)
+    _, idx, w = oracle.route(x, L)
+    out, y = oracle.ffn_combine(L, x, idx, w, want_y=True)
+    ref, ys = _dense_reference(L, x, idx, w)
+    for t in range(W.T):
+        for j in range(W.k):
+            np.testing.assert_allclose(y[t * W.k + j], ys[idx[t, j]][t], rtol=1e-12, atol=1e-15)
+    _bf16_close(out, ref)
+
+
+def test_ffn_zero_gate_gives_residual():
+    W = moegen.WORKLOADS["tiny"]
+    L = moegen.make_layer(W)
+    L.gate_q[:] = 0  # all gate weights 0 -> silu(0) = 0 -> expert output 0
+    x = moegen.make_tokens(W, W.T)
+    res = moegen.make_residual(W, W.T)
+    _, idx, w = oracle.route(x, L)
+    out = oracle.ffn_combine(L, x, idx, w, residual=res)
+    assert (out == res).all()
+
+
+def test_ffn_single_expert_identity():
+    W = moegen.WORKLOADS["tiny"]
+    L = moegen.make_layer(W)
+    x = moegen.make_tokens(W, W.T)
+    idx = np.array([[3], [0], [7], [3]], np.int32)
+    w = np.ones((W.T, 1), np.float32)
+    out, y = oracle.ffn_combine(L, x, idx, w, want_y=True)
+    ref = torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    # y is double; rounding it through fp32 first may differ by one bf16 ulp at ties only
+    _bf16_close(out, y, ulps=1)
+    assert np.mean(out.view(np.int16) == ref) > 0.99
