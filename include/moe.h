@@ -1,0 +1,236 @@
+/*
+ * moe.h -- C ABI of libmoe, a single-GPU (MI355X / gfx950) implementation of
+ * the mixture-of-experts layer of a Basalt-style local inference engine:
+ * router logits, softmax top-k gating, token-to-expert bucketing, block-
+ * quantized (NVFP4, Q6_K-style) SwiGLU expert FFNs with the dequantization
+ * fused into the matmuls, the gate-weighted combine, and the per-step expert
+ * usage histogram that decides which experts stay resident.
+ *
+ * What the pages fix, and where:
+ *   - each token uses a few experts chosen from many; the busiest experts stay
+ *     in GPU memory and the rest may live in system RAM and be streamed on
+ *     demand -- basalt.jgulfo.com, section "Expert tiers"; aiopssre.com
+ *     ("What Basalt changes in a Blackwell local inference stack"), section
+ *     "Experts can move without becoming free";
+ *   - routed experts are NVIDIA NVFP4, packs also carry GGUF Q6_K tensors --
+ *     basalt.jgulfo.com, sections "Models", "Quick start" and the engine notes
+ *     under "All the numbers";
+ *   - 1 to 8 concurrent request slots, so decode batches of 1..8 tokens --
+ *     aiopssre.com, section "Concurrency divides context unless you pay for
+ *     more cache"; devotd.net (en), section "--parallel slots and KV cache
+ *     allocation".
+ * The pages give no formula.  The arithmetic below is the plainest reading;
+ * each entry point states it.
+ *
+ * Conventions (all entry points):
+ *   - Pointers are DEVICE pointers unless marked "host".  Every buffer is
+ *     owned by the caller; the library allocates nothing per call and frees
+ *     nothing it was given.
+ *   - Calls are asynchronous and ordered on the given stream.  T == 0 returns
+ *     MOE_OK without launching anything.
+ *   - Arguments are validated on the host before any launch; an invalid or
+ *     unsupported argument returns an error status and launches nothing (no
+ *     clamping, no truncation).  A failed launch returns MOE_ERR_HIP.  The
+ *     message of the last failure on the calling thread is moe_last_error().
+ *     Device-side faults surface at the caller's next synchronization.
+ *   - Calls on different streams may run concurrently if they write
+ *     different buffers.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *
+ * Supported shapes: 1 <= k <= min(E, 64), E <= 1024, H % 128 == 0,
+ * 128 <= H <= 8192, I % 128 == 0 (NVFP4) or I % 256 == 0 (Q6_K), I <= 8192.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, negative size, k > E, ... */
+  MOE_ERR_UNSUPPORTED = -2,  /* shape or format outside the supported set */
+  MOE_ERR_WORKSPACE = -3,    /* workspace or bucket buffer too small */
+  MOE_ERR_BUDGET = -4,       /* tier: HBM budget below the working set */
+  MOE_ERR_HIP = -5,          /* a HIP runtime call or launch failed */
+  MOE_ERR_HOST_ALLOC = -6    /* tier: host metadata allocation failed */
+} moe_status;
+
+/* Weight formats. */
+#define MOE_FMT_NVFP4 1  /* E2M1 codes, E4M3 scale per 16 along K, fp32 per-tensor scale */
+#define MOE_FMT_Q6K 2    /* 256-element superblocks: 16 x int8 sub-scales, fp16 scale, 6-bit codes */
+
+/* Element types of the expert-output buffer y. */
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+/* Library version of this header (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none).  Host
+ * string owned by the library, valid until the next failing call. */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Expert weights                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Canonical input layouts (what moe_pack_experts reads):
+ *   NVFP4 matrix W[N][K]: codes u8 [N][K/2], element k of row n in nibble
+ *     (k & 1) of byte k/2 (even element low); E2M1 code: bit 3 sign, bits 2..1
+ *     exponent (bias 1), bit 0 mantissa.  scales u8 [N][K/16]: E4M3 (fn) scale
+ *     of elements 16b..16b+15.  One fp32 per-tensor scale ts.
+ *     w[n][k] = e2m1(code) * e4m3(scale) * ts.
+ *   Q6_K-style matrix W[N][K]: row n is K/256 superblocks of 210 bytes:
+ *     ql[128] (low 4 bits of element i: nibble i&1 of byte i/2), qh[64]
+ *     (high 2 bits of element i: bits 2*(i&3) of byte i/4), sc int8[16]
+ *     (sub-block i/16), d fp16 little-endian[2];
+ *     w = d * sc[i/16] * (q - 32), q = low | high << 4 in 0..63.
+ *   Gate and up are [I][H] (K = H); down is [H][I] (K = I).
+ *
+ * The GPU kernels read a packed "blob" per expert (a device-friendly
+ * re-arrangement of the same bytes, 16-byte granules transposed so that one
+ * wavefront load covers consecutive rows).  moe_expert_blob_bytes gives its
+ * size; moe_pack_experts writes it.
+ */
+
+/* One entry of the device-resident expert table (24 bytes). */
+typedef struct moe_expert_ref {
+  const void* blob;   /* device pointer to the packed expert (256-byte aligned) */
+  float ts_gate;      /* NVFP4 per-tensor scales */
+  float ts_up;
+  float ts_down;      /* ignored when the down projection is Q6_K */
+  uint32_t reserved;  /* 0 */
+} moe_expert_ref;
+
+/* Bytes of one packed expert blob (a multiple of 256); 0 if unsupported. */
+size_t moe_expert_blob_bytes(int32_t H, int32_t I, int32_t fmt_gate_up, int32_t fmt_down);
+
+/* Pack E experts from the canonical layouts (device arrays stacked over
+ * experts: gate_q [E][I][H/2], gate_s [E][I][H/16], up likewise, down_q
+ * [E][H][I/2] and down_s [E][H][I/16] for NVFP4, or down_q [E][H][I/256*210]
+ * and down_s == NULL for Q6_K) into E blobs at blobs + e * blob_stride.
+ * blob_stride >= moe_expert_blob_bytes(...) and a multiple of 256. */
+moe_status moe_pack_experts(int32_t E, int32_t H, int32_t I, int32_t fmt_gate_up,
+                            int32_t fmt_down, const uint8_t* gate_q, const uint8_t* gate_s,
+                            const uint8_t* up_q, const uint8_t* up_s, const uint8_t* down_q,
+                            const uint8_t* down_s, void* blobs, size_t blob_stride,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Layer description and bucket buffers                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Host struct holding device pointers; read during each call only. */
+typedef struct moe_layer_desc {
+  int32_t E;            /* experts */
+  int32_t k;            /* experts per token */
+  int32_t H;            /* hidden size */
+  int32_t I;            /* expert intermediate size */
+  int32_t fmt_gate_up;  /* MOE_FMT_NVFP4 */
+  int32_t fmt_down;     /* MOE_FMT_NVFP4 or MOE_FMT_Q6K */
+  int32_t renormalize;  /* 1: softmax renormalised over the selected k; 0: full softmax */
+  int32_t reserved;     /* 0 */
+  const moe_expert_ref* experts;  /* device [E] */
+  const float* w_router;          /* device fp32 [E][H] */
+  const float* router_bias;       /* device fp32 [E], or NULL (no bias) */
+} moe_layer_desc;
+
+/* Per-step bucket results (device pointers into one caller buffer). */
+typedef struct moe_buckets {
+  uint32_t* counts;     /* [E]   assignments per expert */
+  int32_t* offsets;     /* [E+1] exclusive prefix sum of counts */
+  int32_t* sorted_asg;  /* [T*k] assignments a = t*k + j ordered by (expert, a) */
+  int32_t* asg_pos;     /* [T*k] position of assignment a in sorted_asg */
+  int32_t* active;      /* [E]   experts with counts > 0, ascending (first n_active) */
+  int32_t* n_active;    /* [1] */
+  int64_t T_max;        /* capacity in tokens */
+  int32_t E;
+  int32_t k;
+} moe_buckets;
+
+/* Bytes needed for the bucket buffers of (E, T_max, k). */
+size_t moe_buckets_bytes(int32_t E, int64_t T_max, int32_t k);
+
+/* Point the fields of *out into the caller's device buffer buf (bytes long,
+ * 256-byte aligned).  Host-only bookkeeping: launches nothing. */
+moe_status moe_buckets_carve(void* buf, size_t bytes, int32_t E, int64_t T_max, int32_t k,
+                             moe_buckets* out);
+
+/* Device workspace bytes for moe_bucket and moe_expert_ffn on up to T_max
+ * tokens of layer L (covers both calls; one buffer may serve both). */
+size_t moe_workspace_bytes(const moe_layer_desc* L, int64_t T_max);
+
+/* ------------------------------------------------------------------------ */
+/* The layer's steps                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Router and top-k gating ("each token uses only a few experts":
+ * basalt.jgulfo.com, "Expert tiers").
+ *   logits[t][e] = fp32( sum_h x[t][h] * w_router[e][h] + bias[e] ), the sum
+ *     taken in double precision in one fixed order -- 64 interleaved partial
+ *     sums (partial j adds h = j, j+64, ... ascending), combined pairwise
+ *     p[j] += p[j+w] for w = 32, 16, ..., 1, then the bias -- and rounded to
+ *     fp32 once, so the logits (and hence the selected experts) are
+ *     reproducible bit for bit.
+ *   topk_idx[t][0..k) = the k experts first in the order (logit desc, expert
+ *     index asc): ties go to the lower index.
+ *   topk_w[t][j] = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0) (renormalize=1),
+ *     or the full softmax probability of expert idx[t][j] (renormalize=0).
+ * x: bf16 [T][H]; logits: fp32 [T][E]; topk_idx: int32 [T][k];
+ * topk_w: fp32 [T][k].  All caller-allocated. */
+moe_status moe_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, float* logits,
+                     int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* Token-to-expert bucketing: a stable counting sort of the T*k assignments by
+ * expert (deterministic; no dependence on atomic ordering).  Fills every
+ * field of *b for this step.  b->T_max >= T, b->E == L->E, b->k == L->k.
+ * ws: device workspace of at least moe_workspace_bytes(L, T) bytes. */
+moe_status moe_bucket(const moe_layer_desc* L, const int32_t* topk_idx, int64_t T,
+                      const moe_buckets* b, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFNs with fused dequantization (SwiGLU):
+ *   for each assignment a of expert e (token t = a / k), at sorted position
+ *   p = b->asg_pos[a]:
+ *     g = x[t] . dq(Wg_e)^T,  u = x[t] . dq(Wu_e)^T,  h = silu(g) * u,
+ *     y[p] = h . dq(Wd_e)^T,  silu(z) = z / (1 + exp(-z)),
+ *   accumulated in fp32.  y: [T*k][H] of y_dtype (MOE_DTYPE_F32 or _BF16),
+ *   rows in sorted order.  Decode-sized batches run as dequant-fused GEMV;
+ *   larger ones as an MFMA grouped GEMM over experts.
+ * ws: at least moe_workspace_bytes(L, T) bytes. */
+moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                          const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Gate-weighted combine (the scatter-add written as a gather, so the result
+ * does not depend on scheduling):
+ *   out[t] = bf16_rne( residual[t] + sum_{j=0..k-1} topk_w[t][j] * y[asg_pos[t*k+j]] ),
+ *   in fp32 with j ascending.  residual: bf16 [T][H] or NULL; out: bf16 [T][H]
+ *   (may alias residual). */
+moe_status moe_combine(const moe_layer_desc* L, const void* y, int32_t y_dtype,
+                       const moe_buckets* b, const float* topk_w, int64_t T,
+                       const uint16_t* residual, uint16_t* out, hipStream_t stream);
+
+/* Expert-usage histogram deciding residency ("keeps the busiest in VRAM",
+ * "Tier 1 ... the most routed experts": basalt.jgulfo.com, "Expert tiers";
+ * "an adaptive tier moves them": FAQ).  Exponentially decaying integer count,
+ * unsigned 32-bit arithmetic:
+ *   hist[e] = hist[e] - (hist[e] >> decay_shift) + (counts[e] << unit_shift).
+ * hist: uint32 [E], read and written.  0 <= decay_shift, unit_shift < 32. */
+moe_status moe_expert_hist(const moe_layer_desc* L, const moe_buckets* b, uint32_t* hist,
+                           int32_t decay_shift, int32_t unit_shift, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

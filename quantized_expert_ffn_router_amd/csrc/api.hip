@@ -1,0 +1,264 @@
+// api.hip -- the extern "C" entry points of libmoe: argument validation
+// (before any launch), error reporting and kernel dispatch.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace moe {
+hipError_t launch_gemv_ffn(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
+                           float* h, void* y, int y_dtype, hipStream_t s);
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status hip_status(const char* where, hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define CHECK_PTR(p, where) \
+  if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", where, #p)
+
+moe_status check_shape(int E, int k, int H, int I, int fmt_gu, int fmt_down, const char* where) {
+  if (E < 1 || k < 1 || H < 1 || I < 1)
+    return fail(MOE_ERR_INVALID_ARG, "%s: E=%d k=%d H=%d I=%d must be positive", where, E, k, H, I);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "%s: k=%d > E=%d", where, k, E);
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d > 1024", where, E);
+  if (k > 64) return fail(MOE_ERR_UNSUPPORTED, "%s: k=%d > 64", where, k);
+  if (H % 128 != 0 || H > 8192)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: H=%d must be a multiple of 128 and <= 8192", where, H);
+  if (fmt_gu != MOE_FMT_NVFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: gate/up format %d (only NVFP4)", where, fmt_gu);
+  if (fmt_down == MOE_FMT_NVFP4) {
+    if (I % 128 != 0 || I > 8192)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d must be a multiple of 128 and <= 8192", where, I);
+  } else if (fmt_down == MOE_FMT_Q6K) {
+    if (I % 256 != 0 || I > 8192)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d must be a multiple of 256 and <= 8192 for Q6_K",
+                  where, I);
+  } else {
+    return fail(MOE_ERR_UNSUPPORTED, "%s: down format %d", where, fmt_down);
+  }
+  return MOE_OK;
+}
+
+moe_status check_layer(const moe_layer_desc* L, const char* where) {
+  CHECK_PTR(L, where);
+  moe_status st = check_shape(L->E, L->k, L->H, L->I, L->fmt_gate_up, L->fmt_down, where);
+  if (st != MOE_OK) return st;
+  if (L->renormalize != 0 && L->renormalize != 1)
+    return fail(MOE_ERR_INVALID_ARG, "%s: renormalize=%d must be 0 or 1", where, L->renormalize);
+  return MOE_OK;
+}
+
+moe_status check_buckets(const moe_layer_desc* L, const moe_buckets* b, int64_t T,
+                         const char* where) {
+  CHECK_PTR(b, where);
+  if (b->E != L->E || b->k != L->k)
+    return fail(MOE_ERR_INVALID_ARG, "%s: buckets carved for E=%d k=%d, layer has E=%d k=%d", where,
+                b->E, b->k, L->E, L->k);
+  if (T > b->T_max)
+    return fail(MOE_ERR_WORKSPACE, "%s: T=%lld exceeds bucket capacity %lld", where, (long long)T,
+                (long long)b->T_max);
+  if (!b->counts || !b->offsets || !b->sorted_asg || !b->asg_pos || !b->active || !b->n_active)
+    return fail(MOE_ERR_INVALID_ARG, "%s: bucket field is NULL (use moe_buckets_carve)", where);
+  return MOE_OK;
+}
+
+constexpr int64_t kMaxT = (int64_t)1 << 24;
+
+moe_status check_T(int64_t T, int k, const char* where) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%lld < 0", where, (long long)T);
+  if (T > kMaxT || T * k > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T=%lld too large", where, (long long)T);
+  return MOE_OK;
+}
+
+size_t ffn_ws(const moe_layer_desc* L, int64_t T) {
+  size_t A = (size_t)T * L->k;
+  return moe::align_up(A * (size_t)L->I * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_expert_blob_bytes(int32_t H, int32_t I, int32_t fmt_gate_up, int32_t fmt_down) {
+  if (check_shape(1, 1, H, I, fmt_gate_up, fmt_down, "moe_expert_blob_bytes") != MOE_OK) return 0;
+  return moe::blob_layout(H, I, fmt_down).total;
+}
+
+moe_status moe_pack_experts(int32_t E, int32_t H, int32_t I, int32_t fmt_gate_up,
+                            int32_t fmt_down, const uint8_t* gate_q, const uint8_t* gate_s,
+                            const uint8_t* up_q, const uint8_t* up_s, const uint8_t* down_q,
+                            const uint8_t* down_s, void* blobs, size_t blob_stride,
+                            hipStream_t stream) {
+  const char* W = "moe_pack_experts";
+  moe_status st = check_shape(E, 1, H, I, fmt_gate_up, fmt_down, W);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(gate_q, W); CHECK_PTR(gate_s, W); CHECK_PTR(up_q, W); CHECK_PTR(up_s, W);
+  CHECK_PTR(down_q, W); CHECK_PTR(blobs, W);
+  if (fmt_down == MOE_FMT_NVFP4) CHECK_PTR(down_s, W);
+  const moe::BlobLayout lay = moe::blob_layout(H, I, fmt_down);
+  if (blob_stride < lay.total || blob_stride % moe::kAlign != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: blob_stride %zu must be >= %zu and a multiple of 256", W,
+                blob_stride, lay.total);
+  uint8_t* d = (uint8_t*)blobs;
+  const size_t gu_q = (size_t)I * H / 2, gu_s = (size_t)I * H / 16;
+  hipError_t e;
+  // gate / up: N = I rows, K = H
+  e = moe::launch_pack_granules(gate_q, E, gu_q, I, H / 32, 16, H / 2, 1, 16, 0, d + lay.gate_q, blob_stride, stream);
+  if (e == hipSuccess) e = moe::launch_pack_granules(gate_s, E, gu_s, I, H / 128, 8, H / 16, 1, 8, 0, d + lay.gate_s, blob_stride, stream);
+  if (e == hipSuccess) e = moe::launch_pack_granules(up_q, E, gu_q, I, H / 32, 16, H / 2, 1, 16, 0, d + lay.up_q, blob_stride, stream);
+  if (e == hipSuccess) e = moe::launch_pack_granules(up_s, E, gu_s, I, H / 128, 8, H / 16, 1, 8, 0, d + lay.up_s, blob_stride, stream);
+  if (e != hipSuccess) return hip_status(W, e);
+  if (fmt_down == MOE_FMT_NVFP4) {
+    // down: N = H rows, K = I
+    e = moe::launch_pack_granules(down_q, E, (size_t)H * I / 2, H, I / 32, 16, I / 2, 1, 16, 0, d + lay.down_q, blob_stride, stream);
+    if (e == hipSuccess) e = moe::launch_pack_granules(down_s, E, (size_t)H * I / 16, H, I / 128, 8, I / 16, 1, 8, 0, d + lay.down_s, blob_stride, stream);
+  } else {
+    const size_t row = (size_t)(I / 256) * 210, ex = (size_t)H * row;
+    e = moe::launch_pack_granules(down_q, E, ex, H, I / 32, 16, row, 8, 210, 0, d + lay.down_ql, blob_stride, stream);
+    if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 64, 16, row, 4, 210, 128, d + lay.down_qh, blob_stride, stream);
+    if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 256, 16, row, 1, 210, 192, d + lay.down_sc, blob_stride, stream);
+    if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 256, 2, row, 1, 210, 208, d + lay.down_d, blob_stride, stream);
+  }
+  return hip_status(W, e);
+}
+
+size_t moe_buckets_bytes(int32_t E, int64_t T_max, int32_t k) {
+  if (E < 1 || k < 1 || T_max < 0) return 0;
+  size_t A = (size_t)T_max * k;
+  return moe::align_up((size_t)E * 4) + moe::align_up((size_t)(E + 1) * 4) +
+         moe::align_up(A * 4) * 2 + moe::align_up((size_t)E * 4) + moe::align_up(4);
+}
+
+moe_status moe_buckets_carve(void* buf, size_t bytes, int32_t E, int64_t T_max, int32_t k,
+                             moe_buckets* out) {
+  const char* W = "moe_buckets_carve";
+  CHECK_PTR(buf, W);
+  CHECK_PTR(out, W);
+  if (E < 1 || k < 1 || T_max < 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: E=%d k=%d T_max=%lld", W, E, k, (long long)T_max);
+  if ((uintptr_t)buf % moe::kAlign != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: buffer not 256-byte aligned", W);
+  size_t need = moe_buckets_bytes(E, T_max, k);
+  if (bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: %zu bytes < %zu needed", W, bytes, need);
+  size_t A = (size_t)T_max * k;
+  char* p = (char*)buf;
+  out->counts = (uint32_t*)p; p += moe::align_up((size_t)E * 4);
+  out->offsets = (int32_t*)p; p += moe::align_up((size_t)(E + 1) * 4);
+  out->sorted_asg = (int32_t*)p; p += moe::align_up(A * 4);
+  out->asg_pos = (int32_t*)p; p += moe::align_up(A * 4);
+  out->active = (int32_t*)p; p += moe::align_up((size_t)E * 4);
+  out->n_active = (int32_t*)p;
+  out->T_max = T_max;
+  out->E = E;
+  out->k = k;
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_layer_desc* L, int64_t T_max) {
+  if (check_layer(L, "moe_workspace_bytes") != MOE_OK || T_max < 0) return 0;
+  size_t a = moe::bucket_ws_bytes(L->E, T_max * L->k);
+  size_t b = ffn_ws(L, T_max);
+  size_t w = a > b ? a : b;
+  return w ? w : moe::kAlign;
+}
+
+moe_status moe_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, float* logits,
+                     int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  const char* W = "moe_route";
+  moe_status st = check_layer(L, W);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->k, W)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  CHECK_PTR(x, W); CHECK_PTR(logits, W); CHECK_PTR(topk_idx, W); CHECK_PTR(topk_w, W);
+  CHECK_PTR(L->w_router, W);
+  hipError_t e = moe::launch_router(x, T, L->H, L->w_router, L->router_bias, L->E, logits, stream);
+  if (e == hipSuccess) e = moe::launch_topk(logits, T, L->E, L->k, L->renormalize, topk_idx, topk_w, stream);
+  return hip_status(W, e);
+}
+
+moe_status moe_bucket(const moe_layer_desc* L, const int32_t* topk_idx, int64_t T,
+                      const moe_buckets* b, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* W = "moe_bucket";
+  moe_status st = check_layer(L, W);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->k, W)) != MOE_OK) return st;
+  if ((st = check_buckets(L, b, T, W)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  CHECK_PTR(topk_idx, W);
+  size_t need = moe::bucket_ws_bytes(L->E, T * L->k);
+  if (need > 0) {
+    CHECK_PTR(ws, W);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
+  }
+  return hip_status(W, moe::launch_bucket(topk_idx, T * L->k, L->E, b, ws, stream));
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                          const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  const char* W = "moe_expert_ffn";
+  moe_status st = check_layer(L, W);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->k, W)) != MOE_OK) return st;
+  if ((st = check_buckets(L, b, T, W)) != MOE_OK) return st;
+  if (y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "%s: y_dtype=%d", W, y_dtype);
+  if (T == 0) return MOE_OK;
+  CHECK_PTR(x, W); CHECK_PTR(y, W); CHECK_PTR(ws, W); CHECK_PTR(L->experts, W);
+  size_t need = ffn_ws(L, T);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
+  return hip_status(W, moe::launch_gemv_ffn(L, x, b, (float*)ws, y, y_dtype, stream));
+}
+
+moe_status moe_combine(const moe_layer_desc* L, const void* y, int32_t y_dtype,
+                       const moe_buckets* b, const float* topk_w, int64_t T,
+                       const uint16_t* residual, uint16_t* out, hipStream_t stream) {
+  const char* W = "moe_combine";
+  moe_status st = check_layer(L, W);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->k, W)) != MOE_OK) return st;
+  if ((st = check_buckets(L, b, T, W)) != MOE_OK) return st;
+  if (y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "%s: y_dtype=%d", W, y_dtype);
+  if (T == 0) return MOE_OK;
+  CHECK_PTR(y, W); CHECK_PTR(topk_w, W); CHECK_PTR(out, W);
+  return hip_status(W, moe::launch_combine(y, y_dtype, b->asg_pos, topk_w, T, L->k, L->H, residual,
+                                           out, stream));
+}
+
+moe_status moe_expert_hist(const moe_layer_desc* L, const moe_buckets* b, uint32_t* hist,
+                           int32_t decay_shift, int32_t unit_shift, hipStream_t stream) {
+  const char* W = "moe_expert_hist";
+  moe_status st = check_layer(L, W);
+  if (st != MOE_OK) return st;
+  CHECK_PTR(b, W);
+  if (b->E != L->E) return fail(MOE_ERR_INVALID_ARG, "%s: buckets carved for E=%d", W, b->E);
+  CHECK_PTR(b->counts, W);
+  CHECK_PTR(hist, W);
+  if (decay_shift < 0 || decay_shift > 31 || unit_shift < 0 || unit_shift > 31)
+    return fail(MOE_ERR_INVALID_ARG, "%s: shifts (%d, %d) must be in [0, 31]", W, decay_shift,
+                unit_shift);
+  return hip_status(W, moe::launch_hist(b->counts, L->E, hist, decay_shift, unit_shift, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// route.hip -- router logits and top-k gating.
+//
+// Each token picks a few experts out of many (basalt.jgulfo.com, section
+// "Expert tiers").  The router is an fp32 linear map; its logits are summed in
+// double precision in one fixed order so that the selected experts are
+// reproducible bit for bit:
+//   partial j (lane j of a wavefront) adds x[h] * W[e][h] for h = j, j+64, ...
+//   in ascending h (every bf16 x fp32 product is exact in double), the 64
+//   partials are combined pairwise p[j] += p[j+w] for w = 32, 16, ..., 1, the
+//   bias is added and the total is rounded once to fp32.
+// A wavefront computes TB tokens x EB experts at once; the 64 partials of all
+// TB*EB values are reduced with a transposed butterfly: at the level with
+// partner lane^w each lane hands half of its values to the partner and keeps
+// the other half, so the reduction costs about one shuffle per value and ends
+// with value v on lane v * (64 / (TB*EB)).  The pairing at every level is the
+// same as in the tree above, so the result is that tree's sum exactly.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRouterWaves = 4;
+
+template <int TB, int EB>
+__global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
+    const uint16_t* __restrict__ x, int T, int H, const float* __restrict__ Wr,
+    const float* __restrict__ bias, int E, float* __restrict__ logits) {
+  constexpr int V = TB * EB;
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "TB*EB must be a power of two <= 64");
+  extern __shared__ uint16_t xs[];  // [TB][H] bf16 bits
+  const int t0 = blockIdx.x * TB;
+  const int tid = threadIdx.x;
+  // Stage the token block (rows past T are zero) with 16-byte loads.
+  const int vec_per_row = H / 8;
+  for (int i = tid; i < TB * vec_per_row; i += blockDim.x) {
+    int r = i / vec_per_row, c = i % vec_per_row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t0 + r < T) v = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + r) * H + 8 * c);
+    *reinterpret_cast<uint4*>(xs + (size_t)r * H + 8 * c) = v;
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int e0 = (blockIdx.y * kRouterWaves + wave) * EB;
+  if (e0 >= E) return;
+
+  double acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.0;
+
+  const float* wrow[EB];
+#pragma unroll
+  for (int q = 0; q < EB; ++q) wrow[q] = Wr + (size_t)min(e0 + q, E - 1) * H;
+
+#pragma unroll 2
+  for (int h = lane; h < H; h += 64) {
+    double w[EB];
+#pragma unroll
+    for (int q = 0; q < EB; ++q) w[q] = (double)wrow[q][h];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      double xv = (double)bf16_to_f32(xs[i * H + h]);
+#pragma unroll
+      for (int q = 0; q < EB; ++q) acc[i * EB + q] = __fma_rn(xv, w[q], acc[i * EB + q]);
+    }
+  }
+
+  // Transposed butterfly (see file comment).
+  int nv = V;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    if (nv > 1) {
+      const bool upper = (lane & w) != 0;
+      const int half = nv >> 1;
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        if (i < half) {
+          double send = upper ? acc[i] : acc[i + half];
+          double keep = upper ? acc[i + half] : acc[i];
+          double other = __shfl_xor(send, w);
+          acc[i] = keep + other;
+        }
+      }
+      nv = half;
+    } else {
+      acc[0] = acc[0] + __shfl_xor(acc[0], w);
+    }
+  }
+  constexpr int kShift = (V == 1) ? 6 : (V == 2) ? 5 : (V == 4) ? 4 : (V == 8) ? 3 : (V == 16) ? 2 : (V == 32) ? 1 : 0;
+  if ((lane & ((1 << kShift) - 1)) == 0) {
+    const int v = lane >> kShift;
+    const int t = t0 + v / EB, e = e0 + v % EB;
+    if (t < T && e < E) {
+      double s = acc[0];
+      if (bias) s += (double)bias[e];
+      logits[(size_t)t * E + e] = (float)s;
+    }
+  }
+}
+
+// One wavefront per token: k rounds of a wave-wide arg-max with key
+// (logit desc, expert asc), then the gate weights.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E,
+                                              int k, int renorm, int32_t* __restrict__ idx,
+                                              float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* l = logits + (size_t)t * E;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int e = lane + 64 * i;
+    v[i] = (e < E) ? l[e] : 0.0f;
+  }
+  uint32_t taken = 0;
+  for (int i = 0; i < 16; ++i)
+    if (lane + 64 * i >= E) taken |= 1u << i;
+
+  float my_v = 0.0f, top = 0.0f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (!(taken & (1u << i))) {
+        int e = lane + 64 * i;
+        if (v[i] > bv || (v[i] == bv && e < be)) { bv = v[i]; be = e; }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      float ov = __shfl_xor(bv, off);
+      int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (j == 0) top = bv;
+    if (lane == j) { my_v = bv; my_e = be; }
+  }
+
+  float ex = (lane < k) ? expf(my_v - top) : 0.0f;
+  float den;
+  if (renorm) {
+    den = ex;
+  } else {
+    den = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (lane + 64 * i < E) den += expf(v[i] - top);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_e;
+    wout[(size_t)t * k + lane] = ex / den;
+  }
+}
+
+template <int TB, int EB>
+hipError_t launch_router_t(const uint16_t* x, int64_t T, int H, const float* Wr,
+                           const float* bias, int E, float* logits, hipStream_t s) {
+  dim3 grid((unsigned)((T + TB - 1) / TB), (unsigned)((E + EB * kRouterWaves - 1) / (EB * kRouterWaves)));
+  size_t lds = (size_t)TB * H * sizeof(uint16_t);
+  hipLaunchKernelGGL((k_router_logits<TB, EB>), grid, dim3(kRouterWaves * 64), lds, s, x, (int)T,
+                     H, Wr, bias, E, logits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router(const uint16_t* x, int64_t T, int H, const float* Wr,
+                         const float* bias, int E, float* logits, hipStream_t s) {
+  // The x tile of TB tokens stays within 64 KiB of LDS: TB * H <= 32768.
+  const int tb_max = 32768 / H;  // >= 4 for H <= 8192
+  // Decode-sized batches: one expert per wavefront, all tokens at once.
+  if (T <= 1) return launch_router_t<1, 1>(x, T, H, Wr, bias, E, logits, s);
+  if (T <= 2) return launch_router_t<2, 1>(x, T, H, Wr, bias, E, logits, s);
+  if (T <= 4) return launch_router_t<4, 1>(x, T, H, Wr, bias, E, logits, s);
+  if (T <= 8) {
+    if (tb_max >= 8) return launch_router_t<8, 1>(x, T, H, Wr, bias, E, logits, s);
+    return launch_router_t<4, 1>(x, T, H, Wr, bias, E, logits, s);
+  }
+  // Larger batches: TB tokens x EB experts per wavefront, TB * EB = 64.
+  if (tb_max >= 16) return launch_router_t<16, 4>(x, T, H, Wr, bias, E, logits, s);
+  if (tb_max >= 8) return launch_router_t<8, 8>(x, T, H, Wr, bias, E, logits, s);
+  return launch_router_t<4, 16>(x, T, H, Wr, bias, E, logits, s);
+}
+
+hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renorm, int32_t* idx,
+                       float* w, hipStream_t s) {
+  dim3 grid((unsigned)((T + 3) / 4));
+  hipLaunchKernelGGL(k_topk, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe
