@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized MoE layer on one MI355X.
+
+A step is one pass of the whole layer over one decode batch: router logits and
+top-k gating, bucketing, the NVFP4 dequant-fused SwiGLU experts, the
+gate-weighted combine and the usage-histogram update.  Workload: 128 experts,
+top-8, hidden 2048, intermediate 768, NVFP4 gate/up/down, decode batches of
+1, 2, 4 and 8 tokens (one per request slot); the headline line is the 8-token
+batch.  Eight distinct seeded layers (2.7 GB of packed weights) are cycled and
+every step gets fresh activations, so expert weights come from HBM and not
+from the 256 MB Infinity Cache.  Each batch size's steps are captured in a HIP
+graph and replayed.
+
+Printed: one JSON line with the throughput (tokens/s), the FFN kernels'
+roofline (expert-weight bytes of the active experts / FFN time from HIP events
+on the launch stream, against 8 TB/s), and the CPU oracle timed on a bounded
+sample beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+N_LAYERS = 8          # distinct layers cycled per step
+X_POOL = 64           # distinct activation batches per batch size
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=512)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--batches", type=str, default="1,2,4,8")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-steps", type=int, default=4)
+    p.add_argument("--profile-steps", type=int, default=0,
+                   help="only run this many eager steps per batch (for profilers)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer has no multi-GPU path "
+              "(expert-parallel sharding is described in the design notes, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moegen
+    import quantized_expert_ffn_router_amd as q
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    W = moegen.WORKLOADS["decode"]
+    batches = [int(b) for b in args.batches.split(",")]
+    Bmax = max(batches)
+
+    t0 = time.time()
+    host_layers = [moegen.make_layer(W, layer=l) for l in range(N_LAYERS)]
+    layers = [q.DeviceLayer(L) for L in host_layers]
+    gen_s = time.time() - t0
+    expert_bytes = layers[0].blob_bytes + 12  # packed codes + scales, 3 fp32 tensor scales
+    buf = q.StepBuffers(layers[0], Bmax)
+    stream = torch.cuda.Stream()
+
+    # n_active of each step, copied on the device (no host sync inside steps)
+    bk = buf.buckets
+    na_off = bk.n_active - buf.bucket_buf.data_ptr()
+    n_active_view = buf.bucket_buf[na_off:na_off + 4].view(torch.int32)
+
+    results = {}
+    for B in batches:
+        xs = [torch.from_numpy(moegen.make_tokens(W, B, step=s, layer=B).view(np.int16).copy()).to(dev)
+              for s in range(X_POOL)]
+
+        def step(i):
+            return q.layer_forward(layers[i % N_LAYERS], buf, xs[i % X_POOL], B, stream=stream)
+
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                step(i)
+        torch.cuda.synchronize()
+
+        if args.profile_steps:
+            with torch.cuda.stream(stream):
+                for i in range(args.profile_steps):
+                    step(i)
+            torch.cuda.synchronize()
+            continue
+
+        # (1) FFN kernel time: HIP events on the launch stream around each
+        #     moe_expert_ffn call (eager launches), expert bytes from the
+        #     realised active-expert count of each step.
+        n_ev = min(args.steps, 256)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        nact = torch.zeros(n_ev, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(stream):
+            for i in range(n_ev):
+                L = layers[i % N_LAYERS]
+                d = L.desc
+                x = xs[i % X_POOL]
+                q.moe_route(d, x, B, buf.logits, buf.idx, buf.w, stream)
+                q.moe_bucket(d, buf.idx, B, buf.buckets, buf.ws, buf.ws_bytes, stream)
+                starts[i].record(stream)
+                q.moe_expert_ffn(d, x, B, buf.buckets, buf.y, buf.y_dtype, buf.ws, buf.ws_bytes,
+                                 stream)
+                ends[i].record(stream)
+                nact[i:i + 1].copy_(n_active_view)
+                q.moe_combine(d, buf.y, buf.y_dtype, buf.buckets, buf.w, B, None, buf.out, stream)
+                q.moe_expert_hist(d, buf.buckets, buf.hist, 5, 10, stream)
+        torch.cuda.synchronize()
+        ffn_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+        na = nact.cpu().numpy().astype(np.float64)
+        ffn_bytes = na * expert_bytes
+        ffn_gbs = float(ffn_bytes.sum() / (ffn_ms.sum() * 1e-3) / 1e9)
+
+        # (2) whole-step throughput: the steps captured in a HIP graph
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(X_POOL):
+                step(i)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // X_POOL)
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):  # replay() launches on the current stream
+            g.replay()
+            torch.cuda.synchronize()
+            t_start.record(stream)
+            for _ in range(reps):
+                g.replay()
+            t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_start.elapsed_time(t_end)
+        steps_done = reps * X_POOL
+        ms_step = total_ms / steps_done
+        results[B] = dict(
+            batch=B, steps=steps_done, ms_per_step=ms_step, tok_per_s=B / (ms_step * 1e-3),
+            ffn_us=float(ffn_ms.mean() * 1e3), active_experts=float(na.mean()),
+            expert_bytes_per_step=float(ffn_bytes.mean()), ffn_GBps=ffn_gbs,
+            ffn_hbm_frac=ffn_gbs / HBM_PEAK_GBS)
+        del g
+
+    if args.profile_steps:
+        print(json.dumps({"profile_run": True, "batches": batches}))
+        return
+
+    head = results[Bmax]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(W, host_layers[0], Bmax, args.cpu_sample_steps)
+
+    line = {
+        "metric": "MoE-layer decode tok/s + expert-weight HBM GB/s (% peak); prefill TFLOP/s",
+        "value": round(head["tok_per_s"], 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode step, batch {Bmax}: 128 experts, top-8, hidden 2048, "
+                        "intermediate 768, NVFP4 gate/up/down, bf16 activations",
+            "batch": Bmax, "experts": 128, "top_k": 8, "hidden": 2048, "intermediate": 768,
+            "weights": "nvfp4", "layers_cycled": N_LAYERS, "hip_graph": True,
+        },
+        "roofline": {
+            "kernel": "expert FFN (k_gemv_gateup_nvfp4 + k_gemv_down_nvfp4)",
+            "bound": "hbm",
+            "achieved": round(head["ffn_GBps"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["ffn_hbm_frac"], 4),
+            "traffic": None,
+        },
+        "per_batch": [
+            {k: (round(v, 4) if isinstance(v, float) else v) for k, v in results[b].items()}
+            for b in batches
+        ],
+        "cpu_baseline": cpu,
+        "setup_s": round(gen_s, 1),
+    }
+    print(json.dumps(line))
+
+
+def cpu_baseline(W, L, B, n_steps):
+    """The oracle as it stands, single-threaded, on a bounded sample: n_steps
+    decode steps of batch B on one layer.  Reported in the same unit."""
+    import moegen
+    import oracle
+    t = time.time()
+    for s in range(n_steps):
+        x = moegen.make_tokens(W, B, step=10_000 + s)
+        oracle.layer(x, L)
+    dt = time.time() - t
+    return {"value": round(B * n_steps / dt, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_steps} decode steps of batch {B} on one layer, single-threaded "
+                      f"plain C in double precision ({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -4,12 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "common.h"
-
-namespace moe {
-hipError_t launch_gemv_ffn(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
-                           float* h, void* y, int y_dtype, hipStream_t s);
-}
+#include "gemv_common.h"
 
 namespace {
 
@@ -227,7 +222,15 @@ moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   CHECK_PTR(x, W); CHECK_PTR(y, W); CHECK_PTR(ws, W); CHECK_PTR(L->experts, W);
   size_t need = ffn_ws(L, T);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
-  return hip_status(W, moe::launch_gemv_ffn(L, x, b, (float*)ws, y, y_dtype, stream));
+  // Worst-case number of active experts; workgroups past n_active exit.
+  const int max_slots = (int)((T * L->k < L->E) ? T * L->k : L->E);
+  float* h = (float*)ws;
+  hipError_t e = moe::launch_gemv_gateup(L, x, b, max_slots, h, stream);
+  if (e == hipSuccess) {
+    e = (L->fmt_down == MOE_FMT_NVFP4) ? moe::launch_gemv_down(L, h, b, max_slots, y, y_dtype, stream)
+                                       : moe::launch_gemv_down_q6k(L, h, b, max_slots, y, y_dtype, stream);
+  }
+  return hip_status(W, e);
 }
 
 moe_status moe_combine(const moe_layer_desc* L, const void* y, int32_t y_dtype,

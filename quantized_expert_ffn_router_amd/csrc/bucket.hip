@@ -226,6 +226,90 @@ __global__ __launch_bounds__(kThreads) void k_bucket_single(const int32_t* __res
   scatter_chunk(idx, 0, A, E, nbits, cur, ebase, sorted, pos);
 }
 
+// A <= 64 * kWaveRounds: one wavefront does everything (decode-size steps).
+constexpr int kWaveRounds = 4;
+
+__global__ __launch_bounds__(64) void k_bucket_wave(const int32_t* __restrict__ idx, int A,
+                                                    int E, int nbits,
+                                                    uint32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ active,
+                                                    int32_t* __restrict__ n_active,
+                                                    int32_t* __restrict__ sorted,
+                                                    int32_t* __restrict__ pos) {
+  __shared__ int cnt[1024];
+  __shared__ int cur[1024];
+  const int lane = threadIdx.x;
+  int key[kWaveRounds];
+#pragma unroll
+  for (int r = 0; r < kWaveRounds; ++r) {
+    const int a = r * 64 + lane;
+    key[r] = (a < A) ? idx[a] : 0;
+  }
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint64_t peers[kWaveRounds];
+#pragma unroll
+  for (int r = 0; r < kWaveRounds; ++r) {
+    const bool valid = r * 64 + lane < A;
+    peers[r] = match_key(key[r], valid, nbits);
+    if (valid && (peers[r] >> lane) == 1ull) cnt[key[r]] += __popcll(peers[r]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // Exclusive scans over experts: lane owns experts [lane*per, lane*per+per).
+  const int per = (E + 63) / 64;
+  const int e0 = lane * per;
+  int s_cnt = 0, s_act = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) { s_cnt += cnt[e]; s_act += cnt[e] > 0; }
+  }
+  int inc_cnt = s_cnt, inc_act = s_act;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int oc = __shfl_up(inc_cnt, off), oa = __shfl_up(inc_act, off);
+    if (lane >= off) { inc_cnt += oc; inc_act += oa; }
+  }
+  int run = inc_cnt - s_cnt, arun = inc_act - s_act;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int c = cnt[e];
+      counts[e] = (uint32_t)c;
+      offsets[e] = run;
+      cur[e] = run;
+      if (c > 0) active[arun++] = e;
+      run += c;
+    }
+  }
+  if (lane == 63) { offsets[E] = inc_cnt; *n_active = inc_act; }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int r = 0; r < kWaveRounds; ++r) {
+    const int a = r * 64 + lane;
+    const bool valid = a < A;
+    const int rank = __popcll(peers[r] & lanemask_lt());
+    const int base = valid ? cur[key[r]] : 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (valid && (peers[r] >> lane) == 1ull) cur[key[r]] = base + __popcll(peers[r]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (valid) {
+      sorted[base + rank] = a;
+      pos[a] = base + rank;
+    }
+  }
+}
+
 __global__ void k_hist(const uint32_t* __restrict__ counts, int E, uint32_t* __restrict__ hist,
                        int ds, int us) {
   int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -253,6 +337,11 @@ hipError_t launch_bucket(const int32_t* idx, int64_t A, int E, const moe_buckets
                          hipStream_t s) {
   const int nbits = key_bits(E);
   int64_t nb = (A + kChunk - 1) / kChunk;
+  if (A <= 64 * kWaveRounds) {
+    hipLaunchKernelGGL(k_bucket_wave, dim3(1), dim3(64), 0, s, idx, (int)A, E, nbits, b->counts,
+                       b->offsets, b->active, b->n_active, b->sorted_asg, b->asg_pos);
+    return hipGetLastError();
+  }
   if (nb <= 1) {
     hipLaunchKernelGGL(k_bucket_single, dim3(1), dim3(kThreads), 0, s, idx, A, E, nbits,
                        b->counts, b->offsets, b->active, b->n_active, b->sorted_asg, b->asg_pos);

@@ -1,0 +1,118 @@
+// gemv_common.h -- shared pieces of the decode-size expert kernels.
+//
+// Routed experts are block-quantized (NVFP4; GGUF Q6_K in the DQ6_K packs:
+// basalt.jgulfo.com, sections "Models" and "Quick start"), and a token touches
+// only the experts it selected ("Expert tiers").  With 1..8 tokens per step
+// (one per request slot) the expert FFN is bound by reading each active
+// expert's weight bytes once from HBM, so these kernels stream the packed
+// codes with 16-byte loads and dequantize in registers:
+//   - grid = (row blocks of 64, slots of the active-expert list); a workgroup
+//     whose slot is past n_active exits at once, so no workgroup is spent on
+//     an expert without tokens;
+//   - lane l of every wave owns output row 64*blockIdx.x + l: a wave-wide
+//     16-byte load reads the same 32-element K-slice of 64 consecutive rows,
+//     which the packed blob stores contiguously -- no cross-lane reduction;
+//   - K is split into groups (128 elements NVFP4, 256 Q6_K); wave w takes the
+//     GPW consecutive groups starting at (s*NW + w)*GPW for s = 0, 1, ...
+//     All of a wave's weight loads are issued before the token rows are
+//     gathered, so the gather latency hides under the weight fetch;
+//   - the NW partial sums of a row are added through LDS in wave order.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxMT = 8;  // tokens per pass (register arrays are sized for this)
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// 8 E2M1 codes of a 32-bit word (element 2b in the low nibble of byte b) ->
+// 8 exact floats (gfx950 packed FP4 -> F32 conversion, scale 1.0).
+__device__ __forceinline__ void e2m1x8_f32(uint32_t c, float* o) {
+  v2f_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+  v2f_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+  v2f_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+  v2f_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+  o[0] = p0.x; o[1] = p0.y; o[2] = p1.x; o[3] = p1.y;
+  o[4] = p2.x; o[5] = p2.y; o[6] = p3.x; o[7] = p3.y;
+}
+
+// Same codes -> 4 bf16 pairs (exact: E2M1 values have 2 significant bits).
+__device__ __forceinline__ void e2m1x8_bf16(uint32_t c, v2bf_t* o) {
+  o[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0);
+  o[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 1);
+  o[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 2);
+  o[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 3);
+}
+
+__device__ __forceinline__ v2bf_t as_v2bf(uint32_t u) { return __builtin_bit_cast(v2bf_t, u); }
+
+__device__ __forceinline__ float dot16_f32(const float* w, const float* x) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s = fmaf(w[i], x[i], s);
+  return s;
+}
+
+__device__ __forceinline__ void load_f32x16(const float* p, float* xv) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+  float4 a0 = q[0], a1 = q[1], a2 = q[2], a3 = q[3];
+  xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+  xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+  xv[8] = a2.x; xv[9] = a2.y; xv[10] = a2.z; xv[11] = a2.w;
+  xv[12] = a3.x; xv[13] = a3.y; xv[14] = a3.z; xv[15] = a3.w;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_y(void* y, size_t i, float v) {
+  if (BF16) reinterpret_cast<uint16_t*>(y)[i] = f32_to_bf16_rne(v);
+  else reinterpret_cast<float*>(y)[i] = v;
+}
+
+// Stage rows row0 .. row0+mt of h (fp32 [A][K], sorted order) into LDS.
+__device__ __forceinline__ void stage_rows_f32(const float* __restrict__ hin, int K, int row0,
+                                               int mt, float* sm, int nthreads) {
+  const int vpr = K >> 2;
+  for (int i = threadIdx.x; i < mt * vpr; i += nthreads) {
+    int r = i / vpr, c = i - r * vpr;
+    reinterpret_cast<float4*>(sm + (size_t)r * K)[c] =
+        reinterpret_cast<const float4*>(hin + (size_t)(row0 + r) * K)[c];
+  }
+}
+
+// Per-slot header shared by the kernels: expert id, token count and offset.
+struct SlotInfo {
+  int e, cnt, base;
+  moe_expert_ref ref;
+};
+
+__device__ __forceinline__ bool slot_info(const int32_t* __restrict__ active,
+                                          const int32_t* __restrict__ n_active,
+                                          const uint32_t* __restrict__ counts,
+                                          const int32_t* __restrict__ offsets,
+                                          const moe_expert_ref* __restrict__ experts,
+                                          SlotInfo* si) {
+  const int slot = blockIdx.y;
+  if (slot >= *n_active) return false;
+  si->e = active[slot];
+  si->cnt = (int)counts[si->e];
+  si->base = offsets[si->e];
+  si->ref = experts[si->e];
+  return true;
+}
+
+// Launch helpers (one per kernel family), defined in their .hip files.
+hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
+                              int max_slots, float* h, hipStream_t s);
+hipError_t launch_gemv_down(const moe_layer_desc* L, const float* h, const moe_buckets* b,
+                            int max_slots, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemv_down_q6k(const moe_layer_desc* L, const float* h, const moe_buckets* b,
+                                int max_slots, void* y, int y_dtype, hipStream_t s);
+
+}  // namespace moe

@@ -53,16 +53,29 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
 #pragma unroll
   for (int q = 0; q < EB; ++q) wrow[q] = Wr + (size_t)min(e0 + q, E - 1) * H;
 
-#pragma unroll 2
-  for (int h = lane; h < H; h += 64) {
-    double w[EB];
+  // Router weights are fetched CH strides at a time (all loads in flight
+  // before the first use); terms are still added in ascending h.
+  constexpr int CH = (EB == 1) ? 32 : 8;
+  for (int h0 = lane; h0 < H; h0 += 64 * CH) {
+    float wv[CH][EB];
 #pragma unroll
-    for (int q = 0; q < EB; ++q) w[q] = (double)wrow[q][h];
+    for (int c = 0; c < CH; ++c) {
+      const int h = h0 + 64 * c;
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
-      double xv = (double)bf16_to_f32(xs[i * H + h]);
+      for (int q = 0; q < EB; ++q) wv[c][q] = (h < H) ? wrow[q][h] : 0.0f;
+    }
 #pragma unroll
-      for (int q = 0; q < EB; ++q) acc[i * EB + q] = __fma_rn(xv, w[q], acc[i * EB + q]);
+    for (int c = 0; c < CH; ++c) {
+      const int h = h0 + 64 * c;
+      if (h < H) {
+#pragma unroll
+        for (int i = 0; i < TB; ++i) {
+          const double xv = (double)bf16_to_f32(xs[i * H + h]);
+#pragma unroll
+          for (int q = 0; q < EB; ++q)
+            acc[i * EB + q] = __fma_rn(xv, (double)wv[c][q], acc[i * EB + q]);
+        }
+      }
     }
   }
 
@@ -159,6 +172,77 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   }
 }
 
+// E <= 64*NV: one wavefront per token; every logit's rank in the order
+// (logit desc, expert asc) is counted against all E logits (broadcast from
+// LDS), so the k winners are found in one pass with no serial rounds.
+template <int NV>
+__global__ __launch_bounds__(256) void k_topk_rank(const float* __restrict__ logits, int T,
+                                                   int E, int k, int renorm,
+                                                   int32_t* __restrict__ idx,
+                                                   float* __restrict__ wout) {
+  __shared__ __align__(16) float lv[4][64 * NV];
+  __shared__ float topv[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float* l = logits + (size_t)t * E;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (e < E) ? l[e] : -INFINITY;
+    lv[wave][e] = v[i];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int rk[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) rk[i] = 0;
+  const float4* row = reinterpret_cast<const float4*>(lv[wave]);
+  for (int e4 = 0; e4 < (E + 3) / 4; ++e4) {
+    const float4 u4 = row[e4];
+    const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e2 = 4 * e4 + c;
+      if (e2 < E) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int e = lane + 64 * i;
+          rk[i] += (u[c] > v[i] || (u[c] == v[i] && e2 < e)) ? 1 : 0;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (lane + 64 * i < E && rk[i] == 0) topv[wave] = v[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float top = topv[wave];
+  float ex[NV];
+  float den = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const bool valid = lane + 64 * i < E;
+    ex[i] = (valid && rk[i] < k) ? expf(v[i] - top) : 0.0f;
+    if (renorm) den += ex[i];
+    else if (valid) den += expf(v[i] - top);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E && rk[i] < k) {
+      idx[(size_t)t * k + rk[i]] = e;
+      wout[(size_t)t * k + rk[i]] = ex[i] / den;
+    }
+  }
+}
+
 template <int TB, int EB>
 hipError_t launch_router_t(const uint16_t* x, int64_t T, int H, const float* Wr,
                            const float* bias, int E, float* logits, hipStream_t s) {
@@ -192,7 +276,14 @@ hipError_t launch_router(const uint16_t* x, int64_t T, int H, const float* Wr,
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renorm, int32_t* idx,
                        float* w, hipStream_t s) {
   dim3 grid((unsigned)((T + 3) / 4));
-  hipLaunchKernelGGL(k_topk, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk_rank<1>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
+  else if (E <= 128)
+    hipLaunchKernelGGL(k_topk_rank<2>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk_rank<4>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
+  else
+    hipLaunchKernelGGL(k_topk, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
   return hipGetLastError();
 }
 

@@ -105,3 +105,11 @@ def test_equal_logits_tie_to_lower_index():
     assert np.allclose(g["w"], 1.0 / w.k, atol=0)
     check_route(g, L0, x)
     check_buckets(g["buckets"], g["idx"], w.E)
+
+
+def test_many_experts_iterative_topk_and_single_block_bucket():
+    # E = 512 > 256 takes the iterative top-k; 100 x 4 = 400 assignments take
+    # the one-workgroup bucket kernel.
+    w, L = layer("wide", E=512, k=4, H=256, I=128, T=100)
+    x = moegen.make_tokens(w, w.T)
+    check_layer(L, x)
