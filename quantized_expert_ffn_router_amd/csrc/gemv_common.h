@@ -6,17 +6,19 @@
 // (one per request slot) the expert FFN is bound by reading each active
 // expert's weight bytes once from HBM, so these kernels stream the packed
 // codes with 16-byte loads and dequantize in registers:
-//   - grid = (row blocks of 64, slots of the active-expert list); a workgroup
-//     whose slot is past n_active exits at once, so no workgroup is spent on
-//     an expert without tokens;
+//   - grid = (row blocks of 64, slots of the active-expert list[, matrix]); a
+//     workgroup whose slot is past n_active exits at once, so no workgroup is
+//     spent on an expert without tokens;
 //   - lane l of every wave owns output row 64*blockIdx.x + l: a wave-wide
 //     16-byte load reads the same 32-element K-slice of 64 consecutive rows,
 //     which the packed blob stores contiguously -- no cross-lane reduction;
-//   - K is split into groups (128 elements NVFP4, 256 Q6_K); wave w takes the
-//     GPW consecutive groups starting at (s*NW + w)*GPW for s = 0, 1, ...
-//     All of a wave's weight loads are issued before the token rows are
-//     gathered, so the gather latency hides under the weight fetch;
-//   - the NW partial sums of a row are added through LDS in wave order.
+//   - K is cut into groups (128 elements NVFP4, 256 Q6_K) and split over the
+//     S waves of a workgroup; each wave streams its GPS = groups/S groups
+//     through a ring of D register slots (the loads of D groups are always in
+//     flight), so a workgroup never holds more than D groups per lane and
+//     every workgroup of the launch can be resident at once.  S is chosen on
+//     the host from the number of workgroups (small batches split K more);
+//   - the S partial sums of a row are added through LDS in wave order.
 #pragma once
 
 #include "common.h"
@@ -27,6 +29,24 @@ typedef float v2f_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxMT = 8;  // tokens per pass (register arrays are sized for this)
+
+// Loads through the global address space (the expert blob pointer comes from
+// a table, so the compiler would otherwise emit flat loads).
+// (Flat loads would also count against the LDS wait counter, so every LDS
+// wait in the compute loop would wait for the weight prefetch too.)
+// (These helpers only exist in device code; the host pass never sees them.)
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __attribute__((address_space(1))) uint4 g_uint4;
+typedef __attribute__((address_space(1))) uint2 g_uint2;
+typedef __attribute__((address_space(1))) uint16_t g_u16;
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *(const g_uint4*)(uintptr_t)p; }
+__device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *(const g_uint2*)(uintptr_t)p; }
+__device__ __forceinline__ uint16_t ld2(const uint8_t* p) { return *(const g_u16*)(uintptr_t)p; }
+#else
+__device__ uint4 ld16(const uint8_t* p);
+__device__ uint2 ld8(const uint8_t* p);
+__device__ uint16_t ld2(const uint8_t* p);
+#endif
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -52,6 +72,12 @@ __device__ __forceinline__ void e2m1x8_bf16(uint32_t c, v2bf_t* o) {
 }
 
 __device__ __forceinline__ v2bf_t as_v2bf(uint32_t u) { return __builtin_bit_cast(v2bf_t, u); }
+
+// Two floats -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ v2bf_t to_v2bf(float a, float b) {
+  v2f_t f = {a, b};
+  return __builtin_convertvector(f, v2bf_t);
+}
 
 __device__ __forceinline__ float dot16_f32(const float* w, const float* x) {
   float s = 0.0f;
@@ -107,12 +133,37 @@ __device__ __forceinline__ bool slot_info(const int32_t* __restrict__ active,
   return true;
 }
 
+// E4M3 scale bytes 2i, 2i+1 (lo) or 2i+2, 2i+3 (hi) of a word -> fp32 pair, exact
+// (gfx950 converts OCP E4M3).
+template <bool HI>
+__device__ __forceinline__ v2f_t e4m3x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// The 8 E4M3 scales of a group (one per 16-element block) -> fp32.
+__device__ __forceinline__ void e4m3x8(const uint2& s, float* sc) {
+  v2f_t a = e4m3x2<false>(s.x), b = e4m3x2<true>(s.x);
+  v2f_t c = e4m3x2<false>(s.y), e = e4m3x2<true>(s.y);
+  sc[0] = a.x; sc[1] = a.y; sc[2] = b.x; sc[3] = b.y;
+  sc[4] = c.x; sc[5] = c.y; sc[6] = e.x; sc[7] = e.y;
+}
+
+// Split of NG K-groups over S waves: the largest divisor of NG that is at most
+// max_s and keeps items * waves_per_item * S within the wave budget.
+inline int choose_split(int items, int waves_per_item, int NG, int max_s) {
+  const int budget = 4096;
+  int best = 1;
+  for (int s = 1; s <= max_s && s <= NG; ++s)
+    if (NG % s == 0 && (long)items * waves_per_item * s <= budget) best = s;
+  return best;
+}
+
 // Launch helpers (one per kernel family), defined in their .hip files.
+// mt_max: tokens gathered per pass (<= kMaxMT; an expert gets at most T).
 hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
-                              int max_slots, float* h, hipStream_t s);
+                              int max_slots, int mt_max, float* h, hipStream_t s);
 hipError_t launch_gemv_down(const moe_layer_desc* L, const float* h, const moe_buckets* b,
-                            int max_slots, void* y, int y_dtype, hipStream_t s);
-hipError_t launch_gemv_down_q6k(const moe_layer_desc* L, const float* h, const moe_buckets* b,
-                                int max_slots, void* y, int y_dtype, hipStream_t s);
+                            int max_slots, int mt_max, void* y, int y_dtype, hipStream_t s);
+
 
 }  // namespace moe

@@ -1,136 +1,248 @@
-// gemv_down.hip -- decode-size down projection of the routed experts with
-// NVFP4 weights: y[p] = (h[p] . dq(Wd)^T) for each sorted assignment p of the
-// expert.  h stays fp32 (staged in LDS); E2M1 pairs are converted to fp32 with
-// the gfx950 packed FP4 conversion and each 16-element block sum is scaled by
-// its E4M3 scale, the per-tensor scale by the total.  Work split:
-// gemv_common.h.
+// gemv_down.hip -- decode-size down projection of the routed experts:
+// y[p] = h[p] . dq(Wd)^T for each sorted assignment p of an active expert.
+//   NVFP4: E2M1 codes, E4M3 scale per 16 elements, fp32 per-tensor scale.
+//   Q6_K-style (the DQ6_K packs of basalt.jgulfo.com, "Quick start"):
+//     256-element superblocks, 6-bit codes q in a low-nibble plane and a
+//     2-bit plane, int8 sub-scale per 16 elements, fp16 scale d:
+//     w = d * sc * (q - 32).
+// Weights are decoded exactly to bf16 (E2M1 has 2 significant bits, q - 32 is
+// a 6-bit integer) and h is staged in LDS as a bf16 pair hi + lo (h - hi - lo
+// is below 2^-16 |h|), so v_dot2_f32_bf16 on (w, hi) and (w, lo) gives
+// fp32-grade products with fp32 accumulation.  Each 16-element block sum is
+// scaled by its block scale (E4M3, or d * sc).  A workgroup owns 64 rows of
+// one active expert; its S waves split K into 128-element groups
+// (gemv_common.h), loads kept D groups ahead in group order.
 #include "gemv_common.h"
 
 namespace moe {
 
 namespace {
 
-template <int NW, int GPW, bool BF16>
-__global__ __launch_bounds__(NW * 64) void k_gemv_down_nvfp4(
-    const float* __restrict__ hin, int H, int I, int mt_max,
-    const moe_expert_ref* __restrict__ experts, size_t off_dq, size_t off_ds,
-    const uint32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-    void* __restrict__ y) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* hs = reinterpret_cast<float*>(smem);                  // [mt_max][I]
-  float* red = hs + (size_t)mt_max * I;                        // [NW][MT][64]
+// Raw bytes of one 128-element group of a row.
+template <int FMT>
+struct Group;
 
-  SlotInfo si;
-  if (!slot_info(active, n_active, counts, offsets, experts, &si)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = blockIdx.x * 64 + lane;
-  const bool row_ok = n < H;
-  const size_t nc = row_ok ? (size_t)n : 0;
-  const uint8_t* blob = (const uint8_t*)si.ref.blob;
-  const uint8_t* dq = blob + off_dq;
-  const uint8_t* ds = blob + off_ds;
-  const int NG = I >> 7;
-  const int n_sets = (NG + NW * GPW - 1) / (NW * GPW);
+template <>
+struct Group<MOE_FMT_NVFP4> {
+  uint4 c[4];  // 64 code bytes
+  uint2 s;     // 8 E4M3 scales
+};
 
-  for (int c0 = 0; c0 < si.cnt; c0 += mt_max) {
-    const int mt = min(mt_max, si.cnt - c0);
-    float acc[kMaxMT];
+template <>
+struct Group<MOE_FMT_Q6K> {
+  uint4 ql[4];  // low nibbles of the half superblock
+  uint4 qh[2];  // 2-bit high parts
+  uint2 sc;     // 8 int8 sub-scales
+  uint32_t d;   // fp16 superblock scale
+};
+
+struct Planes {
+  const uint8_t* a;  // NVFP4 codes | Q6_K ql
+  const uint8_t* b;  // NVFP4 scales | Q6_K qh
+  const uint8_t* c;  // Q6_K sc
+  const uint8_t* d;  // Q6_K d
+};
+
+__device__ __forceinline__ void load_group(Group<MOE_FMT_NVFP4>& r, const Planes& P, int H,
+                                           size_t nc, int g) {
 #pragma unroll
-    for (int t = 0; t < kMaxMT; ++t) acc[t] = 0.0f;
-    for (int s = 0; s < n_sets; ++s) {
-      const int g0 = (s * NW + wave) * GPW;
-      uint4 cq[GPW][4];
-      uint2 sc[GPW];
+  for (int q = 0; q < 4; ++q) r.c[q] = ld16(P.a + (((size_t)(4 * g + q)) * H + nc) * 16);
+  r.s = ld8(P.b + ((size_t)g * H + nc) * 8);
+}
+
+__device__ __forceinline__ void load_group(Group<MOE_FMT_Q6K>& r, const Planes& P, int H,
+                                           size_t nc, int g) {
+  const int sb = g >> 1, half = g & 1;  // half superblock
 #pragma unroll
-      for (int gi = 0; gi < GPW; ++gi) {
-        const int g = g0 + gi;
-        if (row_ok && g < NG) {
+  for (int q = 0; q < 4; ++q) r.ql[q] = ld16(P.a + (((size_t)(4 * g + q)) * H + nc) * 16);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            cq[gi][q] = *reinterpret_cast<const uint4*>(dq + (((size_t)(4 * g + q)) * H + nc) * 16);
-          sc[gi] = *reinterpret_cast<const uint2*>(ds + ((size_t)g * H + nc) * 8);
-        } else {
+  for (int q = 0; q < 2; ++q) r.qh[q] = ld16(P.b + (((size_t)(2 * g + q)) * H + nc) * 16);
+  r.sc = ld8(P.c + ((size_t)sb * H + nc) * 16 + 8 * half);
+  r.d = ld2(P.d + ((size_t)sb * H + nc) * 2);
+}
+
+// Exact bf16 pairs w[b][0..8) of the 8 blocks of 16 and their fp32 scales.
+__device__ __forceinline__ void decode_group(const Group<MOE_FMT_NVFP4>& r, float ts,
+                                             v2bf_t (*w)[8], float* sc) {
+  e4m3x8(r.s, sc);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) cq[gi][q] = make_uint4(0, 0, 0, 0);
-          sc[gi] = make_uint2(0, 0);
-        }
-      }
-      if (s == 0) {
-        stage_rows_f32(hin, I, si.base + c0, mt, hs, NW * 64);
-        __syncthreads();
-      }
+  for (int b = 0; b < 8; ++b) {
+    sc[b] *= ts;
+    e2m1x8_bf16(word_of(r.c[b >> 1], (b & 1) * 2), w[b]);
+    e2m1x8_bf16(word_of(r.c[b >> 1], (b & 1) * 2 + 1), w[b] + 4);
+  }
+}
+
+__device__ __forceinline__ void decode_group(const Group<MOE_FMT_Q6K>& r, float /*ts*/,
+                                             v2bf_t (*w)[8], float* sc) {
+  const float d = f16_to_f32((uint16_t)r.d);
 #pragma unroll
-      for (int gi = 0; gi < GPW; ++gi) {
-        const int g = g0 + gi;
-        if (g >= NG) break;
+  for (int j = 0; j < 8; ++j) {
+    sc[j] = d * (float)(int8_t)((((j < 4) ? r.sc.x : r.sc.y) >> (8 * (j & 3))) & 0xffu);
+    const uint32_t lo0 = word_of(r.ql[j >> 1], (j & 1) * 2);      // elements 0..7
+    const uint32_t lo1 = word_of(r.ql[j >> 1], (j & 1) * 2 + 1);  // elements 8..15
+    const uint32_t hi = word_of(r.qh[j >> 2], j & 3);             // 2 bits per element
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const uint32_t sw = (b < 4) ? sc[gi].x : sc[gi].y;
-          const float scale = e4m3_to_f32((sw >> (8 * (b & 3))) & 0xffu);
-          float w[16];
-          e2m1x8_f32(word_of(cq[gi][b >> 1], (b & 1) * 2), w);
-          e2m1x8_f32(word_of(cq[gi][b >> 1], (b & 1) * 2 + 1), w + 8);
-#pragma unroll
-          for (int t = 0; t < kMaxMT; ++t) {
-            if (t < mt) {
-              float xv[16];
-              load_f32x16(hs + (size_t)t * I + 128 * g + 16 * b, xv);
-              acc[t] = fmaf(dot16_f32(w, xv), scale, acc[t]);
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < kMaxMT; ++t)
-      if (t < mt) red[(wave * kMaxMT + t) * 64 + lane] = acc[t];
-    __syncthreads();
-    for (int o = tid; o < mt * 64; o += NW * 64) {
-      const int t = o >> 6, r = o & 63;
-      const int n2 = blockIdx.x * 64 + r;
-      if (n2 < H) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) sum += red[(w * kMaxMT + t) * 64 + r];
-        store_y<BF16>(y, (size_t)(si.base + c0 + t) * H + n2, sum * si.ref.ts_down);
-      }
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t lw = (p < 4) ? lo0 : lo1;
+      const uint32_t byte = (lw >> (8 * (p & 3))) & 0xffu;
+      const int q0 = (int)((byte & 15u) | (((hi >> (4 * p)) & 3u) << 4));
+      const int q1 = (int)((byte >> 4) | (((hi >> (4 * p + 2)) & 3u) << 4));
+      w[j][p] = to_v2bf((float)(q0 - 32), (float)(q1 - 32));
     }
   }
 }
 
-template <int NW, int GPW>
+template <int FMT, int GP, int D>
+__device__ __forceinline__ void down_pass(const uint16_t* hsh, const uint16_t* hsl, int H, int I,
+                                          size_t nc, const Planes& P, float ts, int gb, int mt,
+                                          float* myred) {
+  Group<FMT> r[GP];
+#pragma unroll
+  for (int gi = 0; gi < GP && gi < D; ++gi) {
+    load_group(r[gi], P, H, nc, gb + gi);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int gi = 0; gi < GP; ++gi) {
+    if (gi + D < GP) {
+      load_group(r[gi + D], P, H, nc, gb + gi + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int g = gb + gi;
+    v2bf_t w[8][8];
+    float sc[8];
+    decode_group(r[gi], ts, w, sc);
+    for (int t = 0; t < mt; ++t) {
+      const uint4* ph = reinterpret_cast<const uint4*>(hsh + (size_t)t * I + 128 * g);
+      const uint4* pl = reinterpret_cast<const uint4*>(hsl + (size_t)t * I + 128 * g);
+      float a = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint4 h0 = ph[2 * b], h1 = ph[2 * b + 1], l0 = pl[2 * b], l1 = pl[2 * b + 1];
+        const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        float p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][i], as_v2bf(hw[i]), p, false);
+          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][i], as_v2bf(lw[i]), p, false);
+        }
+        a = fmaf(p, sc[b], a);
+      }
+      myred[t * 64 + lane] += a;
+    }
+  }
+}
+
+template <int FMT, int GP, int D, bool BF16>
+__global__ __launch_bounds__(512, 3) void k_gemv_down(
+    const float* __restrict__ hin, int H, int I, int mt_max, int S, int gps_total, Planes P0,
+    const moe_expert_ref* __restrict__ experts, const uint32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
+    const int32_t* __restrict__ n_active, void* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* hsh = reinterpret_cast<uint16_t*>(smem);                      // [mt_max][I] hi
+  uint16_t* hsl = hsh + (size_t)mt_max * I;                               // [mt_max][I] lo
+  float* red = reinterpret_cast<float*>(hsl + (size_t)mt_max * I);        // [S][mt_max][64]
+
+  SlotInfo si;
+  if (!slot_info(active, n_active, counts, offsets, experts, &si)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nthreads = S * 64;
+  const int n = blockIdx.x * 64 + lane;
+  const size_t nc = (n < H) ? (size_t)n : 0;  // rows past the end read row 0, never stored
+  const uintptr_t blob = (uintptr_t)si.ref.blob;
+  const Planes P = {(const uint8_t*)(blob + (uintptr_t)P0.a), (const uint8_t*)(blob + (uintptr_t)P0.b),
+                    (const uint8_t*)(blob + (uintptr_t)P0.c), (const uint8_t*)(blob + (uintptr_t)P0.d)};
+  const float ts = (FMT == MOE_FMT_NVFP4) ? si.ref.ts_down : 1.0f;
+  const int gb = wave * gps_total;
+  float* myred = red + (size_t)wave * mt_max * 64;
+
+  for (int c0 = 0; c0 < si.cnt; c0 += mt_max) {
+    const int mt = min(mt_max, si.cnt - c0);
+    // Stage h rows as hi/lo bf16 pairs.
+    const int vpr = I >> 2;
+    for (int i = tid; i < mt * vpr; i += nthreads) {
+      const int r = i / vpr, c = i - r * vpr;
+      const float4 v = reinterpret_cast<const float4*>(hin + (size_t)(si.base + c0 + r) * I)[c];
+      const v2bf_t h01 = to_v2bf(v.x, v.y), h23 = to_v2bf(v.z, v.w);
+      const v2f_t f01 = __builtin_convertvector(h01, v2f_t), f23 = __builtin_convertvector(h23, v2f_t);
+      const v2bf_t l01 = to_v2bf(v.x - f01.x, v.y - f01.y), l23 = to_v2bf(v.z - f23.x, v.w - f23.y);
+      uint2* dh = reinterpret_cast<uint2*>(hsh + (size_t)r * I) + c;
+      uint2* dl = reinterpret_cast<uint2*>(hsl + (size_t)r * I) + c;
+      *dh = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+      *dl = make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
+    }
+    for (int t = 0; t < mt; ++t) myred[t * 64 + lane] = 0.0f;
+    __syncthreads();
+    for (int sg = 0; sg < gps_total; sg += GP)
+      down_pass<FMT, GP, D>(hsh, hsl, H, I, nc, P, ts, gb + sg, mt, myred);
+    __syncthreads();
+    for (int o = tid; o < mt * 64; o += nthreads) {
+      const int t = o >> 6, r = o & 63;
+      const int n2 = blockIdx.x * 64 + r;
+      if (n2 < H) {
+        float sum = 0.0f;
+        for (int w = 0; w < S; ++w) sum += red[(w * mt_max + t) * 64 + r];
+        store_y<BF16>(y, (size_t)(si.base + c0 + t) * H + n2, sum);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int FMT, int GP>
 hipError_t down_t(const moe_layer_desc* L, const float* h, const moe_buckets* b, int max_slots,
-                  void* y, int y_dtype, hipStream_t s) {
+                  int mt_max, int S, int gps_total, void* y, int y_dtype, hipStream_t s) {
+  constexpr int D = GP < 2 ? GP : 2;
   const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
-  const int mt_max = min(kMaxMT, 8192 / L->I);  // fp32 h tile <= 32 KiB
+  Planes P;
+  if (FMT == MOE_FMT_NVFP4) {
+    P = {(const uint8_t*)lay.down_q, (const uint8_t*)lay.down_s, nullptr, nullptr};
+  } else {
+    P = {(const uint8_t*)lay.down_ql, (const uint8_t*)lay.down_qh, (const uint8_t*)lay.down_sc,
+         (const uint8_t*)lay.down_d};
+  }
   dim3 grid((unsigned)((L->H + 63) / 64), (unsigned)max_slots);
-  size_t lds = sizeof(float) * ((size_t)mt_max * L->I + NW * kMaxMT * 64);
+  size_t lds = (size_t)mt_max * L->I * 4 + sizeof(float) * (size_t)S * mt_max * 64;
   if (y_dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL((k_gemv_down_nvfp4<NW, GPW, true>), grid, dim3(NW * 64), lds, s, h, L->H,
-                       L->I, mt_max, L->experts, lay.down_q, lay.down_s, b->counts, b->offsets,
+    hipLaunchKernelGGL((k_gemv_down<FMT, GP, D, true>), grid, dim3(S * 64), lds, s, h, L->H,
+                       L->I, mt_max, S, gps_total, P, L->experts, b->counts, b->offsets,
                        b->active, b->n_active, y);
   else
-    hipLaunchKernelGGL((k_gemv_down_nvfp4<NW, GPW, false>), grid, dim3(NW * 64), lds, s, h, L->H,
-                       L->I, mt_max, L->experts, lay.down_q, lay.down_s, b->counts, b->offsets,
+    hipLaunchKernelGGL((k_gemv_down<FMT, GP, D, false>), grid, dim3(S * 64), lds, s, h, L->H,
+                       L->I, mt_max, S, gps_total, P, L->experts, b->counts, b->offsets,
                        b->active, b->n_active, y);
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t down_fmt(const moe_layer_desc* L, const float* h, const moe_buckets* b, int max_slots,
+                    int mt_max, void* y, int y_dtype, hipStream_t s) {
+  const int NG = L->I / 128;
+  const int RB = (L->H + 63) / 64;
+  const int S = choose_split(max_slots * RB, 1, NG, 8);  // <= 8 waves
+  const int gps_total = NG / S;
+  const int gp_max = (FMT == MOE_FMT_Q6K) ? 2 : 4;  // register budget (no spills)
+  int GP = gps_total > gp_max ? gp_max : gps_total;
+  while (gps_total % GP) --GP;
+  switch (GP) {
+    case 1: return down_t<FMT, 1>(L, h, b, max_slots, mt_max, S, gps_total, y, y_dtype, s);
+    case 2: return down_t<FMT, 2>(L, h, b, max_slots, mt_max, S, gps_total, y, y_dtype, s);
+    case 3: return down_t<FMT, 3>(L, h, b, max_slots, mt_max, S, gps_total, y, y_dtype, s);
+    default: return down_t<FMT, 4>(L, h, b, max_slots, mt_max, S, gps_total, y, y_dtype, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemv_down(const moe_layer_desc* L, const float* h, const moe_buckets* b,
-                            int max_slots, void* y, int y_dtype, hipStream_t s) {
-  switch (L->I / 128) {  // groups of 128 along K = I
-    case 1: return down_t<1, 1>(L, h, b, max_slots, y, y_dtype, s);
-    case 2: return down_t<2, 1>(L, h, b, max_slots, y, y_dtype, s);
-    case 3: return down_t<3, 1>(L, h, b, max_slots, y, y_dtype, s);
-    case 4: return down_t<4, 1>(L, h, b, max_slots, y, y_dtype, s);
-    case 6: return down_t<3, 2>(L, h, b, max_slots, y, y_dtype, s);
-    case 8: return down_t<4, 2>(L, h, b, max_slots, y, y_dtype, s);
-    default: return down_t<4, 4>(L, h, b, max_slots, y, y_dtype, s);
-  }
+                            int max_slots, int mt_max, void* y, int y_dtype, hipStream_t s) {
+  if (L->fmt_down == MOE_FMT_Q6K)
+    return down_fmt<MOE_FMT_Q6K>(L, h, b, max_slots, mt_max, y, y_dtype, s);
+  return down_fmt<MOE_FMT_NVFP4>(L, h, b, max_slots, mt_max, y, y_dtype, s);
 }
 
 }  // namespace moe

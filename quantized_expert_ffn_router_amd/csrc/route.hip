@@ -60,9 +60,11 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
     float wv[CH][EB];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int h = h0 + 64 * c;
+      // Unconditional loads from a clamped (in-bounds) index keep every load
+      // of the batch in flight; out-of-range strides are never added below.
+      const int hc = min(h0 + 64 * c, H - 1);
 #pragma unroll
-      for (int q = 0; q < EB; ++q) wv[c][q] = (h < H) ? wrow[q][h] : 0.0f;
+      for (int q = 0; q < EB; ++q) wv[c][q] = wrow[q][hc];
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -172,74 +174,80 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   }
 }
 
-// E <= 64*NV: one wavefront per token; every logit's rank in the order
-// (logit desc, expert asc) is counted against all E logits (broadcast from
-// LDS), so the k winners are found in one pass with no serial rounds.
+// Wave-wide arg-max of (value, index) under the order (value desc, index
+// asc), with DPP moves (a few cycles each, unlike LDS-routed shuffles):
+// lane pairs, quads, rows of 16 (rotate by 4 and 8), then row broadcasts; the
+// winner ends in lane 63 and is broadcast with readlane.
+__device__ __forceinline__ void better(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_step(float& v, int& i) {
+  const float ov = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                         CTRL, ROW_MASK, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false);
+  better(v, i, ov, oi);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  dpp_step<0xb1, 0xf>(v, i);   // quad_perm [1,0,3,2]
+  dpp_step<0x4e, 0xf>(v, i);   // quad_perm [2,3,0,1]
+  dpp_step<0x124, 0xf>(v, i);  // row_ror:4
+  dpp_step<0x128, 0xf>(v, i);  // row_ror:8 -> every lane holds its row's best
+  dpp_step<0x142, 0xa>(v, i);  // row_bcast:15 into rows 1 and 3
+  dpp_step<0x143, 0xc>(v, i);  // row_bcast:31 into rows 2 and 3 -> lane 63 holds the best
+  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// One wavefront per token (E <= 64*NV): k rounds of a DPP wave arg-max.
 template <int NV>
-__global__ __launch_bounds__(256) void k_topk_rank(const float* __restrict__ logits, int T,
-                                                   int E, int k, int renorm,
-                                                   int32_t* __restrict__ idx,
-                                                   float* __restrict__ wout) {
-  __shared__ __align__(16) float lv[4][64 * NV];
-  __shared__ float topv[4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+__global__ __launch_bounds__(256) void k_topk_dpp(const float* __restrict__ logits, int T, int E,
+                                                  int k, int renorm, int32_t* __restrict__ idx,
+                                                  float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* l = logits + (size_t)t * E;
   float v[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = (e < E) ? l[e] : -INFINITY;
-    lv[wave][e] = v[i];
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int rk[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) rk[i] = 0;
-  const float4* row = reinterpret_cast<const float4*>(lv[wave]);
-  for (int e4 = 0; e4 < (E + 3) / 4; ++e4) {
-    const float4 u4 = row[e4];
-    const float u[4] = {u4.x, u4.y, u4.z, u4.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e2 = 4 * e4 + c;
-      if (e2 < E) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const int e = lane + 64 * i;
-          rk[i] += (u[c] > v[i] || (u[c] == v[i] && e2 < e)) ? 1 : 0;
-        }
-      }
-    }
-  }
+  for (int i = 0; i < NV; ++i) v[i] = l[min(lane + 64 * i, E - 1)];  // clamped, unconditional
+  uint32_t taken = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
-    if (lane + 64 * i < E && rk[i] == 0) topv[wave] = v[i];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float top = topv[wave];
-  float ex[NV];
-  float den = 0.0f;
+    if (lane + 64 * i >= E) taken |= 1u << i;
+
+  float my_v = 0.0f, top = 0.0f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const bool valid = lane + 64 * i < E;
-    ex[i] = (valid && rk[i] < k) ? expf(v[i] - top) : 0.0f;
-    if (renorm) den += ex[i];
-    else if (valid) den += expf(v[i] - top);
+    for (int i = 0; i < NV; ++i)
+      if (!(taken & (1u << i))) better(bv, be, v[i], lane + 64 * i);
+    wave_argmax(bv, be);
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (j == 0) top = bv;
+    if (lane == j) { my_v = bv; my_e = be; }
+  }
+
+  float ex = (lane < k) ? expf(my_v - top) : 0.0f;
+  float den;
+  if (renorm) {
+    den = ex;
+  } else {
+    den = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (lane + 64 * i < E) den += expf(v[i] - top);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E && rk[i] < k) {
-      idx[(size_t)t * k + rk[i]] = e;
-      wout[(size_t)t * k + rk[i]] = ex[i] / den;
-    }
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_e;
+    wout[(size_t)t * k + lane] = ex / den;
   }
 }
 
@@ -259,14 +267,9 @@ hipError_t launch_router(const uint16_t* x, int64_t T, int H, const float* Wr,
                          const float* bias, int E, float* logits, hipStream_t s) {
   // The x tile of TB tokens stays within 64 KiB of LDS: TB * H <= 32768.
   const int tb_max = 32768 / H;  // >= 4 for H <= 8192
-  // Decode-sized batches: one expert per wavefront, all tokens at once.
-  if (T <= 1) return launch_router_t<1, 1>(x, T, H, Wr, bias, E, logits, s);
-  if (T <= 2) return launch_router_t<2, 1>(x, T, H, Wr, bias, E, logits, s);
-  if (T <= 4) return launch_router_t<4, 1>(x, T, H, Wr, bias, E, logits, s);
-  if (T <= 8) {
-    if (tb_max >= 8) return launch_router_t<8, 1>(x, T, H, Wr, bias, E, logits, s);
-    return launch_router_t<4, 1>(x, T, H, Wr, bias, E, logits, s);
-  }
+  // Decode-sized batches: one (token, expert) pair per wavefront -- many short
+  // waves finish sooner than a few long ones.
+  if (T <= 64) return launch_router_t<1, 1>(x, T, H, Wr, bias, E, logits, s);
   // Larger batches: TB tokens x EB experts per wavefront, TB * EB = 64.
   if (tb_max >= 16) return launch_router_t<16, 4>(x, T, H, Wr, bias, E, logits, s);
   if (tb_max >= 8) return launch_router_t<8, 8>(x, T, H, Wr, bias, E, logits, s);
@@ -277,11 +280,11 @@ hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renorm,
                        float* w, hipStream_t s) {
   dim3 grid((unsigned)((T + 3) / 4));
   if (E <= 64)
-    hipLaunchKernelGGL(k_topk_rank<1>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
+    hipLaunchKernelGGL(k_topk_dpp<1>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
   else if (E <= 128)
-    hipLaunchKernelGGL(k_topk_rank<2>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
+    hipLaunchKernelGGL(k_topk_dpp<2>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
   else if (E <= 256)
-    hipLaunchKernelGGL(k_topk_rank<4>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
+    hipLaunchKernelGGL(k_topk_dpp<4>, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
   else
     hipLaunchKernelGGL(k_topk, grid, dim3(256), 0, s, logits, (int)T, E, k, renorm, idx, w);
   return hipGetLastError();
