@@ -75,6 +75,18 @@ typedef enum moe_status {
 /* Library version of this header (MOE_ABI_VERSION). */
 int moe_abi_version(void);
 
+/* Expert-FFN kernel family used by moe_expert_ffn (process-wide setting, not
+ * synchronized with calls in flight on other threads):
+ *   MOE_FFN_AUTO -- dequant-fused GEMV for decode-sized batches, MFMA grouped
+ *                   GEMM once experts average >= 16 tokens (default);
+ *   MOE_FFN_GEMV / MOE_FFN_GEMM -- force one family (any size; results agree
+ *                   within the stated tolerance).
+ * Returns MOE_ERR_INVALID_ARG for any other value. */
+#define MOE_FFN_AUTO 0
+#define MOE_FFN_GEMV 1
+#define MOE_FFN_GEMM 2
+moe_status moe_set_ffn_mode(int32_t mode);
+
 /* Message of the last failing call on this thread ("" if none).  Host
  * string owned by the library, valid until the next failing call. */
 const char* moe_last_error(void);

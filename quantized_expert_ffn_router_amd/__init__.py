@@ -28,6 +28,10 @@ MOE_FMT_Q6K = 2
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 
+MOE_FFN_AUTO = 0
+MOE_FFN_GEMV = 1
+MOE_FFN_GEMM = 2
+
 
 class MoeError(RuntimeError):
     def __init__(self, status: int, msg: str):
@@ -66,6 +70,7 @@ _LP = ctypes.POINTER(LayerDesc)
 _BP = ctypes.POINTER(Buckets)
 SIGNATURES = {
     "moe_abi_version": (ctypes.c_int, []),
+    "moe_set_ffn_mode": (ctypes.c_int, [_i32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_expert_blob_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_pack_experts": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
@@ -129,6 +134,10 @@ def _stream(stream) -> int | None:
 
 def moe_abi_version() -> int:
     return lib().moe_abi_version()
+
+
+def moe_set_ffn_mode(mode: int):
+    _check(lib().moe_set_ffn_mode(mode))
 
 
 def moe_expert_blob_bytes(H, I, fmt_gate_up, fmt_down) -> int:

@@ -83,7 +83,18 @@ moe_status check_T(int64_t T, int k, const char* where) {
 
 size_t ffn_ws(const moe_layer_desc* L, int64_t T) {
   size_t A = (size_t)T * L->k;
-  return moe::align_up(A * (size_t)L->I * sizeof(float));
+  // h (fp32 for the GEMV path, bf16 for the grouped GEMM) + the GEMM tile list
+  return moe::align_up(A * (size_t)L->I * sizeof(float)) + moe::gemm_tiles_bytes(L->E, (int64_t)A);
+}
+
+int g_ffn_mode = MOE_FFN_AUTO;
+
+// Grouped GEMM once experts average >= 16 tokens (and the batch is not a
+// decode step); dequant-fused GEMV otherwise.
+bool use_gemm(const moe_layer_desc* L, int64_t T) {
+  if (g_ffn_mode == MOE_FFN_GEMV) return false;
+  if (g_ffn_mode == MOE_FFN_GEMM) return true;
+  return T > 64 && T * L->k >= 16 * (int64_t)L->E;
 }
 
 }  // namespace
@@ -91,6 +102,13 @@ size_t ffn_ws(const moe_layer_desc* L, int64_t T) {
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+moe_status moe_set_ffn_mode(int32_t mode) {
+  if (mode != MOE_FFN_AUTO && mode != MOE_FFN_GEMV && mode != MOE_FFN_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "moe_set_ffn_mode: mode %d", mode);
+  g_ffn_mode = mode;
+  return MOE_OK;
+}
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -222,6 +240,11 @@ moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   CHECK_PTR(x, W); CHECK_PTR(y, W); CHECK_PTR(ws, W); CHECK_PTR(L->experts, W);
   size_t need = ffn_ws(L, T);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
+  if (use_gemm(L, T)) {
+    const size_t hbytes = moe::align_up((size_t)T * L->k * (size_t)L->I * sizeof(float));
+    return hip_status(W, moe::launch_gemm_ffn(L, x, T, b, (uint16_t*)ws, (char*)ws + hbytes, y,
+                                               y_dtype, stream));
+  }
   // Worst-case number of active experts; workgroups past n_active exit.
   const int max_slots = (int)((T * L->k < L->E) ? T * L->k : L->E);
   float* h = (float*)ws;

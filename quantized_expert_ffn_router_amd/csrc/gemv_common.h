@@ -159,6 +159,11 @@ inline int choose_split(int items, int waves_per_item, int NG, int max_s) {
 }
 
 // Launch helpers (one per kernel family), defined in their .hip files.
+size_t gemm_tiles_bytes(int E, int64_t A);
+hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                           const moe_buckets* b, uint16_t* hbuf, void* tiles_ws, void* y,
+                           int y_dtype, hipStream_t s);
+
 // mt_max: tokens gathered per pass (<= kMaxMT; an expert gets at most T).
 hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
                               int max_slots, int mt_max, float* h, hipStream_t s);

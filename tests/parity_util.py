@@ -12,9 +12,10 @@ REL_L2 = 5e-3
 W_ABS = 1e-6
 
 
-def run_gpu(L, x, residual=None, y_dtype=0, T_max=None, repeat=1):
+def run_gpu(L, x, residual=None, y_dtype=0, T_max=None, repeat=1, ffn_mode=0):
     import torch
     import quantized_expert_ffn_router_amd as q
+    q.moe_set_ffn_mode(ffn_mode)
     T = x.shape[0]
     dl = q.DeviceLayer(L)
     buf = q.StepBuffers(dl, T_max or max(T, 1), y_dtype)
@@ -23,6 +24,7 @@ def run_gpu(L, x, residual=None, y_dtype=0, T_max=None, repeat=1):
     for _ in range(repeat):
         q.layer_forward(dl, buf, xd, T, rd)
     torch.cuda.synchronize()
+    q.moe_set_ffn_mode(q.MOE_FFN_AUTO)
     A = T * L.k
     res = dict(
         logits=buf.logits[:T].cpu().numpy(),
@@ -70,9 +72,9 @@ def check_out(g_out, o_out):
     return float(err.max()), r
 
 
-def check_layer(L, x, residual=None, y_dtype=0, tokens=None, y_rel=1e-4):
+def check_layer(L, x, residual=None, y_dtype=0, tokens=None, y_rel=1e-4, ffn_mode=0):
     """Full-layer parity; FFN compared on `tokens` (all when None)."""
-    g = run_gpu(L, x, residual, y_dtype)
+    g = run_gpu(L, x, residual, y_dtype, ffn_mode=ffn_mode)
     logits, idx, w = check_route(g, L, x)
     ob = check_buckets(g["buckets"], idx, L.E)
     o_out, o_y = oracle.ffn_combine(L, x, idx, w, residual, tokens, want_y=True)

@@ -49,10 +49,11 @@ def test_ragged_mid_layer_parity():
 
 
 def test_many_tokens_per_expert_and_multiblock_bucket():
-    # 600 x 8 = 4800 assignments: multi-block bucketing, >8 tokens per expert
+    # 600 x 8 = 4800 assignments: multi-block bucketing; ~75 tokens per expert
+    # selects the grouped GEMM (bf16 h), hence the layer-level y tolerance.
     w, L = layer("many", E=64, k=8, H=256, I=128, T=600)
     x = moegen.make_tokens(w, w.T)
-    check_layer(L, x, tokens=list(range(0, 600, 7)))
+    check_layer(L, x, tokens=list(range(0, 600, 7)), y_rel=5e-3)
 
 
 def test_mixed_q6k_decode_parity():
@@ -74,13 +75,19 @@ def test_no_renormalisation_and_k_equals_E():
     check_layer(L, x)
 
 
+# The grouped GEMM rounds h (and Q6_K weights) to bf16 before the MFMAs, so
+# its fp32 expert outputs are compared at the layer tolerance (rel L2 5e-3).
+GEMM_Y_REL = 5e-3
+
+
 def test_prefill_routing_full_size_and_sampled_outputs():
-    """16384 tokens with the Zipf-biased router: logits, indices and bucket
-    arrays for every token; layer outputs on a sample of tokens."""
+    """16384 tokens with the Zipf-biased router (grouped GEMM path): logits,
+    indices and bucket arrays for every token; outputs on a sample of tokens
+    (bf16 expert outputs, as the prefill path stores them)."""
     w, L = layer("prefill")
     x = moegen.make_tokens(w, w.T)
     sample = list(range(0, w.T, 512)) + [w.T - 1]
-    g, _ = check_layer(L, x, tokens=sample)
+    g, _ = check_layer(L, x, tokens=sample, y_dtype=1, y_rel=GEMM_Y_REL)
     counts = g["buckets"]["counts"]
     assert counts.sum() == w.T * w.k and counts.min() > 0
     assert counts.max() > 4 * counts.min()   # biased load
@@ -113,3 +120,30 @@ def test_many_experts_iterative_topk_and_single_block_bucket():
     w, L = layer("wide", E=512, k=4, H=256, I=128, T=100)
     x = moegen.make_tokens(w, w.T)
     check_layer(L, x)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_both_ffn_families_on_the_same_ragged_batch(mode):
+    # 600 tokens x top-8 over 64 experts: ragged M tails in every expert;
+    # mode 1 forces the GEMV kernels, mode 2 the MFMA grouped GEMM.
+    w, L = layer("many", E=64, k=8, H=256, I=128, T=600)
+    x = moegen.make_tokens(w, w.T, step=5)
+    check_layer(L, x, tokens=list(range(0, 600, 5)), ffn_mode=mode,
+                y_rel=1e-4 if mode == 1 else GEMM_Y_REL)
+
+
+def test_gemm_multiple_column_tiles_and_k_steps():
+    # H = 512 (4 down column tiles of 128, 8 K steps of 64), I = 384 (6 gate/up
+    # column tiles, 6 K steps); experts with 1..~90 rows.
+    w, L = layer("gemm_mid", E=16, k=4, H=512, I=384, T=300)
+    x = moegen.make_tokens(w, w.T)
+    check_layer(L, x, residual=moegen.make_residual(w, w.T), tokens=list(range(0, 300, 3)),
+                ffn_mode=2, y_rel=GEMM_Y_REL)
+
+
+def test_mixed_prefill_q6k_down_sampled():
+    """4096-token prefill of the 256-expert layer with the Q6_K-style down
+    projection on the grouped GEMM path."""
+    w, L = layer("mixed")
+    x = moegen.make_tokens(w, 4096, step=1)
+    check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
