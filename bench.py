@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--batches", type=str, default="1,2,4,8")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--cpu-sample-steps", type=int, default=4)
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many eager steps per batch (for profilers)")
@@ -158,6 +160,8 @@ def main():
         print(json.dumps({"profile_run": True, "batches": batches}))
         return
 
+    prefill = None if args.no_prefill else measure_prefill(args, q, moegen, torch, dev)
+
     head = results[Bmax]
     cpu = None
     if not args.no_cpu_baseline:
@@ -195,10 +199,62 @@ def main():
             {k: (round(v, 4) if isinstance(v, float) else v) for k, v in results[b].items()}
             for b in batches
         ],
+        "prefill": prefill,
         "cpu_baseline": cpu,
         "setup_s": round(gen_s, 1),
     }
     print(json.dumps(line))
+
+
+def measure_prefill(args, q, moegen, torch, dev):
+    """16384-token prefill of the same layer shape with the Zipf(1.1)-biased
+    router: whole-layer time and the grouped-GEMM FFN's TFLOP/s
+    (6 * T * k * H * I useful flops, HIP events on the launch stream)."""
+    W = moegen.WORKLOADS["prefill"]
+    L = moegen.make_layer(W, layer=100)
+    dl = q.DeviceLayer(L)
+    T = W.T
+    buf = q.StepBuffers(dl, T, q.MOE_DTYPE_BF16)
+    xs = [torch.from_numpy(moegen.make_tokens(W, T, step=s).view(np.int16).copy()).to(dev)
+          for s in range(2)]
+    stream = torch.cuda.Stream()
+    d = dl.desc
+    n = args.prefill_steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for i in range(2):
+            q.layer_forward(dl, buf, xs[i % 2], T, stream=stream)
+        torch.cuda.synchronize()
+        for i in range(n):
+            x = xs[i % 2]
+            ev[i][0].record(stream)
+            q.moe_route(d, x, T, buf.logits, buf.idx, buf.w, stream)
+            q.moe_bucket(d, buf.idx, T, buf.buckets, buf.ws, buf.ws_bytes, stream)
+            ev[i][1].record(stream)
+            q.moe_expert_ffn(d, x, T, buf.buckets, buf.y, buf.y_dtype, buf.ws, buf.ws_bytes, stream)
+            ev[i][2].record(stream)
+            q.moe_combine(d, buf.y, buf.y_dtype, buf.buckets, buf.w, T, None, buf.out, stream)
+            q.moe_expert_hist(d, buf.buckets, buf.hist, 5, 10, stream)
+            ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ffn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    layer_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    flops = 6.0 * T * W.k * W.H * W.I
+    tflops = flops / (ffn_ms * 1e-3) / 1e12
+    counts = buf.bucket_view(W.E, T, W.k)["counts"]
+    return {
+        "workload": "prefill: 16384 tokens, 128 experts, top-8, hidden 2048, intermediate 768, "
+                    "NVFP4, Zipf(1.1)-biased router, bf16 expert outputs",
+        "steps": n, "layer_ms": round(layer_ms, 4), "tok_per_s": round(T / (layer_ms * 1e-3), 1),
+        "route_bucket_ms": round(route_ms, 4), "ffn_ms": round(ffn_ms, 4),
+        "ffn_tflops": round(tflops, 2),
+        "roofline": {"kernel": "grouped GEMM (k_gemm_gateup_nvfp4 + k_gemm_down)", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
+                        "mean": float(counts.mean())},
+    }
 
 
 def cpu_baseline(W, L, B, n_steps):

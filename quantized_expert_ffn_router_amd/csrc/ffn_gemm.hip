@@ -23,6 +23,8 @@
 //     the weights, so each lane holds matching g and u values and the SwiGLU
 //     epilogue h = silu(g*ts_g) * (u*ts_u) runs in registers; h is stored as
 //     bf16.  Down: y = acc * ts_d in bf16 or fp32.
+#include <type_traits>
+
 #include "gemv_common.h"
 
 namespace moe {
@@ -33,9 +35,6 @@ typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128;       // token rows per tile
-constexpr int BN = 128;       // output columns per tile (gate/up: 64 + 64)
-constexpr int BK = 64;        // K per step
-constexpr int LDA = BK + 8;   // padded LDS row (bf16 elements)
 constexpr int kThreads = 256;
 
 // Tile list: entry i = (expert, first row of the block); built from counts.
@@ -59,45 +58,6 @@ __global__ __launch_bounds__(1024) void k_build_tiles(const uint32_t* __restrict
   if (e == 1023) *n_tiles = pre[1023];
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, to_v2bf(a, b));
-}
-
-// 32 NVFP4 elements (one 16-byte code granule) with their two E4M3 scales ->
-// 16 packed bf16 pairs (exact).
-__device__ __forceinline__ void dequant32_nvfp4(const uint4& c, uint32_t s2, uint32_t* o) {
-  const v2f_t sp = e4m3x2<false>(s2);
-  const float s0 = sp.x, s1 = sp.y;
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float f[8];
-    e2m1x8_f32(w[q], f);
-    const float s = (q < 2) ? s0 : s1;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) o[4 * q + p] = pack_bf16x2(f[2 * p] * s, f[2 * p + 1] * s);
-  }
-}
-
-// 32 Q6_K elements: low nibbles (16 bytes), high bits (8 bytes), the two
-// int8 sub-scales and d -> 16 packed bf16 pairs (d*sc*(q-32) rounded to bf16).
-__device__ __forceinline__ void dequant32_q6k(const uint4& ql, const uint2& qh, uint32_t sc2,
-                                              float d, uint32_t* o) {
-  const float s0 = d * (float)(int8_t)(sc2 & 0xffu);
-  const float s1 = d * (float)(int8_t)((sc2 >> 8) & 0xffu);
-  const uint32_t lw[4] = {ql.x, ql.y, ql.z, ql.w};
-  const uint32_t hw[2] = {qh.x, qh.y};
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {  // elements 2p, 2p+1
-    const uint32_t byte = (lw[p >> 2] >> (8 * (p & 3))) & 0xffu;
-    const uint32_t hb = (hw[p >> 3] >> (4 * (p & 7))) & 0xfu;
-    const int q0 = (int)((byte & 15u) | ((hb & 3u) << 4));
-    const int q1 = (int)((byte >> 4) | ((hb >> 2) << 4));
-    const float s = (p < 8) ? s0 : s1;
-    o[p] = pack_bf16x2((float)(q0 - 32) * s, (float)(q1 - 32) * s);
-  }
-}
-
 // Logical tile of this workgroup with an XCD-major layout of the grid.
 __device__ __forceinline__ int logical_tile(int total) {
   const int w = blockIdx.x;
@@ -105,40 +65,183 @@ __device__ __forceinline__ int logical_tile(int total) {
   return (w & 7) * per + (w >> 3);
 }
 
-// MFMA over one K step of LDS tiles for this wave's 64 x 64 sub-tile:
-// A rows [a0, a0+64), B rows b_rows[0..3] (16 each).
-__device__ __forceinline__ void mma_step(const uint16_t* As, const uint16_t* Bs, int a0,
-                                         const int* b0, v4f_t (*acc)[4]) {
+// ---------------------------------------------------------------- B fragments
+// Lane l of a wave feeds column n0 + l%16 of a 16-column MFMA tile with the
+// 8 K-elements k0 + 8*(l/16) .. +8 of a 32-element K step.  In the packed
+// blob those 8 codes are one dword of the row's 16-byte granule, so a
+// wave-wide load of 16 granules (256 contiguous bytes) covers the fragment.
+
+struct FragNvfp4 {
+  uint32_t code;   // 8 E2M1 codes
+  uint32_t scale;  // E4M3 scale byte of this lane's 16-block (low byte)
+};
+
+__device__ __forceinline__ void load_frag(FragNvfp4& f, const uint8_t* q, const uint8_t* sc, int N,
+                                          int n, int k32) {
   const int lane = threadIdx.x & 63;
-  const int r = lane & 15, kq = (lane >> 4) * 8;
+  f.code = *(const __attribute__((address_space(1))) uint32_t*)(uintptr_t)(
+      q + ((size_t)(k32 >> 5) * N + n) * 16 + 4 * (lane >> 4));
+  const int blk = ((k32 & 127) >> 4) + (lane >> 5);  // 16-block within the 128-group
+  f.scale = *(const __attribute__((address_space(1))) uint8_t*)(uintptr_t)(
+      sc + ((size_t)(k32 >> 7) * N + n) * 8 + blk);
+}
+
+__device__ __forceinline__ v8bf_t dequant_frag(const FragNvfp4& f) {
+  const float s = e4m3x2<false>(f.scale).x;
+  float w[8];
+  e2m1x8_f32(f.code, w);
+  v8bf_t r;
 #pragma unroll
-  for (int kk = 0; kk < BK; kk += 32) {
-    v8bf_t af[4], bf[4];
+  for (int p = 0; p < 4; ++p) {
+    const v2bf_t b = to_v2bf(w[2 * p] * s, w[2 * p + 1] * s);
+    r[2 * p] = b[0];
+    r[2 * p + 1] = b[1];
+  }
+  return r;
+}
+
+struct FragQ6k {
+  uint32_t lo;    // 8 low nibbles
+  uint32_t hi;    // 8 x 2 high bits (low 16 bits)
+  uint32_t sc;    // int8 sub-scale (low byte)
+  uint32_t d;     // fp16 superblock scale
+};
+
+__device__ __forceinline__ void load_frag_q6k(FragQ6k& f, const uint8_t* ql, const uint8_t* qh,
+                                              const uint8_t* sc, const uint8_t* dd, int N, int n,
+                                              int k32) {
+  typedef __attribute__((address_space(1))) uint32_t g32;
+  typedef __attribute__((address_space(1))) uint16_t g16;
+  typedef __attribute__((address_space(1))) uint8_t g8;
+  const int lane = threadIdx.x & 63;
+  const int c = k32 >> 5, sb = k32 >> 8;
+  f.lo = *(const g32*)(uintptr_t)(ql + ((size_t)c * N + n) * 16 + 4 * (lane >> 4));
+  f.hi = *(const g16*)(uintptr_t)(qh + ((size_t)(c >> 1) * N + n) * 16 + 8 * (c & 1) + 2 * (lane >> 4));
+  f.sc = *(const g8*)(uintptr_t)(sc + ((size_t)sb * N + n) * 16 + 2 * (c & 7) + (lane >> 5));
+  f.d = *(const g16*)(uintptr_t)(dd + ((size_t)sb * N + n) * 2);
+}
+
+__device__ __forceinline__ v8bf_t dequant_frag_q6k(const FragQ6k& f) {
+  const float s = f16_to_f32((uint16_t)f.d) * (float)(int8_t)(f.sc & 0xffu);
+  v8bf_t r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const v8bf_t*>(As + (a0 + 16 * i + r) * LDA + kk + kq);
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t byte = (f.lo >> (8 * p)) & 0xffu;
+    const uint32_t hb = (f.hi >> (4 * p)) & 0xfu;
+    const int q0 = (int)((byte & 15u) | ((hb & 3u) << 4));
+    const int q1 = (int)((byte >> 4) | ((hb >> 2) << 4));
+    const v2bf_t b = to_v2bf((float)(q0 - 32) * s, (float)(q1 - 32) * s);
+    r[2 * p] = b[0];
+    r[2 * p + 1] = b[1];
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- main loop
+// WG = 4 waves; tile = 128 rows x 4*NC*16 columns; wave w owns all 128 rows
+// and column tiles cols(w, j), j < NC.  A (bf16 rows) is double-buffered in
+// LDS with one barrier per K step of 64; B fragments go global -> registers,
+// prefetched one K step ahead and dequantized right before their MFMAs.
+constexpr int GBM = 128, GBK = 64, GLDA = GBK + 8;
+
+// GU: column tiles j < NC/2 read planes (p0, p1) and the rest (p2, p3) --
+// the gate and up matrices of one expert; otherwise (p0..p3) are the planes of
+// one matrix (NVFP4 codes, scales; Q6_K ql, qh, sc, d).
+struct ARows {
+  const uint16_t* r[4];  // this thread's 4 A rows (passed by value: no scratch)
+};
+
+template <int FMT, int NC, bool GU, typename ColFn>
+__device__ __forceinline__ void gemm_main(ARows arow, int K, int N,
+                                          const uint8_t* p0, const uint8_t* p1, const uint8_t* p2,
+                                          const uint8_t* p3, ColFn col_of, uint16_t* As,
+                                          v4f_t (*acc)[NC]) {
+  typedef typename std::conditional<FMT == MOE_FMT_NVFP4, FragNvfp4, FragQ6k>::type Frag;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ar = tid >> 3, ac = tid & 7;  // A loader: rows ar + 32*j, 16-byte chunk ac
+  uint4 a0, a1, a2, a3;  // named (not an array) so they stay in registers
+  Frag bnext[2][NC];
+
+  auto load_a = [&](int k0) {
+    a0 = *reinterpret_cast<const uint4*>(arow.r[0] + k0 + 8 * ac);
+    a1 = *reinterpret_cast<const uint4*>(arow.r[1] + k0 + 8 * ac);
+    a2 = *reinterpret_cast<const uint4*>(arow.r[2] + k0 + 8 * ac);
+    a3 = *reinterpret_cast<const uint4*>(arow.r[3] + k0 + 8 * ac);
+  };
+  auto store_a = [&](int buf) {
+    uint16_t* d = As + buf * GBM * GLDA + ar * GLDA + 8 * ac;
+    *reinterpret_cast<uint4*>(d) = a0;
+    *reinterpret_cast<uint4*>(d + 32 * GLDA) = a1;
+    *reinterpret_cast<uint4*>(d + 64 * GLDA) = a2;
+    *reinterpret_cast<uint4*>(d + 96 * GLDA) = a3;
+  };
+  auto load_b = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const v8bf_t*>(Bs + (b0[j] + r) * LDA + kk + kq);
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < NC; ++j) {
+        const int n = col_of(j) + (lane & 15);
+        if constexpr (GU) {
+          if (j < NC / 2) load_frag(bnext[s][j], p0, p1, N, n, k0 + 32 * s);
+          else load_frag(bnext[s][j], p2, p3, N, n, k0 + 32 * s);
+        } else if constexpr (FMT == MOE_FMT_NVFP4) {
+          load_frag(bnext[s][j], p0, p1, N, n, k0 + 32 * s);
+        } else {
+          load_frag_q6k(bnext[s][j], p0, p1, p2, p3, N, n, k0 + 32 * s);
+        }
+      }
+  };
+
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  __syncthreads();
+  const int nsteps = K / GBK;
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    // Dequantize this step's B fragments, then prefetch the next step.
+    v8bf_t bf[2][NC];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        if constexpr (FMT == MOE_FMT_NVFP4) bf[s][j] = dequant_frag(bnext[s][j]);
+        else bf[s][j] = dequant_frag_q6k(bnext[s][j]);
+      }
+    if (st + 1 < nsteps) {
+      load_a((st + 1) * GBK);
+      load_b((st + 1) * GBK);
+    }
+    const uint16_t* Ab = As + buf * GBM * GLDA;
+    const int r = lane & 15, kq = (lane >> 4) * 8;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const v8bf_t af = *reinterpret_cast<const v8bf_t*>(Ab + (16 * i + r) * GLDA + 32 * s + kq);
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[s][j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (st + 1 < nsteps) store_a(buf ^ 1);
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ gate/up
+// Tile columns: 128 consecutive rows n0.. of gate and the same rows of up;
+// wave w takes gate columns n0 + 32w .. +32 (tiles j = 0, 1) and the matching
+// up columns (tiles j = 2, 3).
 
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_gateup_nvfp4(
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_gateup_nvfp4(
     const uint16_t* __restrict__ x, int H, int I, int ktop,
     const moe_expert_ref* __restrict__ experts, size_t off_gq, size_t off_gs, size_t off_uq,
     size_t off_us, const int32_t* __restrict__ offsets, const uint32_t* __restrict__ counts,
     const int32_t* __restrict__ sorted_asg, const int2* __restrict__ tiles,
     const int* __restrict__ n_tiles, int grid_tiles, uint16_t* __restrict__ hout) {
-  __shared__ __align__(16) uint16_t As[BM * LDA];
-  __shared__ __align__(16) uint16_t Bs[BN * LDA];
-  const int NT = I / 64;  // column tiles (64 gate + 64 up columns each)
+  __shared__ __align__(16) uint16_t As[2 * GBM * GLDA];
+  const int NT = I / 128;
   const int L = logical_tile(grid_tiles);
   const int mtile = L / NT, ntile = L - mtile * NT;
   if (mtile >= *n_tiles) return;
@@ -148,78 +251,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_gateup_nvfp4(
   const int base = offsets[e];
   const moe_expert_ref ref = experts[e];
   const uint8_t* blob = (const uint8_t*)ref.blob;
-  const int n0 = ntile * 64;
+  const int n0 = ntile * 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-  // A loader: thread -> rows ar + 32*j (j < 4), 16-byte chunk ac of the K step.
-  const int ar = tid >> 3, ac = tid & 7;
-  const uint16_t* arow[4];
+  ARows arow;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = m0 + ar + 32 * j;
-    const int tok = sorted_asg[base + (row < m_e ? row : 0)] / ktop;
-    arow[j] = x + (size_t)tok * H;
+    const int row = m0 + (tid >> 3) + 32 * j;  // rows past m_e read a valid row, never stored
+    arow.r[j] = x + (size_t)(sorted_asg[base + (row < m_e ? row : 0)] / ktop) * H;
   }
-  // B loader: thread -> B row br (0..63 gate, 64..127 up), 32-element half bh.
-  const int br = tid >> 1, bh = tid & 1;
-  const int wrow = n0 + (br & 63);
-  const uint8_t* bq = blob + (br < 64 ? off_gq : off_uq);
-  const uint8_t* bs = blob + (br < 64 ? off_gs : off_us);
-
-  uint4 a_reg[4], b_reg;
-  uint32_t s_reg;
-  auto gload = [&](int k0) {
+  v4f_t acc[8][4];  // column tiles 0, 1: gate; 2, 3: the same columns of up
 #pragma unroll
-    for (int j = 0; j < 4; ++j)  // rows past m_e read a valid row; their outputs are never stored
-      a_reg[j] = *reinterpret_cast<const uint4*>(arow[j] + k0 + 8 * ac);
-    const int c = k0 / 32 + bh;  // 32-element code granule
-    b_reg = ld16(bq + ((size_t)c * I + wrow) * 16);
-    const uint2 sg = ld8(bs + ((size_t)(k0 / 128) * I + wrow) * 8);
-    const int sb = ((k0 & 127) / 16) + 2 * bh;  // first of the two 16-blocks
-    const uint32_t sw = (sb < 4) ? sg.x : sg.y;
-    s_reg = (sw >> (8 * (sb & 3))) & 0xffffu;
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(As + (ar + 32 * j) * LDA + 8 * ac) = a_reg[j];
-    uint32_t o[16];
-    dequant32_nvfp4(b_reg, s_reg, o);
-    uint4* dst = reinterpret_cast<uint4*>(Bs + br * LDA + 32 * bh);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-    dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
-  };
-
-  v4f_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int wm = wave >> 1, wn = wave & 1;
-  const int a0 = wm * 64;
-  const int b0[4] = {wn * 32, wn * 32 + 16, 64 + wn * 32, 64 + wn * 32 + 16};  // g, g, u, u
+  const int cb = n0 + 32 * wave;
+  gemm_main<MOE_FMT_NVFP4, 4, true>(arow, H, I, blob + off_gq, blob + off_gs, blob + off_uq,
+                                    blob + off_us, [&](int j) { return cb + 16 * (j & 1); }, As,
+                                    acc);
 
-  gload(0);
-  for (int k0 = 0; k0 < H; k0 += BK) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (k0 + BK < H) gload(k0 + BK);
-    mma_step(As, Bs, a0, b0, acc);
-  }
-
-  // SwiGLU epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each tile.
   const float tg = ref.ts_gate, tu = ref.ts_up;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 32 + 16 * j + (lane & 15);
+      const int col = cb + 16 * j + (lane & 15);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = m0 + a0 + 16 * i + 4 * (lane >> 4) + q;
+        const int row = m0 + 16 * i + 4 * (lane >> 4) + q;
         if (row < m_e) {
           const float g = acc[i][j][q] * tg, u = acc[i][j + 2][q] * tu;
           hout[(size_t)(base + row) * I + col] = f32_to_bf16_rne(g / (1.0f + expf(-g)) * u);
@@ -230,16 +289,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_gateup_nvfp4(
 }
 
 // ------------------------------------------------------------------ down
+// Tile columns: 256 consecutive rows of the down weights (output features);
+// wave w takes columns n0 + 64w .. +64 (4 tiles).
 
 template <int FMT, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_down(
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_down(
     const uint16_t* __restrict__ h, int H, int I, const moe_expert_ref* __restrict__ experts,
     size_t off_a, size_t off_b, size_t off_c, size_t off_d, const int32_t* __restrict__ offsets,
     const uint32_t* __restrict__ counts, const int2* __restrict__ tiles,
     const int* __restrict__ n_tiles, int grid_tiles, void* __restrict__ y) {
-  __shared__ __align__(16) uint16_t As[BM * LDA];
-  __shared__ __align__(16) uint16_t Bs[BN * LDA];
-  const int NT = H / BN;
+  __shared__ __align__(16) uint16_t As[2 * GBM * GLDA];
+  const int NT = H / 256;
   const int L = logical_tile(grid_tiles);
   const int mtile = L / NT, ntile = L - mtile * NT;
   if (mtile >= *n_tiles) return;
@@ -249,83 +309,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_down(
   const int base = offsets[e];
   const moe_expert_ref ref = experts[e];
   const uint8_t* blob = (const uint8_t*)ref.blob;
-  const int n0 = ntile * BN;
+  const int n0 = ntile * 256;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-  const int ar = tid >> 3, ac = tid & 7;
-  const uint16_t* arow[4];
+  ARows arow;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = m0 + ar + 32 * j;
-    arow[j] = h + (size_t)(base + (row < m_e ? row : 0)) * I;
+    const int row = m0 + (tid >> 3) + 32 * j;
+    arow.r[j] = h + (size_t)(base + (row < m_e ? row : 0)) * I;
   }
-  const int br = tid >> 1, bh = tid & 1;
-  const int wrow = n0 + br;
-
-  uint4 a_reg[4], b_reg;
-  uint2 qh_reg;
-  uint32_t s_reg, d_reg;
-  auto gload = [&](int k0) {
+  v4f_t acc[8][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)  // rows past m_e read a valid row; their outputs are never stored
-      a_reg[j] = *reinterpret_cast<const uint4*>(arow[j] + k0 + 8 * ac);
-    const int c = k0 / 32 + bh;
-    b_reg = ld16(blob + off_a + ((size_t)c * H + wrow) * 16);
-    if (FMT == MOE_FMT_NVFP4) {
-      const uint2 sg = ld8(blob + off_b + ((size_t)(k0 / 128) * H + wrow) * 8);
-      const int sb = ((k0 & 127) / 16) + 2 * bh;
-      const uint32_t sw = (sb < 4) ? sg.x : sg.y;
-      s_reg = (sw >> (8 * (sb & 3))) & 0xffffu;
-    } else {
-      // high bits: granule c/2 holds 64 elements; this 32-element chunk is its half c&1
-      qh_reg = ld8(blob + off_b + ((size_t)(c >> 1) * H + wrow) * 16 + 8 * (c & 1));
-      const int sb = c >> 3;                  // superblock
-      const int j0 = (c & 7) * 2;             // first 16-element sub-block of the chunk
-      s_reg = (uint32_t)ld2(blob + off_c + ((size_t)sb * H + wrow) * 16 + j0);
-      d_reg = ld2(blob + off_d + ((size_t)sb * H + wrow) * 2);
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(As + (ar + 32 * j) * LDA + 8 * ac) = a_reg[j];
-    uint32_t o[16];
-    if (FMT == MOE_FMT_NVFP4) dequant32_nvfp4(b_reg, s_reg, o);
-    else dequant32_q6k(b_reg, qh_reg, s_reg, f16_to_f32((uint16_t)d_reg), o);
-    uint4* dst = reinterpret_cast<uint4*>(Bs + br * LDA + 32 * bh);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-    dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
-  };
-
-  v4f_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int wm = wave >> 1, wn = wave & 1;
-  const int a0 = wm * 64;
-  const int b0[4] = {wn * 64, wn * 64 + 16, wn * 64 + 32, wn * 64 + 48};
-
-  gload(0);
-  for (int k0 = 0; k0 < I; k0 += BK) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (k0 + BK < I) gload(k0 + BK);
-    mma_step(As, Bs, a0, b0, acc);
-  }
+  const int cb = n0 + 64 * wave;
+  gemm_main<FMT, 4, false>(arow, I, H, blob + off_a, blob + off_b, blob + off_c, blob + off_d,
+                    [&](int j) { return cb + 16 * j; }, As, acc);
 
   const float ts = (FMT == MOE_FMT_NVFP4) ? ref.ts_down : 1.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 64 + 16 * j + (lane & 15);
+      const int col = cb + 16 * j + (lane & 15);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = m0 + a0 + 16 * i + 4 * (lane >> 4) + q;
+        const int row = m0 + 16 * i + 4 * (lane >> 4) + q;
         if (row < m_e) {
           const float v = acc[i][j][q] * ts;
           if (OUT_BF16) reinterpret_cast<uint16_t*>(y)[(size_t)(base + row) * H + col] = f32_to_bf16_rne(v);
@@ -355,7 +365,7 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
   if (err != hipSuccess) return err;
   const int max_mtiles = (int)(A / BM) + L->E;
   {
-    const int NT = L->I / 64;
+    const int NT = L->I / 128;
     int total = max_mtiles * NT;
     total = (total + 7) / 8 * 8;
     hipLaunchKernelGGL(k_gemm_gateup_nvfp4, dim3((unsigned)total), dim3(kThreads), 0, s, x, L->H,
@@ -365,7 +375,7 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
     if (err != hipSuccess) return err;
   }
   {
-    const int NT = L->H / BN;
+    const int NT = L->H / 256;
     int total = max_mtiles * NT;
     total = (total + 7) / 8 * 8;
     const bool bf = (y_dtype == MOE_DTYPE_BF16);

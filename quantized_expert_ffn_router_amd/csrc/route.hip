@@ -22,6 +22,30 @@ namespace {
 
 constexpr int kRouterWaves = 4;
 
+// One level of the transposed butterfly with partner lane ^ W while NV values
+// per lane remain: the lane with bit W clear keeps values [0, NV/2), the other
+// keeps [NV/2, NV); each adds the partner's copy.  Once one value is left the
+// remaining levels are plain pairwise sums.  All indices are compile time.
+template <int NV, int W>
+__device__ __forceinline__ void tb_level(double* acc, int lane) {
+  if constexpr (W >= 1) {
+    if constexpr (NV > 1) {
+      constexpr int HALF = NV / 2;
+      const bool upper = (lane & W) != 0;
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) {
+        const double send = upper ? acc[i] : acc[i + HALF];
+        const double keep = upper ? acc[i + HALF] : acc[i];
+        acc[i] = keep + __shfl_xor(send, W);
+      }
+      tb_level<HALF, W / 2>(acc, lane);
+    } else {
+      acc[0] = acc[0] + __shfl_xor(acc[0], W);
+      tb_level<1, W / 2>(acc, lane);
+    }
+  }
+}
+
 template <int TB, int EB>
 __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
     const uint16_t* __restrict__ x, int T, int H, const float* __restrict__ Wr,
@@ -82,26 +106,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
   }
 
   // Transposed butterfly (see file comment).
-  int nv = V;
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    if (nv > 1) {
-      const bool upper = (lane & w) != 0;
-      const int half = nv >> 1;
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) {
-        if (i < half) {
-          double send = upper ? acc[i] : acc[i + half];
-          double keep = upper ? acc[i + half] : acc[i];
-          double other = __shfl_xor(send, w);
-          acc[i] = keep + other;
-        }
-      }
-      nv = half;
-    } else {
-      acc[0] = acc[0] + __shfl_xor(acc[0], w);
-    }
-  }
+  tb_level<V, 32>(acc, lane);
   constexpr int kShift = (V == 1) ? 6 : (V == 2) ? 5 : (V == 4) ? 4 : (V == 8) ? 3 : (V == 16) ? 2 : (V == 32) ? 1 : 0;
   if ((lane & ((1 << kShift) - 1)) == 0) {
     const int v = lane >> kShift;
