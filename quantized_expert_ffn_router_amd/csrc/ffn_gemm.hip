@@ -234,7 +234,7 @@ __device__ __forceinline__ void gemm_main(ARows arow, int K, int N,
 // wave w takes gate columns n0 + 32w .. +32 (tiles j = 0, 1) and the matching
 // up columns (tiles j = 2, 3).
 
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_gateup_nvfp4(
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_gateup_nvfp4(
     const uint16_t* __restrict__ x, int H, int I, int ktop,
     const moe_expert_ref* __restrict__ experts, size_t off_gq, size_t off_gs, size_t off_uq,
     size_t off_us, const int32_t* __restrict__ offsets, const uint32_t* __restrict__ counts,
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_gateup_nvfp4(
 // wave w takes columns n0 + 64w .. +64 (4 tiles).
 
 template <int FMT, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_down(
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_down(
     const uint16_t* __restrict__ h, int H, int I, const moe_expert_ref* __restrict__ experts,
     size_t off_a, size_t off_b, size_t off_c, size_t off_d, const int32_t* __restrict__ offsets,
     const uint32_t* __restrict__ counts, const int2* __restrict__ tiles,
