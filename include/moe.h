@@ -241,6 +241,83 @@ moe_status moe_combine(const moe_layer_desc* L, const void* y, int32_t y_dtype,
 moe_status moe_expert_hist(const moe_layer_desc* L, const moe_buckets* b, uint32_t* hist,
                            int32_t decay_shift, int32_t unit_shift, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* Optional cold-expert tier: pinned host RAM -> HBM slots                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * Experts outside the GPU memory budget live in system RAM and are streamed in
+ * when routed to ("experts outside its memory budget can live in system RAM
+ * and be streamed as needed": aiopssre.com, "Experts can move without becoming
+ * free"); the most-routed experts stay resident ("Tier 1 ... the most routed
+ * experts", "Tier 3 System RAM": basalt.jgulfo.com, "Expert tiers"); the
+ * resident set follows the usage histogram ("an adaptive tier moves them":
+ * basalt.jgulfo.com, FAQ).  One GPU only: no peer-GPU tier.
+ *
+ * Per layer l: R resident slots (experts chosen by moe_tier_rebalance) in the
+ * caller's HBM pool, plus S staging slots shared by all layers.  Before the
+ * experts of layer l run, moe_tier_prepare copies the step's active list to
+ * the host (the one host synchronization per layer), copies every active
+ * expert that is not resident from pinned host memory into a staging slot on
+ * the copy stream, writes the layer's device expert table (moe_expert_ref [E])
+ * and makes the compute stream wait for those copies.  moe_expert_ffn then
+ * reads every expert through that table, so a tiered step computes exactly
+ * (bit for bit) what the same step computes with every expert resident.
+ * Entries of inactive, non-resident experts are set to blob = NULL.
+ *
+ * Ownership: host blobs (pinned, e.g. hipHostMalloc), the HBM pool, the
+ * device tables and both streams belong to the caller and must outlive the
+ * tier.  The tier owns only host metadata, a few pinned bytes for the active
+ * list and table staging, and two events.  A tier is not thread-safe.
+ */
+typedef struct moe_tier_desc {
+  int32_t L;                      /* layers */
+  int32_t E;                      /* experts per layer */
+  int32_t resident_per_layer;     /* R (0 <= R <= E) */
+  int32_t staging_slots;          /* S: most misses one layer step may have (<= E) */
+  size_t expert_bytes;            /* moe_expert_blob_bytes(...) of every expert */
+  const void* const* host_blobs;  /* host array [L*E]: pinned host address of blob (l, e) */
+  const moe_expert_ref* scales;   /* host array [L*E]: ts_gate/ts_up/ts_down of (l, e); blob ignored */
+  void* hbm_pool;                 /* device, 256-aligned, >= (L*R + S) * expert_bytes */
+  size_t hbm_pool_bytes;
+  hipStream_t copy_stream;        /* side stream for the H2D copies */
+} moe_tier_desc;
+
+typedef struct moe_tier_stats {
+  uint64_t hits;          /* active experts found resident */
+  uint64_t misses;        /* active experts copied from host */
+  uint64_t h2d_bytes;     /* bytes copied host -> HBM (misses and promotions) */
+  uint64_t promotions;    /* experts moved into a resident slot by rebalance */
+  uint64_t prepares;
+  uint64_t rebalances;
+} moe_tier_stats;
+
+typedef struct moe_tier moe_tier;
+
+/* Validates (budget: MOE_ERR_BUDGET if the pool is below (L*R + S) slots)
+ * and creates the tier with no expert resident. */
+moe_status moe_tier_create(const moe_tier_desc* desc, moe_tier** out);
+
+/* After moe_bucket of layer `layer` on `compute`: stage this step's missing
+ * experts and fill table_dev (device moe_expert_ref [E]).  Blocks the host
+ * until the active list of this step is known (one event wait).  Returns
+ * MOE_ERR_BUDGET if the step has more misses than staging slots. */
+moe_status moe_tier_prepare(moe_tier* t, int32_t layer, const moe_buckets* b,
+                            moe_expert_ref* table_dev, hipStream_t compute);
+
+/* Make the R most used experts of `layer` (hist_dev: device uint32 [E], as
+ * updated by moe_expert_hist; ties to the lower index) resident, copying the
+ * newcomers into freed slots.  Synchronizes `compute` (reads the histogram). */
+moe_status moe_tier_rebalance(moe_tier* t, int32_t layer, const uint32_t* hist_dev,
+                              hipStream_t compute);
+
+/* Host copy of the counters; resident expert list of a layer (host int32 [R],
+ * -1 for an empty slot) when resident_out is not NULL. */
+moe_status moe_tier_stats_get(const moe_tier* t, moe_tier_stats* out, int32_t layer,
+                              int32_t* resident_out);
+
+/* Releases host metadata and events (not the caller's buffers). */
+void moe_tier_destroy(moe_tier* t);
+
 #ifdef __cplusplus
 }
 #endif

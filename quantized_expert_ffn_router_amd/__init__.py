@@ -60,7 +60,21 @@ class Buckets(ctypes.Structure):
                 ("T_max", ctypes.c_int64), ("E", ctypes.c_int32), ("k", ctypes.c_int32)]
 
 
+class TierDesc(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("resident_per_layer", ctypes.c_int32), ("staging_slots", ctypes.c_int32),
+                ("expert_bytes", ctypes.c_size_t), ("host_blobs", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("hbm_pool", ctypes.c_void_p),
+                ("hbm_pool_bytes", ctypes.c_size_t), ("copy_stream", ctypes.c_void_p)]
+
+
+class TierStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("hits", "misses", "h2d_bytes", "promotions", "prepares", "rebalances")]
+
+
 assert ctypes.sizeof(ExpertRef) == 24
+assert ctypes.sizeof(TierDesc) == 64
 assert ctypes.sizeof(LayerDesc) == 56
 assert ctypes.sizeof(Buckets) == 64
 
@@ -83,6 +97,11 @@ SIGNATURES = {
     "moe_expert_ffn": (ctypes.c_int, [_LP, _vp, _i64, _BP, _vp, _i32, _vp, _sz, _vp]),
     "moe_combine": (ctypes.c_int, [_LP, _vp, _i32, _BP, _vp, _i64, _vp, _vp, _vp]),
     "moe_expert_hist": (ctypes.c_int, [_LP, _BP, _vp, _i32, _i32, _vp]),
+    "moe_tier_create": (ctypes.c_int, [ctypes.POINTER(TierDesc), ctypes.POINTER(ctypes.c_void_p)]),
+    "moe_tier_prepare": (ctypes.c_int, [_vp, _i32, _BP, _vp, _vp]),
+    "moe_tier_rebalance": (ctypes.c_int, [_vp, _i32, _vp, _vp]),
+    "moe_tier_stats_get": (ctypes.c_int, [_vp, ctypes.POINTER(TierStats), _i32, _vp]),
+    "moe_tier_destroy": (None, [_vp]),
 }
 
 _lib = None
@@ -188,6 +207,33 @@ def moe_combine(desc, y, y_dtype, buckets, topk_w, T, residual, out, stream=None
 def moe_expert_hist(desc, buckets, hist, decay_shift, unit_shift, stream=None):
     _check(lib().moe_expert_hist(ctypes.byref(desc), ctypes.byref(buckets), _ptr(hist),
                                  decay_shift, unit_shift, _stream(stream)))
+
+
+def moe_tier_create(desc: TierDesc) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().moe_tier_create(ctypes.byref(desc), ctypes.byref(h)))
+    return h.value
+
+
+def moe_tier_prepare(tier, layer, buckets, table_dev, stream=None):
+    _check(lib().moe_tier_prepare(tier, layer, ctypes.byref(buckets), _ptr(table_dev),
+                                  _stream(stream)))
+
+
+def moe_tier_rebalance(tier, layer, hist, stream=None):
+    _check(lib().moe_tier_rebalance(tier, layer, _ptr(hist), _stream(stream)))
+
+
+def moe_tier_stats_get(tier, layer=0, R=0):
+    st = TierStats()
+    res = np.zeros(max(R, 1), np.int32)
+    _check(lib().moe_tier_stats_get(tier, ctypes.byref(st), layer,
+                                    res.ctypes.data if R else None))
+    return {n: getattr(st, n) for n, _ in TierStats._fields_}, res[:R]
+
+
+def moe_tier_destroy(tier):
+    lib().moe_tier_destroy(tier)
 
 
 # ---------------------------------------------------------------- device plumbing

@@ -99,6 +99,16 @@ bool use_gemm(const moe_layer_desc* L, int64_t T) {
 
 }  // namespace
 
+namespace moe {
+moe_status tier_fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+}  // namespace moe
+
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }

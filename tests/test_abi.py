@@ -121,3 +121,19 @@ def test_workspace_bytes_cover_hidden_buffers():
     ws = q.moe_workspace_bytes(d, 16384)
     assert ws >= 16384 * 8 * 768 * 4
     assert q.moe_workspace_bytes(d, 1) >= 8 * 768 * 4
+
+
+def test_tier_create_rejects_small_budget_before_any_hip_call():
+    E, L, R, S, eb = 8, 2, 4, 2, 1024
+    ptrs = (ctypes.c_void_p * (L * E))(*([0x1000] * (L * E)))
+    scales = (q.ExpertRef * (L * E))()
+    desc = q.TierDesc(L, E, R, S, eb, ctypes.addressof(ptrs), ctypes.addressof(scales), 0x100000,
+                      (L * R + S) * eb - 1, None)
+    with pytest.raises(q.MoeError) as ei:
+        q.moe_tier_create(desc)
+    assert ei.value.status == q.MOE_ERR_BUDGET
+    assert "HBM pool" in q.last_error()
+    desc.resident_per_layer = E + 1
+    with pytest.raises(q.MoeError) as ei:
+        q.moe_tier_create(desc)
+    assert ei.value.status == q.MOE_ERR_INVALID_ARG

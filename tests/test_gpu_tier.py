@@ -1,0 +1,104 @@
+"""Cold-expert tier on the GPU: a stack of layers whose non-resident experts
+are copied from pinned host memory on demand must compute bit-for-bit what
+the same stack computes with every expert resident; residency follows the
+usage histogram; a tiered layer matches the oracle (teacher-forced)."""
+import numpy as np
+import pytest
+
+import moegen
+import oracle
+from parity_util import check_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _stack_inputs(L=3, n_sets=2, E=64, k=4, H=256, I=256, s=1.2, alpha=0.39):
+    w = moegen.Workload("tierstack", E=E, k=k, H=H, I=I, T=8, fmt_down=moegen.FMT_Q6K)
+    sets = [moegen.make_layer(w, layer=i) for i in range(n_sets)]
+    routers = [moegen.normal_f32(moegen.key(0, moegen.TAG_ROUTER, 1000 + l), E * H, 0.02)
+               .reshape(E, H) for l in range(L)]
+
+    def bias(l, epoch):
+        b, _ = moegen.zipf_bias(moegen.key(0, moegen.TAG_BIAS, l, epoch), E, s, alpha)
+        return b
+    return w, sets, routers, bias
+
+
+def _run(stack, w, steps, rebalance_every=None):
+    import torch
+    outs = []
+    for st in range(steps):
+        x = torch.from_numpy(moegen.make_tokens(w, 8, step=st).view(np.int16).copy()).cuda()
+        stack.step(x, 8, epoch=st // 2)
+        if rebalance_every and (st + 1) % rebalance_every == 0:
+            stack.rebalance()
+        torch.cuda.synchronize()
+        outs.append(x.cpu().numpy().copy())
+    return outs
+
+
+def test_tiered_stack_equals_all_resident_bit_exact():
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    w, sets, routers, bias = _stack_inputs()
+    ref = LayerStack(sets, routers, bias, L=3, k=w.k)
+    tiered = LayerStack(sets, routers, bias, L=3, k=w.k,
+                        tiered={"resident": 16, "staging": 32})
+    a = _run(ref, w, 6)
+    b = _run(tiered, w, 6, rebalance_every=2)
+    for st, (u, v) in enumerate(zip(a, b)):
+        assert np.array_equal(u, v), f"step {st} differs"
+    import quantized_expert_ffn_router_amd as q
+    stats, _ = q.moe_tier_stats_get(tiered.tier)
+    assert stats["prepares"] == 6 * 3 and stats["rebalances"] == 3 * 3
+    assert stats["hits"] > 0 and stats["misses"] > 0
+    assert stats["h2d_bytes"] == (stats["misses"] + stats["promotions"]) * tiered.eb
+    tiered.close()
+
+
+def test_rebalance_keeps_top_R_by_histogram():
+    import torch
+    import quantized_expert_ffn_router_amd as q
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    w, sets, routers, bias = _stack_inputs(L=2)
+    st = LayerStack(sets, routers, bias, L=2, k=w.k, tiered={"resident": 16, "staging": 32})
+    rng = np.random.default_rng(3)
+    h = rng.integers(0, 50, size=w.E).astype(np.int32)  # many ties
+    st.hists[1].copy_(torch.from_numpy(h))
+    st.rebalance()
+    torch.cuda.synchronize()
+    _, res = q.moe_tier_stats_get(st.tier, layer=1, R=16)
+    order = sorted(range(w.E), key=lambda e: (-int(h[e]), e))[:16]
+    assert sorted(res.tolist()) == sorted(order)
+    st.close()
+
+
+def test_staging_overflow_is_reported():
+    import torch
+    import quantized_expert_ffn_router_amd as q
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    w, sets, routers, bias = _stack_inputs(L=1)
+    st = LayerStack(sets, routers, bias, L=1, k=w.k, tiered={"resident": 0, "staging": 2})
+    x = torch.from_numpy(moegen.make_tokens(w, 8).view(np.int16).copy()).cuda()
+    with pytest.raises(q.MoeError) as ei:
+        st.step(x, 8)
+    assert ei.value.status == q.MOE_ERR_BUDGET
+    torch.cuda.synchronize()
+    st.close()
+
+
+def test_tiered_layers_match_oracle_teacher_forced():
+    import torch
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    w, sets, routers, bias = _stack_inputs(L=3)
+    st = LayerStack(sets, routers, bias, L=3, k=w.k, tiered={"resident": 8, "staging": 32})
+    x = torch.from_numpy(moegen.make_tokens(w, 8, step=7).view(np.int16).copy()).cuda()
+    trace = []
+    st.step(x, 8, epoch=1, trace=trace)
+    torch.cuda.synchronize()
+    ins = [t.cpu().numpy().view(np.uint16) for t in trace] + [x.cpu().numpy().view(np.uint16)]
+    for l in range(3):
+        Lw = sets[l % 2]
+        layer = moegen.LayerWeights(**{**Lw.__dict__, "w_router": routers[l], "bias": bias(l, 1)})
+        ref = oracle.layer(ins[l], layer, residual=ins[l])
+        check_out(ins[l + 1], ref["out"])
+    st.close()
