@@ -154,8 +154,12 @@ class Workload:
     extra: dict = field(default_factory=dict)
 
 
-# Zipf-bias strengths fitted with the oracle router (moegen/fit_zipf_alpha.py).
-ZIPF_ALPHA = {"prefill": 0.44, "tiered": 0.39}
+# Zipf-bias strengths fitted with the oracle router; written by
+# moegen/fit_zipf_alpha.py into zipf_alpha.json.
+import json as _json
+
+with open(os.path.join(_HERE, "zipf_alpha.json")) as _f:
+    ZIPF_ALPHA = _json.load(_f)
 
 WORKLOADS = {
     # 8 experts, top-2, hidden 256, intermediate 128, 4 tokens, NVFP4 everywhere
