@@ -44,7 +44,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--prefill-steps", type=int, default=10)
-    p.add_argument("--cpu-sample-steps", type=int, default=4)
+    p.add_argument("--tiered-steps", type=int, default=2048,
+                   help="steps of the 48-layer tiered stack (0: skip)")
+    p.add_argument("--tiered-sets", type=int, default=4,
+                   help="distinct expert-weight sets shared round-robin by the 48 layers")
+    p.add_argument("--cpu-sample-steps", type=int, default=12)
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many eager steps per batch (for profilers)")
     return p.parse_args()
@@ -161,6 +165,9 @@ def main():
         return
 
     prefill = None if args.no_prefill else measure_prefill(args, q, moegen, torch, dev)
+    del layers, buf
+    torch.cuda.empty_cache()
+    tiered = None if args.tiered_steps <= 0 else measure_tiered(args, q, moegen, torch)
 
     head = results[Bmax]
     cpu = None
@@ -200,6 +207,7 @@ def main():
             for b in batches
         ],
         "prefill": prefill,
+        "tiered": tiered,
         "cpu_baseline": cpu,
         "setup_s": round(gen_s, 1),
     }
@@ -254,6 +262,83 @@ def measure_prefill(args, q, moegen, torch, dev):
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
         "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
                         "mean": float(counts.mean())},
+    }
+
+
+def measure_tiered(args, q, moegen, torch):
+    """48 stacked mixed-format layers (256 experts, top-8, hidden 2048,
+    intermediate 512, NVFP4 gate/up, Q6_K down), 96 experts resident per layer
+    in HBM, the rest in pinned host RAM copied on demand; 8 tokens per step;
+    router bias Zipf(1.2) with the ranking redrawn every 256 steps (drift);
+    resident sets rebalanced from the usage histograms every 8 steps."""
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    W = moegen.WORKLOADS["tiered"]
+    Lyr, R, S, T = W.extra["layers"], W.extra["resident"], 64, W.T
+    drift, rb_every = W.extra["drift"], 8
+    sets = [moegen.make_layer(W, layer=200 + i) for i in range(args.tiered_sets)]
+    routers = [moegen.normal_f32(moegen.key(0, moegen.TAG_ROUTER, 300 + l), W.E * W.H, W.w_std)
+               .reshape(W.E, W.H) for l in range(Lyr)]
+
+    def bias(l, epoch):
+        b, _ = moegen.zipf_bias(moegen.key(0, moegen.TAG_BIAS, 300 + l, epoch), W.E, W.zipf_s,
+                                W.zipf_alpha)
+        return b
+
+    stack = LayerStack(sets, routers, bias, L=Lyr, k=W.k, tiered={"resident": R, "staging": S})
+    del sets
+    # pinned host -> HBM copy ceiling on this box (one expert-sized copy stream)
+    hb = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    db = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    db.copy_(hb, non_blocking=True)
+    torch.cuda.synchronize()
+    t = time.time()
+    for _ in range(4):
+        db.copy_(hb, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d_ceiling = 4 * (256 << 20) / (time.time() - t) / 1e9
+    del hb, db
+    xs = [torch.from_numpy(moegen.make_tokens(W, T, step=s, layer=999).view(np.int16).copy()).cuda()
+          for s in range(16)]
+    x = torch.empty_like(xs[0])
+    stream = torch.cuda.current_stream()
+    for st in range(4):  # warm: first fill of the resident sets
+        x.copy_(xs[st % 16])
+        stack.step(x, T, epoch=0)
+    stack.rebalance()
+    torch.cuda.synchronize()
+    s0, _ = q.moe_tier_stats_get(stack.tier)
+    t = time.time()
+    per_epoch = []
+    prev = s0
+    for st in range(args.tiered_steps):
+        x.copy_(xs[st % 16])
+        stack.step(x, T, epoch=st // drift)
+        if (st + 1) % rb_every == 0:
+            stack.rebalance()
+        if (st + 1) % drift == 0:
+            cur, _ = q.moe_tier_stats_get(stack.tier)
+            per_epoch.append(round((cur["misses"] - prev["misses"]) /
+                                   max(1, (cur["misses"] - prev["misses"]) + (cur["hits"] - prev["hits"])), 4))
+            prev = cur
+    torch.cuda.synchronize()
+    wall = time.time() - t
+    s1, _ = q.moe_tier_stats_get(stack.tier)
+    stack.close()
+    d = {k: s1[k] - s0[k] for k in s1}
+    h2d_gbs = d["h2d_bytes"] / wall / 1e9
+    return {
+        "workload": "tiered decode: 48 layers x (256 experts, top-8, hidden 2048, intermediate "
+                    "512, NVFP4 gate/up, Q6_K down), 96 resident per layer, 8 tokens/step, "
+                    "Zipf(1.2) routing drifting every 256 steps",
+        "steps": args.tiered_steps, "wall_s": round(wall, 3),
+        "tok_per_s": round(T * args.tiered_steps / wall, 2),
+        "ms_per_step": round(wall / args.tiered_steps * 1e3, 3),
+        "miss_rate": round(d["misses"] / max(1, d["misses"] + d["hits"]), 4),
+        "miss_rate_per_epoch": per_epoch,
+        "h2d_GBps": round(h2d_gbs, 2), "pinned_h2d_ceiling_GBps": round(h2d_ceiling, 2),
+        "h2d_frac_of_ceiling": round(h2d_gbs / h2d_ceiling, 4),
+        "expert_sets": args.tiered_sets,
+        "counters": d,
     }
 
 
