@@ -257,15 +257,9 @@ moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   }
   // Worst-case number of active experts; workgroups past n_active exit.
   const int max_slots = (int)((T * L->k < L->E) ? T * L->k : L->E);
-  float* h = (float*)ws;
-  // Tokens per LDS pass: an expert gets at most T tokens; tiles stay <= 32 KiB.
-  const int mt_tok = (int)(T < moe::kMaxMT ? T : moe::kMaxMT);
-  const int mt_gu = mt_tok < 16384 / L->H ? mt_tok : 16384 / L->H;
-  const int mt_dn = mt_tok < 8192 / L->I ? mt_tok : 8192 / L->I;
-  hipError_t e = moe::launch_gemv_gateup(L, x, b, max_slots, mt_gu, h, stream);
-  if (e == hipSuccess) {
-    e = moe::launch_gemv_down(L, h, b, max_slots, mt_dn, y, y_dtype, stream);
-  }
+  uint16_t* h = (uint16_t*)ws;  // bf16 [T*k][I], sorted order
+  hipError_t e = moe::launch_gemv_gateup(L, x, b, max_slots, h, stream);
+  if (e == hipSuccess) e = moe::launch_gemv_down(L, h, b, max_slots, y, y_dtype, stream);
   return hip_status(W, e);
 }
 

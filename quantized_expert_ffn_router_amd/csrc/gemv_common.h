@@ -136,8 +136,12 @@ __device__ __forceinline__ bool slot_info(const int32_t* __restrict__ active,
                                           const moe_expert_ref* __restrict__ experts,
                                           SlotInfo* si) {
   const int slot = blockIdx.y;
-  if (slot >= *n_active) return false;
-  si->e = active[slot];
+  // Both loads in one round trip: active[] has E >= gridDim.y entries, so
+  // active[slot] is in bounds even for a slot past n_active (then unused).
+  const int na = __builtin_nontemporal_load(n_active);
+  const int e = __builtin_nontemporal_load(active + slot);
+  if (slot >= na) return false;
+  si->e = e;
   si->cnt = (int)counts[si->e];
   si->base = offsets[si->e];
   si->ref = experts[si->e];
@@ -175,11 +179,12 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
                            const moe_buckets* b, uint16_t* hbuf, void* tiles_ws, void* y,
                            int y_dtype, hipStream_t s);
 
-// mt_max: tokens gathered per pass (<= kMaxMT; an expert gets at most T).
+// h passes from the gate/up kernel to the down kernel as bf16 [A][I] (sorted
+// order).
 hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
-                              int max_slots, int mt_max, float* h, hipStream_t s);
-hipError_t launch_gemv_down(const moe_layer_desc* L, const float* h, const moe_buckets* b,
-                            int max_slots, int mt_max, void* y, int y_dtype, hipStream_t s);
+                              int max_slots, uint16_t* h, hipStream_t s);
+hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const moe_buckets* b,
+                            int max_slots, void* y, int y_dtype, hipStream_t s);
 
 
 }  // namespace moe

@@ -6,17 +6,22 @@
 //     2-bit plane, int8 sub-scale per 16 elements, fp16 scale d:
 //     w = d * sc * (q - 32).
 // Weights are decoded exactly to bf16 (E2M1 has 2 significant bits, q - 32 is
-// a 6-bit integer) and h is staged in LDS as a bf16 pair hi + lo (h - hi - lo
-// is below 2^-16 |h|), so v_dot2_f32_bf16 on (w, hi) and (w, lo) gives
-// fp32-grade products with fp32 accumulation.  Each 16-element block sum is
-// scaled by its block scale (E4M3, or d * sc).  A workgroup owns 64 rows of
-// one active expert; its S waves split K into 128-element groups
-// (gemv_common.h), loads kept D groups ahead in group order.
+// a 6-bit integer) and meet h (bf16, from the gate/up kernel) in
+// v_dot2_f32_bf16 with fp32 accumulation.  Each 16-element block sum is scaled
+// by its block scale (E4M3, or d * sc).  A workgroup owns 64 rows of one
+// active expert; its S waves split K into 128-element groups (gemv_common.h),
+// loads kept D groups ahead in group order.  Every lane needs every h value of
+// its K-slice (lanes are rows), so h is read with wave-uniform addresses:
+// scalar loads, SGPR operands of v_dot2, no per-value VALU broadcast (the
+// kernel is otherwise close to its VALU budget).  Each wave accumulates its
+// per-token sums in its own LDS slice.
 #include "gemv_common.h"
 
 namespace moe {
 
 namespace {
+
+constexpr int kDnMT = 16;  // tokens per batch (an expert's further tokens take more batches)
 
 // Raw bytes of one 128-element group of a row.
 template <int FMT>
@@ -93,16 +98,26 @@ __device__ __forceinline__ void decode_group(const Group<MOE_FMT_Q6K>& r, float 
   }
 }
 
+// Issue the loads of the first D groups of a pass.
 template <int FMT, int GP, int D>
-__device__ __forceinline__ void down_pass(const uint16_t* hsh, const uint16_t* hsl, int H, int I,
-                                          size_t nc, const Planes& P, float ts, int gb, int mt,
-                                          float* myred) {
-  Group<FMT> r[GP];
+__device__ __forceinline__ void dn_issue(Group<FMT> (&r)[GP], const Planes& P, int H, size_t nc,
+                                         int gb) {
 #pragma unroll
   for (int gi = 0; gi < GP && gi < D; ++gi) {
     load_group(r[gi], P, H, nc, gb + gi);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// One pass of GP groups over the mt rows of h at sorted positions p0..
+// (wave-uniform addresses, so scalar loads), the first D groups already in
+// flight; the rest are issued D groups ahead of use.  The token loop is a
+// plain loop (the register footprint does not grow with the batch); per-token
+// sums accumulate in acc[t * 64 + lane].
+template <int FMT, int GP, int D>
+__device__ __forceinline__ void dn_consume(Group<FMT> (&r)[GP], const uint16_t* __restrict__ h,
+                                           int p0, int H, int I, size_t nc, const Planes& P,
+                                           float ts, int gb, int mt, float* acc) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int gi = 0; gi < GP; ++gi) {
@@ -114,42 +129,36 @@ __device__ __forceinline__ void down_pass(const uint16_t* hsh, const uint16_t* h
     v2bf_t w[8][8];
     float sc[8];
     decode_group(r[gi], ts, w, sc);
+#pragma unroll 1
     for (int t = 0; t < mt; ++t) {
-      const uint4* ph = reinterpret_cast<const uint4*>(hsh + (size_t)t * I + 128 * g);
-      const uint4* pl = reinterpret_cast<const uint4*>(hsl + (size_t)t * I + 128 * g);
+      const uint32_t* hp = reinterpret_cast<const uint32_t*>(h + (size_t)(p0 + t) * I) + 64 * g;
       float a = 0.0f;
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
-        const uint4 h0 = ph[2 * b], h1 = ph[2 * b + 1], l0 = pl[2 * b], l1 = pl[2 * b + 1];
-        const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-        const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         float p = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][i], as_v2bf(hw[i]), p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][i], as_v2bf(lw[i]), p, false);
-        }
+        for (int i = 0; i < 8; ++i)
+          p = __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(hp[8 * b + i]), w[b][i], p, false);
         a = fmaf(p, sc[b], a);
       }
-      myred[t * 64 + lane] += a;
+      acc[t * 64 + lane] += a;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int FMT, int GP, int D, bool BF16>
-__global__ __launch_bounds__(512, 3) void k_gemv_down(
-    const float* __restrict__ hin, int H, int I, int mt_max, int S, int gps_total, Planes P0,
+__global__ __launch_bounds__(512) void k_gemv_down(
+    const uint16_t* __restrict__ h, int H, int I, int S, int gps_total, Planes P0,
     const moe_expert_ref* __restrict__ experts, const uint32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const int32_t* __restrict__ n_active, void* __restrict__ y) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* hsh = reinterpret_cast<uint16_t*>(smem);                      // [mt_max][I] hi
-  uint16_t* hsl = hsh + (size_t)mt_max * I;                               // [mt_max][I] lo
-  float* red = reinterpret_cast<float*>(hsl + (size_t)mt_max * I);        // [S][mt_max][64]
+  extern __shared__ __align__(16) float red[];  // [S][kDnMT][64]
 
   SlotInfo si;
   if (!slot_info(active, n_active, counts, offsets, experts, &si)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int nthreads = S * 64;
   const int n = blockIdx.x * 64 + lane;
   const size_t nc = (n < H) ? (size_t)n : 0;  // rows past the end read row 0, never stored
@@ -158,44 +167,33 @@ __global__ __launch_bounds__(512, 3) void k_gemv_down(
                     (const uint8_t*)(blob + (uintptr_t)P0.c), (const uint8_t*)(blob + (uintptr_t)P0.d)};
   const float ts = (FMT == MOE_FMT_NVFP4) ? si.ref.ts_down : 1.0f;
   const int gb = wave * gps_total;
-  float* myred = red + (size_t)wave * mt_max * 64;
+  float* acc = red + (size_t)wave * kDnMT * 64;
 
-  for (int c0 = 0; c0 < si.cnt; c0 += mt_max) {
-    const int mt = min(mt_max, si.cnt - c0);
-    // Stage h rows as hi/lo bf16 pairs.
-    const int vpr = I >> 2;
-    for (int i = tid; i < mt * vpr; i += nthreads) {
-      const int r = i / vpr, c = i - r * vpr;
-      const float4 v = reinterpret_cast<const float4*>(hin + (size_t)(si.base + c0 + r) * I)[c];
-      const v2bf_t h01 = to_v2bf(v.x, v.y), h23 = to_v2bf(v.z, v.w);
-      const v2f_t f01 = __builtin_convertvector(h01, v2f_t), f23 = __builtin_convertvector(h23, v2f_t);
-      const v2bf_t l01 = to_v2bf(v.x - f01.x, v.y - f01.y), l23 = to_v2bf(v.z - f23.x, v.w - f23.y);
-      uint2* dh = reinterpret_cast<uint2*>(hsh + (size_t)r * I) + c;
-      uint2* dl = reinterpret_cast<uint2*>(hsl + (size_t)r * I) + c;
-      *dh = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
-      *dl = make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
+  for (int c0 = 0; c0 < si.cnt; c0 += kDnMT) {
+    const int mt = min(kDnMT, si.cnt - c0);
+    __syncthreads();  // the previous batch's reads of red are done
+    for (int t = 0; t < mt; ++t) acc[t * 64 + lane] = 0.0f;  // this wave's slice only
+    for (int sg = 0; sg < gps_total; sg += GP) {
+      Group<FMT> r[GP];
+      dn_issue<FMT, GP, D>(r, P, H, nc, gb + sg);
+      dn_consume<FMT, GP, D>(r, h, si.base + c0, H, I, nc, P, ts, gb + sg, mt, acc);
     }
-    for (int t = 0; t < mt; ++t) myred[t * 64 + lane] = 0.0f;
-    __syncthreads();
-    for (int sg = 0; sg < gps_total; sg += GP)
-      down_pass<FMT, GP, D>(hsh, hsl, H, I, nc, P, ts, gb + sg, mt, myred);
     __syncthreads();
     for (int o = tid; o < mt * 64; o += nthreads) {
-      const int t = o >> 6, r = o & 63;
-      const int n2 = blockIdx.x * 64 + r;
+      const int t = o >> 6, rr = o & 63;
+      const int n2 = blockIdx.x * 64 + rr;
       if (n2 < H) {
         float sum = 0.0f;
-        for (int w = 0; w < S; ++w) sum += red[(w * mt_max + t) * 64 + r];
+        for (int w = 0; w < S; ++w) sum += red[((size_t)w * kDnMT + t) * 64 + rr];
         store_y<BF16>(y, (size_t)(si.base + c0 + t) * H + n2, sum);
       }
     }
-    __syncthreads();
   }
 }
 
 template <int FMT, int GP>
-hipError_t down_t(const moe_layer_desc* L, const float* h, const moe_buckets* b, int max_slots,
-                  int mt_max, int S, int gps_total, void* y, int y_dtype, hipStream_t s) {
+hipError_t down_t(const moe_layer_desc* L, const uint16_t* h, const moe_buckets* b,
+                  int max_slots, int S, int gps_total, void* y, int y_dtype, hipStream_t s) {
   constexpr int D = GP < 2 ? GP : 2;
   const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
   Planes P;
@@ -206,43 +204,49 @@ hipError_t down_t(const moe_layer_desc* L, const float* h, const moe_buckets* b,
          (const uint8_t*)lay.down_d};
   }
   dim3 grid((unsigned)((L->H + 63) / 64), (unsigned)max_slots);
-  size_t lds = (size_t)mt_max * L->I * 4 + sizeof(float) * (size_t)S * mt_max * 64;
+  const size_t lds = sizeof(float) * (size_t)S * kDnMT * 64;
   if (y_dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL((k_gemv_down<FMT, GP, D, true>), grid, dim3(S * 64), lds, s, h, L->H,
-                       L->I, mt_max, S, gps_total, P, L->experts, b->counts, b->offsets,
-                       b->active, b->n_active, y);
+    hipLaunchKernelGGL((k_gemv_down<FMT, GP, D, true>), grid, dim3(S * 64), lds, s, h, L->H, L->I,
+                       S, gps_total, P, L->experts, b->counts, b->offsets, b->active,
+                       b->n_active, y);
   else
     hipLaunchKernelGGL((k_gemv_down<FMT, GP, D, false>), grid, dim3(S * 64), lds, s, h, L->H,
-                       L->I, mt_max, S, gps_total, P, L->experts, b->counts, b->offsets,
-                       b->active, b->n_active, y);
+                       L->I, S, gps_total, P, L->experts, b->counts, b->offsets, b->active,
+                       b->n_active, y);
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t down_fmt(const moe_layer_desc* L, const float* h, const moe_buckets* b, int max_slots,
-                    int mt_max, void* y, int y_dtype, hipStream_t s) {
+hipError_t down_fmt(const moe_layer_desc* L, const uint16_t* h, const moe_buckets* b,
+                    int max_slots, void* y, int y_dtype, hipStream_t s) {
   const int NG = L->I / 128;
-  const int RB = (L->H + 63) / 64;
-  const int S = choose_split(max_slots * RB, 1, NG, 8);  // <= 8 waves
+  // One row block of 64 rows per workgroup; S waves split K (the largest
+  // divisor of NG up to 8 that leaves each wave at least two groups).
+  int S = 1;
+  for (int c = 2; c <= 8; ++c)
+    if (NG % c == 0 && NG / c >= 2) S = c;
   const int gps_total = NG / S;
   const int gp_max = (FMT == MOE_FMT_Q6K) ? 2 : 4;  // register budget (no spills)
   int GP = gps_total > gp_max ? gp_max : gps_total;
   while (gps_total % GP) --GP;
-  switch (GP) {
-    case 1: return down_t<FMT, 1>(L, h, b, max_slots, mt_max, S, gps_total, y, y_dtype, s);
-    case 2: return down_t<FMT, 2>(L, h, b, max_slots, mt_max, S, gps_total, y, y_dtype, s);
-    case 3: return down_t<FMT, 3>(L, h, b, max_slots, mt_max, S, gps_total, y, y_dtype, s);
-    default: return down_t<FMT, 4>(L, h, b, max_slots, mt_max, S, gps_total, y, y_dtype, s);
+  if (GP == 1) return down_t<FMT, 1>(L, h, b, max_slots, S, gps_total, y, y_dtype, s);
+  if constexpr (FMT == MOE_FMT_Q6K) {
+    return down_t<FMT, 2>(L, h, b, max_slots, S, gps_total, y, y_dtype, s);
+  } else {
+    switch (GP) {
+      case 2: return down_t<FMT, 2>(L, h, b, max_slots, S, gps_total, y, y_dtype, s);
+      case 3: return down_t<FMT, 3>(L, h, b, max_slots, S, gps_total, y, y_dtype, s);
+      default: return down_t<FMT, 4>(L, h, b, max_slots, S, gps_total, y, y_dtype, s);
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemv_down(const moe_layer_desc* L, const float* h, const moe_buckets* b,
-                            int max_slots, int mt_max, void* y, int y_dtype, hipStream_t s) {
-  if (L->fmt_down == MOE_FMT_Q6K)
-    return down_fmt<MOE_FMT_Q6K>(L, h, b, max_slots, mt_max, y, y_dtype, s);
-  return down_fmt<MOE_FMT_NVFP4>(L, h, b, max_slots, mt_max, y, y_dtype, s);
+hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const moe_buckets* b,
+                            int max_slots, void* y, int y_dtype, hipStream_t s) {
+  if (L->fmt_down == MOE_FMT_Q6K) return down_fmt<MOE_FMT_Q6K>(L, h, b, max_slots, y, y_dtype, s);
+  return down_fmt<MOE_FMT_NVFP4>(L, h, b, max_slots, y, y_dtype, s);
 }
 
 }  // namespace moe

@@ -6,88 +6,122 @@
 // E2M1 codes become exact bf16 pairs that meet the bf16 activations in
 // v_dot2_f32_bf16 (fp32 accumulation); each 16-element block sum is scaled by
 // its E4M3 scale (hardware conversion), the per-tensor scale by the total.
+//
+// Every lane of a wave needs the same activations (lanes are rows), so they
+// are read with wave-uniform addresses: the compiler turns those into scalar
+// loads through the scalar cache and feeds them to v_dot2 as SGPR operands.
+// A broadcast from LDS instead costs a full 64-lane LDS read per 8 values,
+// which measured as the limit of the kernel at batch 8.
+// h leaves rounded to bf16 (the operand type of v_dot2 in the down
+// projection), as in the prefill path.
 #include "gemv_common.h"
 
 namespace moe {
 
 namespace {
 
-// One pass over the mt staged tokens.  GPS groups per wave (the group loop
-// unrolls fully, so the prefetch needs no loop-carried registers), D groups of
-// weight loads in flight ahead of use.  Each group's codes and scales are
-// decoded right after they arrive, before any per-token branch, so the load
-// registers die at once and nothing waits on memory inside the token loop.
-template <int GPS, int D>
-__device__ __forceinline__ void gateup_pass(const uint16_t* xs, int H, int I, size_t nc,
-                                            const uint8_t* pq, const uint8_t* ps, int gb,
-                                            int mt, float* acc) {
+constexpr int kGuMT = 16;  // tokens per batch (an expert's further tokens take more batches)
+
+// Register ring of one pass: GPS groups of 128 elements (64 code bytes and 8
+// E4M3 scale bytes per lane each).
+template <int GPS>
+struct GURing {
   uint4 rc[GPS][4];
   uint2 rs[GPS];
-  // Group loads are issued in group order (scheduling barriers keep them
-  // apart) so that waiting for group gi never waits for a later group.
+};
+
+// Issue the loads of the first D groups of a pass.
+template <int GPS, int D>
+__device__ __forceinline__ void gu_issue(GURing<GPS>& R, const uint8_t* pq, const uint8_t* ps,
+                                         int I, size_t nc, int gb) {
 #pragma unroll
   for (int gi = 0; gi < GPS && gi < D; ++gi) {
     const int g = gb + gi;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rc[gi][q] = ld16(pq + (((size_t)(4 * g + q)) * I + nc) * 16);
-    rs[gi] = ld8(ps + ((size_t)g * I + nc) * 8);
+    for (int q = 0; q < 4; ++q) R.rc[gi][q] = ld16(pq + (((size_t)(4 * g + q)) * I + nc) * 16);
+    R.rs[gi] = ld8(ps + ((size_t)g * I + nc) * 8);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// Row offset (elements) of the token of sorted assignment p: p's token is
+// sorted_asg[p] / k (k a power of two in every shipped layer; the shift is
+// negative otherwise and a division is used).
+__device__ __forceinline__ size_t token_row(const int32_t* __restrict__ sorted_asg, int p,
+                                            int ktop, int kshift, int H) {
+  const int a = sorted_asg[p];
+  const int tok = kshift >= 0 ? (a >> kshift) : a / ktop;
+  return (size_t)tok * H;
+}
+
+// One pass of GPS groups over the mt tokens of sorted positions p0.., the
+// first D groups already in flight.  The group loop unrolls fully, so the
+// ring needs no loop-carried registers; D groups of weight loads stay in
+// flight ahead of use, issued in group order (scheduling barriers keep them
+// apart) so that waiting for group gi never waits for a later group.  Each
+// group is decoded once to bf16 pairs; the token loop is a plain loop (the
+// register footprint does not grow with the batch) whose activations come
+// from scalar loads and whose per-token sums accumulate in this wave's LDS
+// slice acc[t * 64 + lane].
+template <int GPS, int D>
+__device__ __forceinline__ void gu_consume(GURing<GPS>& R, const uint16_t* __restrict__ x,
+                                           const int32_t* __restrict__ sorted_asg, int p0,
+                                           int ktop, int kshift, int H, int I, size_t nc,
+                                           const uint8_t* pq, const uint8_t* ps, int gb, int mt,
+                                           float* acc) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int gi = 0; gi < GPS; ++gi) {
     if (gi + D < GPS) {  // keep D groups in flight
       const int g2 = gb + gi + D;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) rc[gi + D][q] = ld16(pq + (((size_t)(4 * g2 + q)) * I + nc) * 16);
-      rs[gi + D] = ld8(ps + ((size_t)g2 * I + nc) * 8);
+      for (int q = 0; q < 4; ++q)
+        R.rc[gi + D][q] = ld16(pq + (((size_t)(4 * g2 + q)) * I + nc) * 16);
+      R.rs[gi + D] = ld8(ps + ((size_t)g2 * I + nc) * 8);
       __builtin_amdgcn_sched_barrier(0);
     }
     const int g = gb + gi;
     float sc[8];
-    e4m3x8(rs[gi], sc);
+    e4m3x8(R.rs[gi], sc);
     v2bf_t w[8][8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      e2m1x8_bf16(word_of(rc[gi][b >> 1], (b & 1) * 2), w[b]);
-      e2m1x8_bf16(word_of(rc[gi][b >> 1], (b & 1) * 2 + 1), w[b] + 4);
+      e2m1x8_bf16(word_of(R.rc[gi][b >> 1], (b & 1) * 2), w[b]);
+      e2m1x8_bf16(word_of(R.rc[gi][b >> 1], (b & 1) * 2 + 1), w[b] + 4);
     }
+#pragma unroll 1
+    for (int t = 0; t < mt; ++t) {
+      const uint32_t* xp =
+          reinterpret_cast<const uint32_t*>(x + token_row(sorted_asg, p0 + t, ktop, kshift, H)) +
+          64 * g;
+      float a = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kMaxMT; ++t) {
-      if (t < mt) {
-        const uint4* xp = reinterpret_cast<const uint4*>(xs + (size_t)t * H + 128 * g);
+      for (int b = 0; b < 8; ++b) {
+        float p = 0.0f;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const uint4 xa = xp[2 * b], xb = xp[2 * b + 1];
-          float p = 0.0f;
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][0], as_v2bf(xa.x), p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][1], as_v2bf(xa.y), p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][2], as_v2bf(xa.z), p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][3], as_v2bf(xa.w), p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][4], as_v2bf(xb.x), p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][5], as_v2bf(xb.y), p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][6], as_v2bf(xb.z), p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(w[b][7], as_v2bf(xb.w), p, false);
-          acc[t] = fmaf(p, sc[b], acc[t]);
-        }
+        for (int i = 0; i < 8; ++i)
+          p = __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(xp[8 * b + i]), w[b][i], p, false);
+        a = fmaf(p, sc[b], a);
       }
+      acc[t * 64 + lane] += a;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int GPS, int D>
-__global__ __launch_bounds__(512, 3) void k_gemv_gateup_nvfp4(
-    const uint16_t* __restrict__ x, int H, int I, int ktop, int mt_max, int S, int gps_total,
+__global__ __launch_bounds__(512) void k_gemv_gateup_nvfp4(
+    const uint16_t* __restrict__ x, int H, int I, int ktop, int kshift, int S, int gps_total,
     const moe_expert_ref* __restrict__ experts, size_t off_gq, size_t off_gs, size_t off_uq,
     size_t off_us, const uint32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_asg, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, float* __restrict__ hout) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                       // [mt_max][H]
-  float* red = reinterpret_cast<float*>(smem + (size_t)mt_max * H * 2);   // [2S][mt_max][64]
+    const int32_t* __restrict__ n_active, uint16_t* __restrict__ hout) {
+  __shared__ float red[8][kGuMT][64];  // [wave][token][row] partial sums over K
 
   SlotInfo si;
   if (!slot_info(active, n_active, counts, offsets, experts, &si)) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int nthreads = 2 * S * 64;
   const int mat = wave / S, ks = wave - mat * S;
   const int n = blockIdx.x * 64 + lane;
@@ -96,30 +130,18 @@ __global__ __launch_bounds__(512, 3) void k_gemv_gateup_nvfp4(
   const uint8_t* pq = blob + (mat ? off_uq : off_gq);
   const uint8_t* ps = blob + (mat ? off_us : off_gs);
   const int gb = ks * gps_total;
-  const int vpr = H >> 3;
+  float* acc = &red[wave][0][0];
 
-  for (int c0 = 0; c0 < si.cnt; c0 += mt_max) {
-    const int mt = min(mt_max, si.cnt - c0);
-    // Gather this pass's token rows (bf16) into LDS before the weight loads
-    // (memory counters retire in order).
-    for (int i = tid; i < mt * vpr; i += nthreads) {
-      const int r = i / vpr, c = i - r * vpr;
-      const int tok = sorted_asg[si.base + c0 + r] / ktop;
-      reinterpret_cast<uint4*>(xs + (size_t)r * H)[c] =
-          reinterpret_cast<const uint4*>(x + (size_t)tok * H)[c];
+  for (int c0 = 0; c0 < si.cnt; c0 += kGuMT) {
+    const int mt = min(kGuMT, si.cnt - c0);
+    __syncthreads();  // the previous batch's reads of red are done
+    for (int t = 0; t < mt; ++t) acc[t * 64 + lane] = 0.0f;  // this wave's slice only
+    for (int sg = 0; sg < gps_total; sg += GPS) {  // passes of GPS groups
+      GURing<GPS> R;
+      gu_issue<GPS, D>(R, pq, ps, I, nc, gb + sg);
+      gu_consume<GPS, D>(R, x, sorted_asg, si.base + c0, ktop, kshift, H, I, nc, pq, ps, gb + sg,
+                         mt, acc);
     }
-    __syncthreads();
-
-    float acc[kMaxMT];
-#pragma unroll
-    for (int t = 0; t < kMaxMT; ++t) acc[t] = 0.0f;
-    for (int sg = 0; sg < gps_total; sg += GPS)  // passes of GPS groups
-      gateup_pass<GPS, D>(xs, H, I, nc, pq, ps, gb + sg, mt, acc);
-
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < kMaxMT; ++t)
-      if (t < mt) red[(wave * mt_max + t) * 64 + lane] = acc[t];
     __syncthreads();
     for (int o = tid; o < mt * 64; o += nthreads) {
       const int t = o >> 6, r = o & 63;
@@ -127,12 +149,13 @@ __global__ __launch_bounds__(512, 3) void k_gemv_gateup_nvfp4(
       if (n2 < I) {
         float gsum = 0.0f, usum = 0.0f;
         for (int w = 0; w < S; ++w) {
-          gsum += red[(w * mt_max + t) * 64 + r];
-          usum += red[((S + w) * mt_max + t) * 64 + r];
+          gsum += red[w][t][r];
+          usum += red[S + w][t][r];
         }
         gsum *= si.ref.ts_gate;
         usum *= si.ref.ts_up;
-        hout[(size_t)(si.base + c0 + t) * I + n2] = gsum / (1.0f + expf(-gsum)) * usum;
+        const float h = gsum / (1.0f + expf(-gsum)) * usum;
+        hout[(size_t)(si.base + c0 + t) * I + n2] = f32_to_bf16_rne(h);
       }
     }
   }
@@ -141,26 +164,30 @@ __global__ __launch_bounds__(512, 3) void k_gemv_gateup_nvfp4(
 }  // namespace
 
 hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
-                              int max_slots, int mt_max, float* h, hipStream_t s) {
+                              int max_slots, uint16_t* h, hipStream_t s) {
   const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
   const int NG = L->H / 128;
   const int RB = (L->I + 63) / 64;
-  // K split over S <= 4 waves per matrix (divisor of NG, within the wave
-  // budget); each wave takes NG/S groups in passes of GP <= 8 groups.
-  const int S = choose_split(max_slots * RB, 2, NG, 4);
+  // K split over S <= 4 waves per matrix (the largest divisor of NG up to 4);
+  // each wave takes NG/S groups in passes of GP <= 8 groups.
+  int S = 4;
+  while (NG % S) --S;
   const int gps_total = NG / S;
   int GP = gps_total;
   if (GP > 8) {
     GP = 8;
     while (gps_total % GP) --GP;
   }
+  int kshift = -1;
+  for (int i = 0; i < 31; ++i)
+    if ((1 << i) == L->k) kshift = i;
   dim3 grid((unsigned)RB, (unsigned)max_slots);
   dim3 block((unsigned)(2 * S * 64));
-  size_t lds = (size_t)mt_max * L->H * 2 + sizeof(float) * 2 * S * mt_max * 64;
-#define GU_LAUNCH(G)                                                                          \
-  hipLaunchKernelGGL((k_gemv_gateup_nvfp4<G, (G < 2 ? G : 2)>), grid, block, lds, s, x, L->H, \
-                     L->I, L->k, mt_max, S, gps_total, L->experts, lay.gate_q, lay.gate_s, lay.up_q,      \
-                     lay.up_s, b->counts, b->offsets, b->sorted_asg, b->active, b->n_active, h)
+#define GU_LAUNCH(G)                                                                           \
+  hipLaunchKernelGGL((k_gemv_gateup_nvfp4<G, (G < 2 ? G : 2)>), grid, block, 0, s, x, L->H,   \
+                     L->I, L->k, kshift, S, gps_total, L->experts, lay.gate_q, lay.gate_s,     \
+                     lay.up_q, lay.up_s, b->counts, b->offsets, b->sorted_asg, b->active,      \
+                     b->n_active, h)
   switch (GP) {
     case 1: GU_LAUNCH(1); break;
     case 2: GU_LAUNCH(2); break;

@@ -72,7 +72,13 @@ def check_out(g_out, o_out):
     return float(err.max()), r
 
 
-def check_layer(L, x, residual=None, y_dtype=0, tokens=None, y_rel=1e-4, ffn_mode=0):
+# Expert outputs y: both FFN families round h to bf16 before the down
+# projection (relative error <= 2^-9 per element, about 1.1e-3 relative L2 on
+# y for incoherent errors); the bar is the layer's own 5e-3.
+Y_REL = 5e-3
+
+
+def check_layer(L, x, residual=None, y_dtype=0, tokens=None, y_rel=Y_REL, ffn_mode=0):
     """Full-layer parity; FFN compared on `tokens` (all when None)."""
     g = run_gpu(L, x, residual, y_dtype, ffn_mode=ffn_mode)
     logits, idx, w = check_route(g, L, x)

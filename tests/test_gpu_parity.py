@@ -1,8 +1,8 @@
 """GPU parity: every step of the HIP path against the oracle, element by
 element, on the same seeded inputs.  Routing logits, indices, bucket arrays and
 the histogram must match bit for bit; gate weights within 1e-6; the bf16 layer
-output within max-abs 2e-2 and relative L2 5e-3 (and the fp32 expert outputs
-within relative L2 1e-4)."""
+output within max-abs 2e-2 and relative L2 5e-3, and the expert outputs y
+within relative L2 5e-3 (h is rounded to bf16 before the down projection)."""
 import numpy as np
 import pytest
 
@@ -128,8 +128,7 @@ def test_both_ffn_families_on_the_same_ragged_batch(mode):
     # mode 1 forces the GEMV kernels, mode 2 the MFMA grouped GEMM.
     w, L = layer("many", E=64, k=8, H=256, I=128, T=600)
     x = moegen.make_tokens(w, w.T, step=5)
-    check_layer(L, x, tokens=list(range(0, 600, 5)), ffn_mode=mode,
-                y_rel=1e-4 if mode == 1 else GEMM_Y_REL)
+    check_layer(L, x, tokens=list(range(0, 600, 5)), ffn_mode=mode, y_rel=GEMM_Y_REL)
 
 
 def test_gemm_multiple_column_tiles_and_k_steps():
