@@ -51,7 +51,45 @@ def parse():
     p.add_argument("--cpu-sample-steps", type=int, default=12)
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many eager steps per batch (for profilers)")
+    p.add_argument("--profile-prefill", type=int, default=0,
+                   help="only run this many prefill steps (for profilers)")
+    p.add_argument("--copy-calibration", type=int, default=0,
+                   help="only copy this many MiB device to device 8 times (counter calibration)")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.md")
+
+
+def sources_digest():
+    """sha256 over the library's kernel sources: counter readings are only
+    used while the kernels they were taken on are unchanged."""
+    import hashlib
+    d = os.path.join(ROOT, "quantized_expert_ffn_router_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind):
+    """HBM bytes per FFN call from the committed FETCH_SIZE / WRITE_SIZE
+    summary, each scaled by its copy-kernel calibration factor; None when the
+    summary is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(blob)
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_digest() or kind not in rec:
+        return None
+    r = rec[kind]
+    return (r["fetch_kib_per_call"] * rec["fetch_factor"] +
+            r["write_kib_per_call"] * rec["write_factor"]) * 1024.0
 
 
 def main():
@@ -69,6 +107,21 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # A plain elementwise kernel that reads n bytes and writes n bytes.
+        n = args.copy_calibration << 20
+        a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(8):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "copies": 8}))
+        return
+    if args.profile_prefill:
+        args.prefill_steps = args.profile_prefill
+        print(json.dumps({"profile_run": True, "prefill": measure_prefill(args, q, moegen, torch, dev)}))
+        return
     W = moegen.WORKLOADS["decode"]
     batches = [int(b) for b in args.batches.split(",")]
     Bmax = max(batches)
@@ -200,7 +253,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(head["ffn_hbm_frac"], 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode_ffn_b8"),
         },
         "per_batch": [
             {k: (round(v, 4) if isinstance(v, float) else v) for k, v in results[b].items()}
@@ -259,7 +312,8 @@ def measure_prefill(args, q, moegen, torch, dev):
         "ffn_tflops": round(tflops, 2),
         "roofline": {"kernel": "grouped GEMM (k_gemm_gateup_nvfp4 + k_gemm_down)", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("prefill_ffn")},
         "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
                         "mean": float(counts.mean())},
     }
