@@ -11,12 +11,14 @@
 //   - tile order is XCD-aware: consecutive workgroup ids go to different XCDs
 //     (8), so logical tiles are laid out XCD-major and the column tiles of one
 //     token block share that XCD's L2 for the re-read token rows;
-//   - per K step of 64: the A tile (gathered bf16 token rows, or the bf16 h
-//     rows of the down projection) is copied to LDS; the B tile is read from
-//     the packed weight blob, dequantized exactly to bf16 (E2M1 x E4M3 has at
-//     most 6 significant bits, Q6_K d*sc*(q-32) at most 24 and is rounded to
-//     bf16 -- see the design notes) and written to LDS; the next K step's
-//     global data is loaded into registers while the MFMAs of this one run;
+//   - per K step of 128: the A tile (gathered bf16 token rows, or the bf16 h
+//     rows of the down projection) is copied to LDS; each wave reads its B
+//     fragments from the packed weight blob (one 16-byte granule per lane and
+//     column tile, see "B fragments") and dequantizes them in registers,
+//     exactly to bf16 (E2M1 x E4M3 has at most 6 significant bits; Q6_K
+//     d*sc*(q-32) has up to 24 and is rounded to bf16 -- see the design
+//     notes); the next K step's global data is loaded into registers while
+//     the MFMAs of this one run;
 //   - 4 waves, each a 64 x 64 sub-tile = 4 x 4 v_mfma_f32_16x16x32_bf16 tiles
 //     with fp32 accumulation;
 //   - gate/up: the 128 B columns are 64 gate rows and the same 64 up rows of
@@ -66,34 +68,50 @@ __device__ __forceinline__ int logical_tile(int total) {
 }
 
 // ---------------------------------------------------------------- B fragments
-// Lane l of a wave feeds column n0 + l%16 of a 16-column MFMA tile with the
-// 8 K-elements k0 + 8*(l/16) .. +8 of a 32-element K step.  In the packed
-// blob those 8 codes are one dword of the row's 16-byte granule, so a
-// wave-wide load of 16 granules (256 contiguous bytes) covers the fragment.
+// The K loop runs in steps of 128 = 4 MFMA sub-steps of 32.  Within a step
+// the k index is permuted so that a lane's weights come from one 16-byte
+// granule: lane l (column n0 + l%16, group q = l/16) supplies, in sub-step s,
+// the 8 K-elements 32q + 8s .. +8 of the step -- word s of granule
+// (step*4 + q, n).  The A operand uses the same permutation (it is read from
+// LDS at k = 32q + 8s), so the product is unchanged and one 16-byte load per
+// lane covers a column tile for the whole step.
+
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __attribute__((address_space(1))) uint4 g128_t;
+typedef __attribute__((address_space(1))) uint2 g64_t;
+typedef __attribute__((address_space(1))) uint16_t g16_t;
+__device__ __forceinline__ uint4 gl16(const uint8_t* p) { return *(const g128_t*)(uintptr_t)p; }
+__device__ __forceinline__ uint2 gl8(const uint8_t* p) { return *(const g64_t*)(uintptr_t)p; }
+__device__ __forceinline__ uint32_t gl2(const uint8_t* p) { return *(const g16_t*)(uintptr_t)p; }
+#else
+__device__ uint4 gl16(const uint8_t* p);
+__device__ uint2 gl8(const uint8_t* p);
+__device__ uint32_t gl2(const uint8_t* p);
+#endif
 
 struct FragNvfp4 {
-  uint32_t code;   // 8 E2M1 codes
-  uint32_t scale;  // E4M3 scale byte of this lane's 16-block (low byte)
+  uint4 code;      // 32 E2M1 codes: word s = sub-step s
+  uint32_t scale;  // the two E4M3 block scales of the granule (low 16 bits)
 };
 
 __device__ __forceinline__ void load_frag(FragNvfp4& f, const uint8_t* q, const uint8_t* sc, int N,
-                                          int n, int k32) {
-  const int lane = threadIdx.x & 63;
-  f.code = *(const __attribute__((address_space(1))) uint32_t*)(uintptr_t)(
-      q + ((size_t)(k32 >> 5) * N + n) * 16 + 4 * (lane >> 4));
-  const int blk = ((k32 & 127) >> 4) + (lane >> 5);  // 16-block within the 128-group
-  f.scale = *(const __attribute__((address_space(1))) uint8_t*)(uintptr_t)(
-      sc + ((size_t)(k32 >> 7) * N + n) * 8 + blk);
+                                          int n, int step) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  f.code = gl16(q + ((size_t)(4 * step + grp) * N + n) * 16);
+  f.scale = gl2(sc + ((size_t)step * N + n) * 8 + 2 * grp);
 }
 
+// Sub-step s: 8 exact bf16 values (E2M1 x E4M3 has at most 6 significant bits).
+template <int S>
 __device__ __forceinline__ v8bf_t dequant_frag(const FragNvfp4& f) {
-  const float s = e4m3x2<false>(f.scale).x;
-  float w[8];
-  e2m1x8_f32(f.code, w);
+  const float s = e4m3x2<false>(f.scale)[S >> 1];  // block 0 for words 0, 1; block 1 for 2, 3
+  const uint32_t w = S == 0 ? f.code.x : S == 1 ? f.code.y : S == 2 ? f.code.z : f.code.w;
+  float v[8];
+  e2m1x8_f32(w, v);
   v8bf_t r;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const v2bf_t b = to_v2bf(w[2 * p] * s, w[2 * p + 1] * s);
+    const v2bf_t b = to_v2bf(v[2 * p] * s, v[2 * p + 1] * s);
     r[2 * p] = b[0];
     r[2 * p + 1] = b[1];
   }
@@ -101,35 +119,34 @@ __device__ __forceinline__ v8bf_t dequant_frag(const FragNvfp4& f) {
 }
 
 struct FragQ6k {
-  uint32_t lo;    // 8 low nibbles
-  uint32_t hi;    // 8 x 2 high bits (low 16 bits)
-  uint32_t sc;    // int8 sub-scale (low byte)
-  uint32_t d;     // fp16 superblock scale
+  uint4 lo;     // 32 low nibbles: word s = sub-step s
+  uint2 hi;     // 32 x 2 high bits: 16 bits per sub-step
+  uint32_t sc;  // the two int8 sub-scales of the granule (low 16 bits)
+  uint32_t d;   // fp16 superblock scale
 };
 
 __device__ __forceinline__ void load_frag_q6k(FragQ6k& f, const uint8_t* ql, const uint8_t* qh,
                                               const uint8_t* sc, const uint8_t* dd, int N, int n,
-                                              int k32) {
-  typedef __attribute__((address_space(1))) uint32_t g32;
-  typedef __attribute__((address_space(1))) uint16_t g16;
-  typedef __attribute__((address_space(1))) uint8_t g8;
-  const int lane = threadIdx.x & 63;
-  const int c = k32 >> 5, sb = k32 >> 8;
-  f.lo = *(const g32*)(uintptr_t)(ql + ((size_t)c * N + n) * 16 + 4 * (lane >> 4));
-  f.hi = *(const g16*)(uintptr_t)(qh + ((size_t)(c >> 1) * N + n) * 16 + 8 * (c & 1) + 2 * (lane >> 4));
-  f.sc = *(const g8*)(uintptr_t)(sc + ((size_t)sb * N + n) * 16 + 2 * (c & 7) + (lane >> 5));
-  f.d = *(const g16*)(uintptr_t)(dd + ((size_t)sb * N + n) * 2);
+                                              int step) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  const int c = 4 * step + grp, sb = c >> 3;
+  f.lo = gl16(ql + ((size_t)c * N + n) * 16);
+  f.hi = gl8(qh + ((size_t)(c >> 1) * N + n) * 16 + 8 * (c & 1));
+  f.sc = gl2(sc + ((size_t)sb * N + n) * 16 + 2 * (c & 7));
+  f.d = gl2(dd + ((size_t)sb * N + n) * 2);
 }
 
+template <int S>
 __device__ __forceinline__ v8bf_t dequant_frag_q6k(const FragQ6k& f) {
-  const float s = f16_to_f32((uint16_t)f.d) * (float)(int8_t)(f.sc & 0xffu);
+  const float s = f16_to_f32((uint16_t)f.d) * (float)(int8_t)((f.sc >> (8 * (S >> 1))) & 0xffu);
+  const uint32_t lo = S == 0 ? f.lo.x : S == 1 ? f.lo.y : S == 2 ? f.lo.z : f.lo.w;
+  const uint32_t h16 = ((S < 2 ? f.hi.x : f.hi.y) >> (16 * (S & 1))) & 0xffffu;
   v8bf_t r;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const uint32_t byte = (f.lo >> (8 * p)) & 0xffu;
-    const uint32_t hb = (f.hi >> (4 * p)) & 0xfu;
-    const int q0 = (int)((byte & 15u) | ((hb & 3u) << 4));
-    const int q1 = (int)((byte >> 4) | ((hb >> 2) << 4));
+    const uint32_t byte = (lo >> (8 * p)) & 0xffu;
+    const int q0 = (int)((byte & 15u) | (((h16 >> (4 * p)) & 3u) << 4));
+    const int q1 = (int)((byte >> 4) | (((h16 >> (4 * p + 2)) & 3u) << 4));
     const v2bf_t b = to_v2bf((float)(q0 - 32) * s, (float)(q1 - 32) * s);
     r[2 * p] = b[0];
     r[2 * p + 1] = b[1];
@@ -139,92 +156,118 @@ __device__ __forceinline__ v8bf_t dequant_frag_q6k(const FragQ6k& f) {
 
 // ---------------------------------------------------------------- main loop
 // WG = 4 waves; tile = 128 rows x 4*NC*16 columns; wave w owns all 128 rows
-// and column tiles cols(w, j), j < NC.  A (bf16 rows) is double-buffered in
-// LDS with one barrier per K step of 64; B fragments go global -> registers,
-// prefetched one K step ahead and dequantized right before their MFMAs.
-constexpr int GBM = 128, GBK = 64, GLDA = GBK + 8;
+// and column tiles cols(w, j), j < NC.  K runs in steps of 128.
+//   - A (bf16 rows) lives in LDS as 256-byte rows whose 16-byte chunks are
+//     XOR-swizzled (chunk c of row r at position c ^ (r & 15)), so the
+//     fragment reads (16 rows, one chunk) hit distinct banks.  The load unit
+//     copies it global -> LDS itself (global_load_lds_dwordx4: lane i of a
+//     wave writes LDS slot i, so lane i fetches the chunk that belongs in
+//     slot i); two buffers, loads one step ahead, and before the barrier the
+//     wave waits until only the step's weight loads are still in flight.
+//   - B fragments go global -> registers, one step ahead, and are
+//     dequantized right before their MFMAs.
+constexpr int GBM = 128, GBK = 128;
+constexpr int ARB = GBK;  // bf16 per LDS row (no padding: swizzled)
+
+__device__ __forceinline__ int aswz(int r, int c) { return r * ARB + 8 * (c ^ (r & 15)); }
 
 // GU: column tiles j < NC/2 read planes (p0, p1) and the rest (p2, p3) --
 // the gate and up matrices of one expert; otherwise (p0..p3) are the planes of
 // one matrix (NVFP4 codes, scales; Q6_K ql, qh, sc, d).
 struct ARows {
-  const uint16_t* r[4];  // this thread's 4 A rows (passed by value: no scratch)
+  const uint16_t* base;  // x or h
+  uint32_t off[8];       // element offsets of rows 32w + 4k + lane/16 (k < 8)
 };
 
+// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int FMT, int NC, bool GU, typename ColFn>
-__device__ __forceinline__ void gemm_main(ARows arow, int K, int N,
+__device__ __forceinline__ void gemm_main(const ARows& arow, int K, int N,
                                           const uint8_t* p0, const uint8_t* p1, const uint8_t* p2,
                                           const uint8_t* p3, ColFn col_of, uint16_t* As,
                                           v4f_t (*acc)[NC]) {
   typedef typename std::conditional<FMT == MOE_FMT_NVFP4, FragNvfp4, FragQ6k>::type Frag;
+  constexpr int kBLoads = NC * ((FMT == MOE_FMT_NVFP4) ? 2 : 4);  // weight loads per step
   const int tid = threadIdx.x, lane = tid & 63;
-  const int ar = tid >> 3, ac = tid & 7;  // A loader: rows ar + 32*j, 16-byte chunk ac
-  uint4 a0, a1, a2, a3;  // named (not an array) so they stay in registers
-  Frag bnext[2][NC];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  Frag bnext[NC];
 
-  auto load_a = [&](int k0) {
-    a0 = *reinterpret_cast<const uint4*>(arow.r[0] + k0 + 8 * ac);
-    a1 = *reinterpret_cast<const uint4*>(arow.r[1] + k0 + 8 * ac);
-    a2 = *reinterpret_cast<const uint4*>(arow.r[2] + k0 + 8 * ac);
-    a3 = *reinterpret_cast<const uint4*>(arow.r[3] + k0 + 8 * ac);
-  };
-  auto store_a = [&](int buf) {
-    uint16_t* d = As + buf * GBM * GLDA + ar * GLDA + 8 * ac;
-    *reinterpret_cast<uint4*>(d) = a0;
-    *reinterpret_cast<uint4*>(d + 32 * GLDA) = a1;
-    *reinterpret_cast<uint4*>(d + 64 * GLDA) = a2;
-    *reinterpret_cast<uint4*>(d + 96 * GLDA) = a3;
-  };
-  auto load_b = [&](int k0) {
+  // Rows 32w + 4k + lane/16, slot lane%16 of row r holds chunk (lane%16) ^ (r & 15).
+  auto load_a = [&](int k0, int buf) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int k = 0; k < 8; ++k) {
+      const int r = 32 * wave + 4 * k + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      const uint16_t* src = arow.base + arow.off[k] + k0 + 8 * c;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src,
+          (void __attribute__((address_space(3)))*)(As + buf * GBM * ARB + (32 * wave + 4 * k) * ARB),
+          16, 0, 0);
+    }
+  };
+  auto load_b = [&](int step) {
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int n = col_of(j) + (lane & 15);
-        if constexpr (GU) {
-          if (j < NC / 2) load_frag(bnext[s][j], p0, p1, N, n, k0 + 32 * s);
-          else load_frag(bnext[s][j], p2, p3, N, n, k0 + 32 * s);
-        } else if constexpr (FMT == MOE_FMT_NVFP4) {
-          load_frag(bnext[s][j], p0, p1, N, n, k0 + 32 * s);
-        } else {
-          load_frag_q6k(bnext[s][j], p0, p1, p2, p3, N, n, k0 + 32 * s);
-        }
+    for (int j = 0; j < NC; ++j) {
+      const int n = col_of(j) + (lane & 15);
+      if constexpr (GU) {
+        if (j < NC / 2) load_frag(bnext[j], p0, p1, N, n, step);
+        else load_frag(bnext[j], p2, p3, N, n, step);
+      } else if constexpr (FMT == MOE_FMT_NVFP4) {
+        load_frag(bnext[j], p0, p1, N, n, step);
+      } else {
+        load_frag_q6k(bnext[j], p0, p1, p2, p3, N, n, step);
       }
+    }
   };
 
-  load_a(0);
+  load_a(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   load_b(0);
-  store_a(0);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<kBLoads>();  // step 0's rows are in LDS (its weight loads may still fly)
   __syncthreads();
   const int nsteps = K / GBK;
+  const int r = lane & 15, cq = 4 * (lane >> 4);
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
-    // Dequantize this step's B fragments, then prefetch the next step.
-    v8bf_t bf[2][NC];
+    Frag bcur[NC];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int j = 0; j < NC; ++j) bcur[j] = bnext[j];
+    const bool more = st + 1 < nsteps;
+    if (more) {
+      load_a((st + 1) * GBK, buf ^ 1);  // the buffer step st-1 read
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(st + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const uint16_t* Ab = As + buf * GBM * ARB;
+    auto sub = [&](auto S_) {
+      constexpr int S = decltype(S_)::value;
+      v8bf_t bf[NC];
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
-        if constexpr (FMT == MOE_FMT_NVFP4) bf[s][j] = dequant_frag(bnext[s][j]);
-        else bf[s][j] = dequant_frag_q6k(bnext[s][j]);
+        if constexpr (FMT == MOE_FMT_NVFP4) bf[j] = dequant_frag<S>(bcur[j]);
+        else bf[j] = dequant_frag_q6k<S>(bcur[j]);
       }
-    if (st + 1 < nsteps) {
-      load_a((st + 1) * GBK);
-      load_b((st + 1) * GBK);
-    }
-    const uint16_t* Ab = As + buf * GBM * GLDA;
-    const int r = lane & 15, kq = (lane >> 4) * 8;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const v8bf_t af = *reinterpret_cast<const v8bf_t*>(Ab + (16 * i + r) * GLDA + 32 * s + kq);
+        const v8bf_t af = *reinterpret_cast<const v8bf_t*>(Ab + aswz(16 * i + r, cq + S));
 #pragma unroll
         for (int j = 0; j < NC; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[s][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
       }
-    }
-    if (st + 1 < nsteps) store_a(buf ^ 1);
+    };
+    sub(std::integral_constant<int, 0>{});
+    sub(std::integral_constant<int, 1>{});
+    sub(std::integral_constant<int, 2>{});
+    sub(std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) wait_vmcnt<kBLoads>();  // step st+1's rows are in LDS
     __syncthreads();
   }
 }
@@ -240,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_gateup_nvfp4(
     size_t off_us, const int32_t* __restrict__ offsets, const uint32_t* __restrict__ counts,
     const int32_t* __restrict__ sorted_asg, const int2* __restrict__ tiles,
     const int* __restrict__ n_tiles, int grid_tiles, uint16_t* __restrict__ hout) {
-  __shared__ __align__(16) uint16_t As[2 * GBM * GLDA];
+  __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
   const int NT = I / 128;
   const int L = logical_tile(grid_tiles);
   const int mtile = L / NT, ntile = L - mtile * NT;
@@ -255,10 +298,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_gateup_nvfp4(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
   ARows arow;
+  arow.base = x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = m0 + (tid >> 3) + 32 * j;  // rows past m_e read a valid row, never stored
-    arow.r[j] = x + (size_t)(sorted_asg[base + (row < m_e ? row : 0)] / ktop) * H;
+  for (int k = 0; k < 8; ++k) {  // rows past m_e read a valid row, never stored
+    const int row = m0 + 32 * (tid >> 6) + 4 * k + ((tid & 63) >> 4);
+    arow.off[k] = (uint32_t)(sorted_asg[base + (row < m_e ? row : 0)] / ktop) * (uint32_t)H;
   }
   v4f_t acc[8][4];  // column tiles 0, 1: gate; 2, 3: the same columns of up
 #pragma unroll
@@ -298,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_down(
     size_t off_a, size_t off_b, size_t off_c, size_t off_d, const int32_t* __restrict__ offsets,
     const uint32_t* __restrict__ counts, const int2* __restrict__ tiles,
     const int* __restrict__ n_tiles, int grid_tiles, void* __restrict__ y) {
-  __shared__ __align__(16) uint16_t As[2 * GBM * GLDA];
+  __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
   const int NT = H / 256;
   const int L = logical_tile(grid_tiles);
   const int mtile = L / NT, ntile = L - mtile * NT;
@@ -313,10 +357,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_down(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
   ARows arow;
+  arow.base = h;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = m0 + (tid >> 3) + 32 * j;
-    arow.r[j] = h + (size_t)(base + (row < m_e ? row : 0)) * I;
+  for (int k = 0; k < 8; ++k) {
+    const int row = m0 + 32 * (tid >> 6) + 4 * k + ((tid & 63) >> 4);
+    arow.off[k] = (uint32_t)(base + (row < m_e ? row : 0)) * (uint32_t)I;
   }
   v4f_t acc[8][4];
 #pragma unroll
