@@ -37,7 +37,7 @@ typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128;       // token rows per tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512; // 8 waves
 
 // Tile list: entry i = (expert, first row of the block); built from counts.
 __global__ __launch_bounds__(1024) void k_build_tiles(const uint32_t* __restrict__ counts,
@@ -155,8 +155,10 @@ __device__ __forceinline__ v8bf_t dequant_frag_q6k(const FragQ6k& f) {
 }
 
 // ---------------------------------------------------------------- main loop
-// WG = 4 waves; tile = 128 rows x 4*NC*16 columns; wave w owns all 128 rows
-// and column tiles cols(w, j), j < NC.  K runs in steps of 128.
+// WG = 8 waves; tile = 128 rows x 8*NC*16 columns; wave w owns all 128 rows
+// and column tiles cols(w, j), j < NC (NC = 2: 64 accumulators per lane, so
+// four waves fit per SIMD and hide each other's LDS and barrier waits).  K
+// runs in steps of 128.
 //   - A (bf16 rows) lives in LDS as 256-byte rows whose 16-byte chunks are
 //     XOR-swizzled (chunk c of row r at position c ^ (r & 15)), so the
 //     fragment reads (16 rows, one chunk) hit distinct banks.  The load unit
@@ -176,7 +178,7 @@ __device__ __forceinline__ int aswz(int r, int c) { return r * ARB + 8 * (c ^ (r
 // one matrix (NVFP4 codes, scales; Q6_K ql, qh, sc, d).
 struct ARows {
   const uint16_t* base;  // x or h
-  uint32_t off[8];       // element offsets of rows 32w + 4k + lane/16 (k < 8)
+  uint32_t off[4];       // element offsets of rows 16w + 4k + lane/16 (k < 4, w < 8)
 };
 
 // s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt not waited on).
@@ -197,16 +199,16 @@ __device__ __forceinline__ void gemm_main(const ARows& arow, int K, int N,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   Frag bnext[NC];
 
-  // Rows 32w + 4k + lane/16, slot lane%16 of row r holds chunk (lane%16) ^ (r & 15).
+  // Rows 16w + 4k + lane/16, slot lane%16 of row r holds chunk (lane%16) ^ (r & 15).
   auto load_a = [&](int k0, int buf) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = 32 * wave + 4 * k + (lane >> 4);
+    for (int k = 0; k < 4; ++k) {
+      const int r = 16 * wave + 4 * k + (lane >> 4);
       const int c = (lane & 15) ^ (r & 15);
       const uint16_t* src = arow.base + arow.off[k] + k0 + 8 * c;
       __builtin_amdgcn_global_load_lds(
           (const void*)src,
-          (void __attribute__((address_space(3)))*)(As + buf * GBM * ARB + (32 * wave + 4 * k) * ARB),
+          (void __attribute__((address_space(3)))*)(As + buf * GBM * ARB + (16 * wave + 4 * k) * ARB),
           16, 0, 0);
     }
   };
@@ -300,33 +302,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_gateup_nvfp4(
   ARows arow;
   arow.base = x;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {  // rows past m_e read a valid row, never stored
-    const int row = m0 + 32 * (tid >> 6) + 4 * k + ((tid & 63) >> 4);
+  for (int k = 0; k < 4; ++k) {  // rows past m_e read a valid row, never stored
+    const int row = m0 + 16 * (tid >> 6) + 4 * k + ((tid & 63) >> 4);
     arow.off[k] = (uint32_t)(sorted_asg[base + (row < m_e ? row : 0)] / ktop) * (uint32_t)H;
   }
-  v4f_t acc[8][4];  // column tiles 0, 1: gate; 2, 3: the same columns of up
+  v4f_t acc[8][2];  // column tile 0: gate rows cb..; 1: the same rows of up
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int cb = n0 + 32 * wave;
-  gemm_main<MOE_FMT_NVFP4, 4, true>(arow, H, I, blob + off_gq, blob + off_gs, blob + off_uq,
-                                    blob + off_us, [&](int j) { return cb + 16 * (j & 1); }, As,
-                                    acc);
+    for (int j = 0; j < 2; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int cb = n0 + 16 * wave;
+  gemm_main<MOE_FMT_NVFP4, 2, true>(arow, H, I, blob + off_gq, blob + off_gs, blob + off_uq,
+                                    blob + off_us, [&](int) { return cb; }, As, acc);
 
   const float tg = ref.ts_gate, tu = ref.ts_up;
+  const int col = cb + (lane & 15);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = cb + 16 * j + (lane & 15);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = m0 + 16 * i + 4 * (lane >> 4) + q;
-        if (row < m_e) {
-          const float g = acc[i][j][q] * tg, u = acc[i][j + 2][q] * tu;
-          hout[(size_t)(base + row) * I + col] = f32_to_bf16_rne(g / (1.0f + expf(-g)) * u);
-        }
+    for (int q = 0; q < 4; ++q) {
+      const int row = m0 + 16 * i + 4 * (lane >> 4) + q;
+      if (row < m_e) {
+        const float g = acc[i][0][q] * tg, u = acc[i][1][q] * tu;
+        hout[(size_t)(base + row) * I + col] = f32_to_bf16_rne(g / (1.0f + expf(-g)) * u);
       }
     }
   }
@@ -359,24 +357,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_down(
   ARows arow;
   arow.base = h;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int row = m0 + 32 * (tid >> 6) + 4 * k + ((tid & 63) >> 4);
+  for (int k = 0; k < 4; ++k) {
+    const int row = m0 + 16 * (tid >> 6) + 4 * k + ((tid & 63) >> 4);
     arow.off[k] = (uint32_t)(base + (row < m_e ? row : 0)) * (uint32_t)I;
   }
-  v4f_t acc[8][4];
+  v4f_t acc[8][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int cb = n0 + 64 * wave;
-  gemm_main<FMT, 4, false>(arow, I, H, blob + off_a, blob + off_b, blob + off_c, blob + off_d,
+    for (int j = 0; j < 2; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int cb = n0 + 32 * wave;
+  gemm_main<FMT, 2, false>(arow, I, H, blob + off_a, blob + off_b, blob + off_c, blob + off_d,
                     [&](int j) { return cb + 16 * j; }, As, acc);
 
   const float ts = (FMT == MOE_FMT_NVFP4) ? ref.ts_down : 1.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int col = cb + 16 * j + (lane & 15);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
