@@ -80,7 +80,10 @@ int moe_abi_version(void);
  *   MOE_FFN_AUTO -- dequant-fused GEMV for decode-sized batches, MFMA grouped
  *                   GEMM once experts average >= 16 tokens (default);
  *   MOE_FFN_GEMV / MOE_FFN_GEMM -- force one family (any size; results agree
- *                   within the stated tolerance).
+ *                   within the stated tolerance).  The grouped GEMM needs
+ *                   H % 256 == 0, T*H < 2^32 and T*k*I < 2^32; AUTO uses the
+ *                   GEMV otherwise, and a forced GEMM call fails with
+ *                   MOE_ERR_UNSUPPORTED.
  * Returns MOE_ERR_INVALID_ARG for any other value. */
 #define MOE_FFN_AUTO 0
 #define MOE_FFN_GEMV 1
@@ -217,7 +220,9 @@ moe_status moe_bucket(const moe_layer_desc* L, const int32_t* topk_idx, int64_t 
  *     y[p] = h . dq(Wd_e)^T,  silu(z) = z / (1 + exp(-z)),
  *   accumulated in fp32.  y: [T*k][H] of y_dtype (MOE_DTYPE_F32 or _BF16),
  *   rows in sorted order.  Decode-sized batches run as dequant-fused GEMV;
- *   larger ones as an MFMA grouped GEMM over experts.
+ *   larger ones as an MFMA grouped GEMM over experts, which multiplies an
+ *   fp16 copy of x scaled per token row by a power of two (exact for every
+ *   value above 2^-29 of the row's largest magnitude).
  * ws: at least moe_workspace_bytes(L, T) bytes. */
 moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                           const moe_buckets* b, void* y, int32_t y_dtype, void* ws,

@@ -81,20 +81,38 @@ moe_status check_T(int64_t T, int k, const char* where) {
   return MOE_OK;
 }
 
-size_t ffn_ws(const moe_layer_desc* L, int64_t T) {
-  size_t A = (size_t)T * L->k;
-  // h (fp32 for the GEMV path, bf16 for the grouped GEMM) + the GEMM tile list
-  return moe::align_up(A * (size_t)L->I * sizeof(float)) + moe::gemm_tiles_bytes(L->E, (int64_t)A);
+// Workspace of moe_expert_ffn: h (bf16 [T*k][I], both paths), then for the
+// grouped GEMM an fp16 copy of x ([T][H]), its row scales ([T]) and the tile list.
+struct FfnWs {
+  size_t h, xh, xscale, tiles, total;
+};
+FfnWs ffn_ws_layout(const moe_layer_desc* L, int64_t T) {
+  const size_t A = (size_t)T * L->k;
+  FfnWs w;
+  w.h = 0;
+  w.xh = moe::align_up(A * (size_t)L->I * sizeof(uint16_t));
+  w.xscale = w.xh + moe::align_up((size_t)T * L->H * sizeof(uint16_t));
+  w.tiles = w.xscale + moe::align_up((size_t)T * sizeof(float));
+  w.total = w.tiles + moe::gemm_tiles_bytes(L->E, (int64_t)A);
+  return w;
 }
+size_t ffn_ws(const moe_layer_desc* L, int64_t T) { return ffn_ws_layout(L, T).total; }
 
 int g_ffn_mode = MOE_FFN_AUTO;
+
+// The grouped GEMM needs 256-column down tiles and 32-bit element offsets
+// of the token rows (x: T*H values) and of h (T*k*I values).
+bool gemm_fits(const moe_layer_desc* L, int64_t T) {
+  return L->H % 256 == 0 && (uint64_t)T * (uint64_t)L->H <= UINT32_MAX &&
+         (uint64_t)T * (uint64_t)L->k * (uint64_t)L->I <= UINT32_MAX;
+}
 
 // Grouped GEMM once experts average >= 16 tokens (and the batch is not a
 // decode step); dequant-fused GEMV otherwise.
 bool use_gemm(const moe_layer_desc* L, int64_t T) {
   if (g_ffn_mode == MOE_FFN_GEMV) return false;
   if (g_ffn_mode == MOE_FFN_GEMM) return true;
-  return T > 64 && T * L->k >= 16 * (int64_t)L->E;
+  return T > 64 && T * L->k >= 16 * (int64_t)L->E && gemm_fits(L, T);
 }
 
 }  // namespace
@@ -251,9 +269,14 @@ moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   size_t need = ffn_ws(L, T);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
   if (use_gemm(L, T)) {
-    const size_t hbytes = moe::align_up((size_t)T * L->k * (size_t)L->I * sizeof(float));
-    return hip_status(W, moe::launch_gemm_ffn(L, x, T, b, (uint16_t*)ws, (char*)ws + hbytes, y,
-                                               y_dtype, stream));
+    if (!gemm_fits(L, T))
+      return fail(MOE_ERR_UNSUPPORTED, "%s: grouped GEMM needs H %% 256 == 0, T*H and T*k*I < 2^32",
+                  W);
+    const FfnWs w = ffn_ws_layout(L, T);
+    char* c = (char*)ws;
+    return hip_status(W, moe::launch_gemm_ffn(L, x, T, b, (uint16_t*)(c + w.h),
+                                               (uint16_t*)(c + w.xh), (float*)(c + w.xscale),
+                                               c + w.tiles, y, y_dtype, stream));
   }
   // Worst-case number of active experts; workgroups past n_active exit.
   const int max_slots = (int)((T * L->k < L->E) ? T * L->k : L->E);

@@ -34,6 +34,8 @@ namespace moe {
 namespace {
 
 typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128;       // token rows per tile
@@ -60,11 +62,85 @@ __global__ __launch_bounds__(1024) void k_build_tiles(const uint32_t* __restrict
   if (e == 1023) *n_tiles = pre[1023];
 }
 
-// Logical tile of this workgroup with an XCD-major layout of the grid.
-__device__ __forceinline__ int logical_tile(int total) {
-  const int w = blockIdx.x;
-  const int per = total / 8;  // total is a multiple of 8
-  return (w & 7) * per + (w >> 3);
+// fp16 copy of the token rows for the gate/up GEMM, one wave per row.  Each
+// row is scaled by 2^-e, e chosen so that its largest magnitude lands in
+// [2^14, 2^15): every value above 2^-29 of the row maximum converts exactly
+// (bf16 carries 8 significant bits, fp16 11) and nothing can overflow.
+// xscale[t] = 2^e scales the row's products back in the epilogue.  Rows that
+// hold an inf or NaN keep e = 0 and carry it through as the bf16 path would.
+__global__ __launch_bounds__(256) void k_rows_to_f16(const uint16_t* __restrict__ x, int64_t T,
+                                                     int H, uint16_t* __restrict__ xh,
+                                                     float* __restrict__ xscale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * H);
+  uint4* dst = reinterpret_cast<uint4*>(xh + t * H);
+  const int nch = H / 8;
+  uint32_t mx = 0;  // largest |x| as bf16 magnitude bits (ordered like the values)
+  for (int c = lane; c < nch; c += 64) {
+    const uint4 v = src[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int o = 32; o; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  const int eb = (int)(mx >> 7);  // biased exponent (bf16 and fp32 share it)
+  int e = (mx == 0 || eb == 0xff) ? 0 : eb - 141;  // 2^(eb-127) * 2^-e in [2^14, 2^15)
+  e = e < -126 ? -126 : (e > 126 ? 126 : e);
+  const float down = __uint_as_float((uint32_t)(127 - e) << 23);
+  if (lane == 0) xscale[t] = __uint_as_float((uint32_t)(127 + e) << 23);
+  for (int c = lane; c < nch; c += 64) {
+    const uint4 v = src[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = (_Float16)(__uint_as_float(w[i] << 16) * down);
+      const _Float16 hi = (_Float16)(__uint_as_float(w[i] & 0xffff0000u) * down);
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Row block (tile row) record: the expert and the block's rows in bucket order.
+struct TileRec {
+  moe_expert_ref ref;  // blob and per-tensor scales of the expert
+  int srow;            // first row of the block in bucket (sorted) order
+  int nrows;           // valid rows, 1..128
+};
+static_assert(sizeof(TileRec) == 32, "TileRec layout");
+
+// Row tables of the row blocks, one workgroup of 128 threads per block:
+// record, token row offset of each row (row r -> token * H; rows past the
+// block's end repeat row 0, read but never stored) and that token's fp16 row
+// scale.
+__global__ __launch_bounds__(128) void k_tile_rows(
+    const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
+    const uint32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const moe_expert_ref* __restrict__ experts, const int32_t* __restrict__ sorted_asg, int ktop,
+    int H, const float* __restrict__ xscale, TileRec* __restrict__ recs,
+    uint32_t* __restrict__ toff, float* __restrict__ rsc) {
+  const int mt = blockIdx.x;
+  if (mt >= *n_tiles) return;
+  const int2 te = tiles[mt];
+  const int e = te.x, m0 = te.y;
+  const int nrows = min((int)counts[e] - m0, 128);
+  const int srow = offsets[e] + m0;
+  const int r = threadIdx.x;
+  const int tok = sorted_asg[srow + (r < nrows ? r : 0)] / ktop;
+  toff[(size_t)mt * 128 + r] = (uint32_t)tok * (uint32_t)H;
+  rsc[(size_t)mt * 128 + r] = xscale[tok];
+  if (r == 0) {
+    TileRec t;
+    t.ref = experts[e];
+    t.srow = srow;
+    t.nrows = nrows;
+    recs[mt] = t;
+  }
 }
 
 // ---------------------------------------------------------------- B fragments
@@ -118,6 +194,22 @@ __device__ __forceinline__ v8bf_t dequant_frag(const FragNvfp4& f) {
   return r;
 }
 
+// The same 8 values as fp16 -- also exact (E2M1 x E4M3 lies in [2^-10, 2688]
+// with at most 5 significant bits): the codes convert to fp16 pairs and one
+// packed fp16 multiply applies the block scale, 2 VALU per pair instead of 4.
+template <int S>
+__device__ __forceinline__ v8h_t dequant_frag_h(const FragNvfp4& f) {
+  const v2h_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.scale, 1.0f, false);
+  const _Float16 sc = s2[S >> 1];
+  const v2h_t ss = {sc, sc};
+  const uint32_t w = S == 0 ? f.code.x : S == 1 ? f.code.y : S == 2 ? f.code.z : f.code.w;
+  const v2h_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const v2h_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const v2h_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const v2h_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  return v8h_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 struct FragQ6k {
   uint4 lo;     // 32 low nibbles: word s = sub-step s
   uint2 hi;     // 32 x 2 high bits: 16 bits per sub-step
@@ -155,31 +247,29 @@ __device__ __forceinline__ v8bf_t dequant_frag_q6k(const FragQ6k& f) {
 }
 
 // ---------------------------------------------------------------- main loop
-// WG = 8 waves; tile = 128 rows x 8*NC*16 columns; wave w owns all 128 rows
-// and column tiles cols(w, j), j < NC (NC = 2: 64 accumulators per lane, so
-// four waves fit per SIMD and hide each other's LDS and barrier waits).  K
-// runs in steps of 128.
-//   - A (bf16 rows) lives in LDS as 256-byte rows whose 16-byte chunks are
-//     XOR-swizzled (chunk c of row r at position c ^ (r & 15)), so the
+// Persistent workgroups of 8 waves.  A tile is 128 token rows x 8*NC*16
+// columns; wave w owns all 128 rows and column tiles j < NC (NC = 2: 64
+// accumulators per lane, 4 waves per SIMD).  K runs in steps of 128.
+//   - A (token rows, 16-bit) lives in LDS as 256-byte rows whose 16-byte
+//     chunks are XOR-swizzled (chunk c of row r at c ^ (r & 15)), so the
 //     fragment reads (16 rows, one chunk) hit distinct banks.  The load unit
 //     copies it global -> LDS itself (global_load_lds_dwordx4: lane i of a
-//     wave writes LDS slot i, so lane i fetches the chunk that belongs in
-//     slot i); two buffers, loads one step ahead, and before the barrier the
-//     wave waits until only the step's weight loads are still in flight.
-//   - B fragments go global -> registers, one step ahead, and are
-//     dequantized right before their MFMAs.
+//     wave writes LDS slot i); two buffers, loads one step ahead.
+//   - B fragments go global -> registers one step ahead and are dequantized
+//     right before their MFMAs.
+//   - The operands enter the MFMA as (B, A), so the accumulator holds the
+//     transposed tile: lane l has row l%16 and the 4 consecutive columns
+//     4*(l/16) .. +4 of each 16 x 16 block, stored with one 8- or 16-byte
+//     store.
+//   - Each workgroup walks a list of tiles.  The step stream does not stop
+//     at tile boundaries: the last step of a tile already loads step 0 of the
+//     next one, whose row table (token row offsets, row scales) was copied
+//     into LDS during the tile's first step, so no tile waits on a chain of
+//     dependent metadata loads, and the epilogue overlaps the next loads.
 constexpr int GBM = 128, GBK = 128;
-constexpr int ARB = GBK;  // bf16 per LDS row (no padding: swizzled)
+constexpr int ARB = GBK;  // 16-bit values per LDS row (no padding: swizzled)
 
 __device__ __forceinline__ int aswz(int r, int c) { return r * ARB + 8 * (c ^ (r & 15)); }
-
-// GU: column tiles j < NC/2 read planes (p0, p1) and the rest (p2, p3) --
-// the gate and up matrices of one expert; otherwise (p0..p3) are the planes of
-// one matrix (NVFP4 codes, scales; Q6_K ql, qh, sc, d).
-struct ARows {
-  const uint16_t* base;  // x or h
-  uint32_t off[4];       // element offsets of rows 16w + 4k + lane/16 (k < 4, w < 8)
-};
 
 // s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt not waited on).
 template <int N>
@@ -188,68 +278,85 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int FMT, int NC, bool GU, typename ColFn>
-__device__ __forceinline__ void gemm_main(const ARows& arow, int K, int N,
-                                          const uint8_t* p0, const uint8_t* p1, const uint8_t* p2,
-                                          const uint8_t* p3, ColFn col_of, uint16_t* As,
-                                          v4f_t (*acc)[NC]) {
-  typedef typename std::conditional<FMT == MOE_FMT_NVFP4, FragNvfp4, FragQ6k>::type Frag;
-  constexpr int kBLoads = NC * ((FMT == MOE_FMT_NVFP4) ? 2 : 4);  // weight loads per step
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  Frag bnext[NC];
+// Weight planes of one column tile: NVFP4 (codes, scales) or Q6_K (ql, qh,
+// sc, d) of one matrix.
+struct Planes {
+  const uint8_t* p[4];
+};
 
-  // Rows 16w + 4k + lane/16, slot lane%16 of row r holds chunk (lane%16) ^ (r & 15).
-  auto load_a = [&](int k0, int buf) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = 16 * wave + 4 * k + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 15);
-      const uint16_t* src = arow.base + arow.off[k] + k0 + 8 * c;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src,
-          (void __attribute__((address_space(3)))*)(As + buf * GBM * ARB + (16 * wave + 4 * k) * ARB),
-          16, 0, 0);
-    }
-  };
-  auto load_b = [&](int step) {
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const int n = col_of(j) + (lane & 15);
-      if constexpr (GU) {
-        if (j < NC / 2) load_frag(bnext[j], p0, p1, N, n, step);
-        else load_frag(bnext[j], p2, p3, N, n, step);
-      } else if constexpr (FMT == MOE_FMT_NVFP4) {
-        load_frag(bnext[j], p0, p1, N, n, step);
-      } else {
-        load_frag_q6k(bnext[j], p0, p1, p2, p3, N, n, step);
-      }
-    }
-  };
+template <int FMT>
+using FragOf = typename std::conditional<FMT == MOE_FMT_NVFP4, FragNvfp4, FragQ6k>::type;
 
-  load_a(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_b(0);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<kBLoads>();  // step 0's rows are in LDS (its weight loads may still fly)
-  __syncthreads();
-  const int nsteps = K / GBK;
+template <int FMT>
+__device__ __forceinline__ void load_b_tile(FragOf<FMT>& f, const Planes& P, int N, int n,
+                                            int step) {
+  if constexpr (FMT == MOE_FMT_NVFP4) load_frag(f, P.p[0], P.p[1], N, n, step);
+  else load_frag_q6k(f, P.p[0], P.p[1], P.p[2], P.p[3], N, n, step);
+}
+
+// Rows 16w + 4k + lane/16 (k < 4) of the A tile: slot lane%16 of row r holds
+// chunk (lane%16) ^ (r & 15).  off[k]: element offset of that row's values.
+__device__ __forceinline__ void load_a_tile(const uint16_t* base, const uint32_t (&off)[4], int k0,
+                                            uint16_t* Abuf, int wave, int lane) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 16 * wave + 4 * k + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(base + off[k] + k0 + 8 * c),
+        (void __attribute__((address_space(3)))*)(Abuf + (16 * wave + 4 * k) * ARB), 16, 0, 0);
+  }
+}
+
+// Half h (0, 1) of load_a_tile: rows k = 2h, 2h + 1.
+__device__ __forceinline__ void load_a_half(const uint16_t* base, const uint32_t (&off)[4], int k0,
+                                            uint16_t* Abuf, int wave, int lane, int h) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int k = 2 * h + kk;
+    const int r = 16 * wave + 4 * k + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(base + off[k] + k0 + 8 * c),
+        (void __attribute__((address_space(3)))*)(Abuf + (16 * wave + 4 * k) * ARB), 16, 0, 0);
+  }
+}
+
+// The 4 sub-steps of one K step on A buffer Ab: acc[i][j] += tile i of A x
+// column tile j of B, computed transposed (see above).  issue(S) runs before
+// the MFMAs of sub-step S: the next step's loads are spread over the step, so
+// no wave stalls on a full memory queue right after the barrier.
+template <int FMT, int NC, bool F16, typename Issue>
+__device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const uint16_t* Ab,
+                                          int lane, v4f_t (*acc)[NC], Issue issue) {
   const int r = lane & 15, cq = 4 * (lane >> 4);
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    Frag bcur[NC];
+  auto sub = [&](auto S_) {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (F16) {
+      static_assert(FMT == MOE_FMT_NVFP4, "fp16 operands: NVFP4 weights");
+      v8h_t bf[NC];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) bcur[j] = bnext[j];
-    const bool more = st + 1 < nsteps;
-    if (more) {
-      load_a((st + 1) * GBK, buf ^ 1);  // the buffer step st-1 read
+      for (int j = 0; j < NC; ++j) bf[j] = dequant_frag_h<S>(bcur[j]);
       __builtin_amdgcn_sched_barrier(0);
-      load_b(st + 1);
+      issue(S_);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    const uint16_t* Ab = As + buf * GBM * ARB;
-    auto sub = [&](auto S_) {
-      constexpr int S = decltype(S_)::value;
+      // A fragments are read one row tile ahead of their MFMAs; the fences
+      // keep the compiler from serializing read -> wait -> MFMA under the
+      // 128-register budget of 4 waves per SIMD.
+      v8h_t an = *reinterpret_cast<const v8h_t*>(Ab + aswz(r, cq + S));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const v8h_t af = an;
+        if (i + 1 < 8) an = *reinterpret_cast<const v8h_t*>(Ab + aswz(16 * (i + 1) + r, cq + S));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af, acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      issue(S_);
+      __builtin_amdgcn_sched_barrier(0);
       v8bf_t bf[NC];
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
@@ -261,189 +368,343 @@ __device__ __forceinline__ void gemm_main(const ARows& arow, int K, int N,
         const v8bf_t af = *reinterpret_cast<const v8bf_t*>(Ab + aswz(16 * i + r, cq + S));
 #pragma unroll
         for (int j = 0; j < NC; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, acc[i][j], 0, 0, 0);
       }
-    };
-    sub(std::integral_constant<int, 0>{});
-    sub(std::integral_constant<int, 1>{});
-    sub(std::integral_constant<int, 2>{});
-    sub(std::integral_constant<int, 3>{});
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) wait_vmcnt<kBLoads>();  // step st+1's rows are in LDS
-    __syncthreads();
-  }
+    }
+  };
+  sub(std::integral_constant<int, 0>{});
+  sub(std::integral_constant<int, 1>{});
+  sub(std::integral_constant<int, 2>{});
+  sub(std::integral_constant<int, 3>{});
+}
+
+// Tiles of this workgroup.  Workgroup w runs on XCD w % 8 (all workgroups of
+// the grid are resident, dispatched round robin); each XCD takes a contiguous
+// 1/8 of the logical tiles, in which consecutive tiles are the column tiles of
+// one row block, so those share the XCD's L2 for the row block's A rows.
+struct TileRange {
+  int first, end, stride;
+};
+__device__ __forceinline__ TileRange tile_range(int n_logical) {
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3, per8 = (n_logical + 7) >> 3;
+  TileRange t;
+  t.first = x * per8 + j;
+  t.end = min((x + 1) * per8, n_logical);
+  t.stride = (int)(gridDim.x >> 3);
+  return t;
 }
 
 // ------------------------------------------------------------------ gate/up
 // Tile columns: 128 consecutive rows n0.. of gate and the same rows of up;
-// wave w takes gate columns n0 + 32w .. +32 (tiles j = 0, 1) and the matching
-// up columns (tiles j = 2, 3).
+// wave w takes gate rows n0 + 16w .. +16 (tile j = 0) and the same up rows
+// (tile j = 1), so each lane holds matching g and u values.
 
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_gateup_nvfp4(
-    const uint16_t* __restrict__ x, int H, int I, int ktop,
-    const moe_expert_ref* __restrict__ experts, size_t off_gq, size_t off_gs, size_t off_uq,
-    size_t off_us, const int32_t* __restrict__ offsets, const uint32_t* __restrict__ counts,
-    const int32_t* __restrict__ sorted_asg, const int2* __restrict__ tiles,
-    const int* __restrict__ n_tiles, int grid_tiles, uint16_t* __restrict__ hout) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_gateup_nvfp4(
+    const uint16_t* __restrict__ xh, int H, int I, size_t off_gq, size_t off_gs, size_t off_uq,
+    size_t off_us, const TileRec* __restrict__ recs, const uint32_t* __restrict__ toff,
+    const float* __restrict__ rsc, const int* __restrict__ n_tiles, uint16_t* __restrict__ hout) {
   __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
+  __shared__ uint32_t st_off[3][GBM];  // row tables of up to 3 tiles in flight
+  __shared__ float st_rs[3][GBM];
   const int NT = I / 128;
-  const int L = logical_tile(grid_tiles);
-  const int mtile = L / NT, ntile = L - mtile * NT;
-  if (mtile >= *n_tiles) return;
-  const int2 te = tiles[mtile];
-  const int e = te.x, m0 = te.y;
-  const int m_e = (int)counts[e];
-  const int base = offsets[e];
-  const moe_expert_ref ref = experts[e];
-  const uint8_t* blob = (const uint8_t*)ref.blob;
-  const int n0 = ntile * 128;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const TileRange tr = tile_range(*n_tiles * NT);
+  if (tr.first >= tr.end) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nsteps = H / GBK;
 
-  ARows arow;
-  arow.base = x;
+  // Copy the row table of row block mt into LDS slot s (waves 0-3, async).
+  auto stage_rows = [&](int mt, int s) {
+    if (wave < 4) {
+      const int half = wave & 1;
+      const void* src = (wave < 2) ? (const void*)(toff + (size_t)mt * GBM + 64 * half + lane)
+                                   : (const void*)(rsc + (size_t)mt * GBM + 64 * half + lane);
+      void* dst = (wave < 2) ? (void*)&st_off[s][64 * half] : (void*)&st_rs[s][64 * half];
+      __builtin_amdgcn_global_load_lds(src, (void __attribute__((address_space(3)))*)dst, 4, 0, 0);
+    }
+  };
+  auto read_rows = [&](int s, uint32_t (&off)[4]) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {  // rows past m_e read a valid row, never stored
-    const int row = m0 + 16 * (tid >> 6) + 4 * k + ((tid & 63) >> 4);
-    arow.off[k] = (uint32_t)(sorted_asg[base + (row < m_e ? row : 0)] / ktop) * (uint32_t)H;
-  }
-  v4f_t acc[8][2];  // column tile 0: gate rows cb..; 1: the same rows of up
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int cb = n0 + 16 * wave;
-  gemm_main<MOE_FMT_NVFP4, 2, true>(arow, H, I, blob + off_gq, blob + off_gs, blob + off_uq,
-                                    blob + off_us, [&](int) { return cb; }, As, acc);
+    for (int k = 0; k < 4; ++k) off[k] = st_off[s][16 * wave + 4 * k + (lane >> 4)];
+  };
+  auto planes_of = [&](const uint8_t* blob, Planes (&P)[2]) {
+    P[0].p[0] = blob + off_gq; P[0].p[1] = blob + off_gs;
+    P[1].p[0] = blob + off_uq; P[1].p[1] = blob + off_us;
+  };
 
-  const float tg = ref.ts_gate, tu = ref.ts_up;
-  const int col = cb + (lane & 15);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = m0 + 16 * i + 4 * (lane >> 4) + q;
-      if (row < m_e) {
-        const float g = acc[i][0][q] * tg, u = acc[i][1][q] * tu;
-        hout[(size_t)(base + row) * I + col] = f32_to_bf16_rne(g / (1.0f + expf(-g)) * u);
+  // First tile: row table and step 0 loaded up front.
+  int L = tr.first, slot = 0, buf = 0;
+  const int mt = L / NT;
+  int cb = (L - mt * NT) * 128 + 16 * wave;
+  TileRec cur = recs[mt];
+  Planes P[2];
+  planes_of((const uint8_t*)cur.ref.blob, P);
+  stage_rows(mt, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  uint32_t off[4];
+  read_rows(0, off);
+  FragNvfp4 bnext[2];
+  load_a_tile(xh, off, 0, As, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frag(bnext[0], P[0].p[0], P[0].p[1], I, cb + (lane & 15), 0);
+  load_frag(bnext[1], P[1].p[0], P[1].p[1], I, cb + (lane & 15), 0);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<4>();  // step 0's rows are in LDS (its weight loads may still fly)
+  __syncthreads();
+
+  int cbl = cb;  // column base of the weight loads (switches to the next tile early)
+  for (;;) {
+    const int Ln = L + tr.stride;
+    const bool has_next = Ln < tr.end;
+    const int mtn = Ln / NT, cbn = (Ln - mtn * NT) * 128 + 16 * wave;
+    const int slotn = slot == 2 ? 0 : slot + 1;
+    TileRec nxt = cur;
+    if (has_next) {  // the next tile's record and row table, read in its last step
+      nxt = recs[mtn];
+      stage_rows(mtn, slotn);
+      if (nsteps == 1) {
+        wait_vmcnt<0>();
+        __syncthreads();
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    v4f_t acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int st = 0; st < nsteps; ++st) {
+      FragNvfp4 bcur[2] = {bnext[0], bnext[1]};
+      const bool more = st + 1 < nsteps;
+      if (!more && has_next) {
+        read_rows(slotn, off);
+        planes_of((const uint8_t*)nxt.ref.blob, P);
+        cbl = cbn;
+      }
+      const bool ld = more || has_next;
+      const int stn = more ? st + 1 : 0;
+      uint16_t* Anext = As + (buf ^ 1) * GBM * ARB;
+      // Next step: weights first (they come from farther away), rows after.
+      step_mfma<MOE_FMT_NVFP4, 2, true>(bcur, As + buf * GBM * ARB, lane, acc, [&](auto S_) {
+        constexpr int S = decltype(S_)::value;
+        if (!ld) return;
+        if constexpr (S == 0) {
+          load_frag(bnext[0], P[0].p[0], P[0].p[1], I, cbl + (lane & 15), stn);
+          load_frag(bnext[1], P[1].p[0], P[1].p[1], I, cbl + (lane & 15), stn);
+        } else if constexpr (S == 1) {
+          load_a_half(xh, off, stn * GBK, Anext, wave, lane, 0);
+        } else if constexpr (S == 2) {
+          load_a_half(xh, off, stn * GBK, Anext, wave, lane, 1);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      if (ld) wait_vmcnt<0>();  // the next step's rows are in LDS
+      __syncthreads();
+      buf ^= 1;
+    }
+
+    // SwiGLU epilogue: lane holds row 16i + lane%16, columns cb + 4*(lane/16) .. +4.
+    const float tg = cur.ref.ts_gate, tu = cur.ref.ts_up;
+    const int c0 = cb + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 16 * i + (lane & 15);
+      if (r < cur.nrows) {
+        const float rs = st_rs[slot][r];
+        uint32_t hv[2];
+#pragma unroll
+        for (int q = 0; q < 4; q += 2) {
+          float h2[2];
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const float g = acc[i][0][q + d] * (tg * rs), u = acc[i][1][q + d] * (tu * rs);
+            h2[d] = swiglu(g, u);
+          }
+          hv[q >> 1] = (uint32_t)f32_to_bf16_rne(h2[0]) | ((uint32_t)f32_to_bf16_rne(h2[1]) << 16);
+        }
+        *reinterpret_cast<uint2*>(hout + (size_t)(cur.srow + r) * I + c0) = make_uint2(hv[0], hv[1]);
+      }
+    }
+    if (!has_next) break;
+    L = Ln; cb = cbn; slot = slotn; cur = nxt;
   }
 }
 
 // ------------------------------------------------------------------ down
 // Tile columns: 256 consecutive rows of the down weights (output features);
-// wave w takes columns n0 + 64w .. +64 (4 tiles).
+// wave w takes columns n0 + 32w .. +32 (tiles j = 0, 1).  The A rows are the
+// tile's rows of h, contiguous in bucket order.
 
 template <int FMT, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_down(
-    const uint16_t* __restrict__ h, int H, int I, const moe_expert_ref* __restrict__ experts,
-    size_t off_a, size_t off_b, size_t off_c, size_t off_d, const int32_t* __restrict__ offsets,
-    const uint32_t* __restrict__ counts, const int2* __restrict__ tiles,
-    const int* __restrict__ n_tiles, int grid_tiles, void* __restrict__ y) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_down(
+    const uint16_t* __restrict__ h, int H, int I, size_t off_a, size_t off_b, size_t off_c,
+    size_t off_d, const TileRec* __restrict__ recs, const int* __restrict__ n_tiles,
+    void* __restrict__ y) {
   __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
   const int NT = H / 256;
-  const int L = logical_tile(grid_tiles);
-  const int mtile = L / NT, ntile = L - mtile * NT;
-  if (mtile >= *n_tiles) return;
-  const int2 te = tiles[mtile];
-  const int e = te.x, m0 = te.y;
-  const int m_e = (int)counts[e];
-  const int base = offsets[e];
-  const moe_expert_ref ref = experts[e];
-  const uint8_t* blob = (const uint8_t*)ref.blob;
-  const int n0 = ntile * 256;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const TileRange tr = tile_range(*n_tiles * NT);
+  if (tr.first >= tr.end) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nsteps = I / GBK;
+  constexpr int kB = (FMT == MOE_FMT_NVFP4) ? 2 : 4;  // weight loads per column tile
 
-  ARows arow;
-  arow.base = h;
+  auto rows_of = [&](const TileRec& t, uint32_t (&off)[4]) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int row = m0 + 16 * (tid >> 6) + 4 * k + ((tid & 63) >> 4);
-    arow.off[k] = (uint32_t)(base + (row < m_e ? row : 0)) * (uint32_t)I;
-  }
-  v4f_t acc[8][2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int cb = n0 + 32 * wave;
-  gemm_main<FMT, 2, false>(arow, I, H, blob + off_a, blob + off_b, blob + off_c, blob + off_d,
-                    [&](int j) { return cb + 16 * j; }, As, acc);
+    for (int k = 0; k < 4; ++k) {  // rows past nrows read a valid row, never stored
+      const int r = 16 * wave + 4 * k + (lane >> 4);
+      off[k] = (uint32_t)(t.srow + (r < t.nrows ? r : 0)) * (uint32_t)I;
+    }
+  };
+  auto planes_of = [&](const uint8_t* blob, Planes& P) {
+    P.p[0] = blob + off_a; P.p[1] = blob + off_b; P.p[2] = blob + off_c; P.p[3] = blob + off_d;
+  };
 
-  const float ts = (FMT == MOE_FMT_NVFP4) ? ref.ts_down : 1.0f;
+  int L = tr.first, buf = 0;
+  const int mt = L / NT;
+  int cb = (L - mt * NT) * 256 + 32 * wave;
+  TileRec cur = recs[mt];
+  Planes P;
+  planes_of((const uint8_t*)cur.ref.blob, P);
+  uint32_t off[4];
+  rows_of(cur, off);
+  FragOf<FMT> bnext[2];
+  load_a_tile(h, off, 0, As, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_b_tile<FMT>(bnext[0], P, H, cb + (lane & 15), 0);
+  load_b_tile<FMT>(bnext[1], P, H, cb + 16 + (lane & 15), 0);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<2 * kB>();
+  __syncthreads();
+
+  int cbl = cb;  // column base of the weight loads (switches to the next tile early)
+  for (;;) {
+    const int Ln = L + tr.stride;
+    const bool has_next = Ln < tr.end;
+    const int mtn = Ln / NT, cbn = (Ln - mtn * NT) * 256 + 32 * wave;
+    TileRec nxt = cur;
+    if (has_next) nxt = recs[mtn];
+    v4f_t acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int st = 0; st < nsteps; ++st) {
+      FragOf<FMT> bcur[2] = {bnext[0], bnext[1]};
+      const bool more = st + 1 < nsteps;
+      if (!more && has_next) {
+        rows_of(nxt, off);
+        planes_of((const uint8_t*)nxt.ref.blob, P);
+        cbl = cbn;
+      }
+      const bool ld = more || has_next;
+      const int stn = more ? st + 1 : 0;
+      uint16_t* Anext = As + (buf ^ 1) * GBM * ARB;
+      step_mfma<FMT, 2, false>(bcur, As + buf * GBM * ARB, lane, acc, [&](auto S_) {
+        constexpr int S = decltype(S_)::value;
+        if (!ld) return;
+        if constexpr (S == 0) {
+          load_b_tile<FMT>(bnext[0], P, H, cbl + (lane & 15), stn);
+          load_b_tile<FMT>(bnext[1], P, H, cbl + 16 + (lane & 15), stn);
+          load_a_tile(h, off, stn * GBK, Anext, wave, lane);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      if (ld) wait_vmcnt<0>();
+      __syncthreads();
+      buf ^= 1;
+    }
+
+    // Epilogue: lane holds row 16i + lane%16, columns cb + 16j + 4*(lane/16) .. +4.
+    const float ts = (FMT == MOE_FMT_NVFP4) ? cur.ref.ts_down : 1.0f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = cb + 16 * j + (lane & 15);
+    for (int i = 0; i < 8; ++i) {
+      const int r = 16 * i + (lane & 15);
+      if (r < cur.nrows) {
+        const size_t o = (size_t)(cur.srow + r) * H + cb + 4 * (lane >> 4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = m0 + 16 * i + 4 * (lane >> 4) + q;
-        if (row < m_e) {
-          const float v = acc[i][j][q] * ts;
-          if (OUT_BF16) reinterpret_cast<uint16_t*>(y)[(size_t)(base + row) * H + col] = f32_to_bf16_rne(v);
-          else reinterpret_cast<float*>(y)[(size_t)(base + row) * H + col] = v;
+        for (int j = 0; j < 2; ++j) {
+          const v4f_t v = acc[i][j] * ts;
+          if (OUT_BF16) {
+            const uint32_t a = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+            const uint32_t b = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + o + 16 * j) = make_uint2(a, b);
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + o + 16 * j) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
         }
       }
     }
+    if (!has_next) break;
+    L = Ln; cb = cbn; cur = nxt;
   }
 }
+
+int g_gemm_slots = 0;  // workgroups of a persistent launch: 2 per CU
 
 }  // namespace
 
 size_t gemm_tiles_bytes(int E, int64_t A) {
-  return align_up((size_t)(A / BM + E + 1) * sizeof(int2)) + align_up(sizeof(int));
+  const size_t mt = (size_t)(A / BM + E + 1);
+  return align_up(mt * sizeof(int2)) + align_up(sizeof(int)) + align_up(mt * sizeof(TileRec)) +
+         2 * align_up(mt * GBM * sizeof(uint32_t));
 }
 
-// Grouped-GEMM expert FFN.  ws_h: bf16 [A][I]; ws_tiles: gemm_tiles_bytes().
+// Grouped-GEMM expert FFN.  hbuf: bf16 [A][I]; xh: fp16 [T][H]; xscale: [T];
+// tiles_ws: gemm_tiles_bytes().
 hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
-                           const moe_buckets* b, uint16_t* hbuf, void* tiles_ws, void* y,
-                           int y_dtype, hipStream_t s) {
+                           const moe_buckets* b, uint16_t* hbuf, uint16_t* xh, float* xscale,
+                           void* tiles_ws, void* y, int y_dtype, hipStream_t s) {
   const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
   const int64_t A = T * L->k;
-  int2* tiles = (int2*)tiles_ws;
-  int* n_tiles = (int*)((char*)tiles_ws + align_up((size_t)(A / BM + L->E + 1) * sizeof(int2)));
+  const size_t mtmax = (size_t)(A / BM + L->E + 1);
+  char* w = (char*)tiles_ws;
+  int2* tiles = (int2*)w;
+  w += align_up(mtmax * sizeof(int2));
+  int* n_tiles = (int*)w;
+  w += align_up(sizeof(int));
+  TileRec* recs = (TileRec*)w;
+  w += align_up(mtmax * sizeof(TileRec));
+  uint32_t* toff = (uint32_t*)w;
+  w += align_up(mtmax * GBM * sizeof(uint32_t));
+  float* rsc = (float*)w;
+  if (g_gemm_slots == 0) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_gemm_slots = (2 * cus + 7) / 8 * 8;
+  }
+  const int max_mtiles = (int)(A / BM) + L->E;
   hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, b->counts, L->E, BM, tiles, n_tiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int max_mtiles = (int)(A / BM) + L->E;
-  {
-    const int NT = L->I / 128;
-    int total = max_mtiles * NT;
-    total = (total + 7) / 8 * 8;
-    hipLaunchKernelGGL(k_gemm_gateup_nvfp4, dim3((unsigned)total), dim3(kThreads), 0, s, x, L->H,
-                       L->I, L->k, L->experts, lay.gate_q, lay.gate_s, lay.up_q, lay.up_s,
-                       b->offsets, b->counts, b->sorted_asg, tiles, n_tiles, total, hbuf);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_rows_to_f16, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, T, L->H, xh,
+                     xscale);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_tile_rows, dim3((unsigned)max_mtiles), dim3(GBM), 0, s, tiles, n_tiles,
+                     b->counts, b->offsets, L->experts, b->sorted_asg, L->k, L->H, xscale, recs,
+                     toff, rsc);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const dim3 grid((unsigned)g_gemm_slots), block(kThreads);
+  hipLaunchKernelGGL(k_gemm_gateup_nvfp4, grid, block, 0, s, xh, L->H, L->I, lay.gate_q, lay.gate_s,
+                     lay.up_q, lay.up_s, recs, toff, rsc, n_tiles, hbuf);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const bool bf = (y_dtype == MOE_DTYPE_BF16);
+  if (L->fmt_down == MOE_FMT_NVFP4) {
+    if (bf)
+      hipLaunchKernelGGL((k_gemm_down<MOE_FMT_NVFP4, true>), grid, block, 0, s, hbuf, L->H, L->I,
+                         lay.down_q, lay.down_s, (size_t)0, (size_t)0, recs, n_tiles, y);
+    else
+      hipLaunchKernelGGL((k_gemm_down<MOE_FMT_NVFP4, false>), grid, block, 0, s, hbuf, L->H, L->I,
+                         lay.down_q, lay.down_s, (size_t)0, (size_t)0, recs, n_tiles, y);
+  } else {
+    if (bf)
+      hipLaunchKernelGGL((k_gemm_down<MOE_FMT_Q6K, true>), grid, block, 0, s, hbuf, L->H, L->I,
+                         lay.down_ql, lay.down_qh, lay.down_sc, lay.down_d, recs, n_tiles, y);
+    else
+      hipLaunchKernelGGL((k_gemm_down<MOE_FMT_Q6K, false>), grid, block, 0, s, hbuf, L->H, L->I,
+                         lay.down_ql, lay.down_qh, lay.down_sc, lay.down_d, recs, n_tiles, y);
   }
-  {
-    const int NT = L->H / 256;
-    int total = max_mtiles * NT;
-    total = (total + 7) / 8 * 8;
-    const bool bf = (y_dtype == MOE_DTYPE_BF16);
-    if (L->fmt_down == MOE_FMT_NVFP4) {
-      if (bf)
-        hipLaunchKernelGGL((k_gemm_down<MOE_FMT_NVFP4, true>), dim3((unsigned)total), dim3(kThreads), 0, s,
-                           hbuf, L->H, L->I, L->experts, lay.down_q, lay.down_s, (size_t)0, (size_t)0,
-                           b->offsets, b->counts, tiles, n_tiles, total, y);
-      else
-        hipLaunchKernelGGL((k_gemm_down<MOE_FMT_NVFP4, false>), dim3((unsigned)total), dim3(kThreads), 0, s,
-                           hbuf, L->H, L->I, L->experts, lay.down_q, lay.down_s, (size_t)0, (size_t)0,
-                           b->offsets, b->counts, tiles, n_tiles, total, y);
-    } else {
-      if (bf)
-        hipLaunchKernelGGL((k_gemm_down<MOE_FMT_Q6K, true>), dim3((unsigned)total), dim3(kThreads), 0, s,
-                           hbuf, L->H, L->I, L->experts, lay.down_ql, lay.down_qh, lay.down_sc,
-                           lay.down_d, b->offsets, b->counts, tiles, n_tiles, total, y);
-      else
-        hipLaunchKernelGGL((k_gemm_down<MOE_FMT_Q6K, false>), dim3((unsigned)total), dim3(kThreads), 0, s,
-                           hbuf, L->H, L->I, L->experts, lay.down_ql, lay.down_qh, lay.down_sc,
-                           lay.down_d, b->offsets, b->counts, tiles, n_tiles, total, y);
-    }
-    err = hipGetLastError();
-  }
-  return err;
+  return hipGetLastError();
 }
 
 }  // namespace moe

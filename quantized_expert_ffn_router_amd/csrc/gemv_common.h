@@ -85,6 +85,13 @@ __device__ __forceinline__ void e2m1x8_bf16(uint32_t c, v2bf_t* o) {
 __device__ __forceinline__ v2bf_t as_v2bf(uint32_t u) { return __builtin_bit_cast(v2bf_t, u); }
 
 // Two floats -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+// silu(g) * u = g * u / (1 + e^-g) with the hardware exp2 and reciprocal
+// (about 1 ulp each; h is rounded to bf16 right after, 2^-9 relative).  Large
+// |g| give the right limits: e^-g -> 0 or inf, so the factor -> 1 or 0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f)) * u;
+}
+
 __device__ __forceinline__ v2bf_t to_v2bf(float a, float b) {
   v2f_t f = {a, b};
   return __builtin_convertvector(f, v2bf_t);
@@ -176,8 +183,8 @@ inline int choose_split(int items, int waves_per_item, int NG, int max_s) {
 // Launch helpers (one per kernel family), defined in their .hip files.
 size_t gemm_tiles_bytes(int E, int64_t A);
 hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
-                           const moe_buckets* b, uint16_t* hbuf, void* tiles_ws, void* y,
-                           int y_dtype, hipStream_t s);
+                           const moe_buckets* b, uint16_t* hbuf, uint16_t* xh, float* xscale,
+                           void* tiles_ws, void* y, int y_dtype, hipStream_t s);
 
 // h passes from the gate/up kernel to the down kernel as bf16 [A][I] (sorted
 // order).

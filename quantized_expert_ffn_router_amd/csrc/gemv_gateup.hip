@@ -154,7 +154,7 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_nvfp4(
         }
         gsum *= si.ref.ts_gate;
         usum *= si.ref.ts_up;
-        const float h = gsum / (1.0f + expf(-gsum)) * usum;
+        const float h = swiglu(gsum, usum);
         hout[(size_t)(si.base + c0 + t) * I + n2] = f32_to_bf16_rne(h);
       }
     }

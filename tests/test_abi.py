@@ -118,9 +118,13 @@ def test_zero_tokens_is_a_noop_and_null_checks():
 
 def test_workspace_bytes_cover_hidden_buffers():
     d = _desc(E=128, k=8, H=2048, I=768)
-    ws = q.moe_workspace_bytes(d, 16384)
-    assert ws >= 16384 * 8 * 768 * 4
-    assert q.moe_workspace_bytes(d, 1) >= 8 * 768 * 4
+    # h (bf16 [T*k][I]) + fp16 copy of x ([T][H]) + its row scales + the
+    # grouped GEMM's row-block tables (>= one 128-entry table per block)
+    T = 16384
+    ws = q.moe_workspace_bytes(d, T)
+    blocks = T * 8 // 128
+    assert ws >= T * 8 * 768 * 2 + T * 2048 * 2 + T * 4 + blocks * 128 * 8
+    assert q.moe_workspace_bytes(d, 1) >= 8 * 768 * 2 + 2048 * 2 + 4
 
 
 def test_tier_create_rejects_small_budget_before_any_hip_call():
