@@ -59,7 +59,10 @@ __global__ __launch_bounds__(1024) void k_build_tiles(const uint32_t* __restrict
   }
   const int start = pre[e] - nt;
   for (int i = 0; i < nt; ++i) tiles[start + i] = make_int2(e, i * bm);
-  if (e == 1023) *n_tiles = pre[1023];
+  if (e == 1023) {
+    n_tiles[0] = pre[1023];
+    n_tiles[1] = 0;  // fp16 h overflow flag of this call
+  }
 }
 
 // fp16 copy of the token rows for the gate/up GEMM, one wave per row.  Each
@@ -177,6 +180,43 @@ __device__ __forceinline__ void load_frag(FragNvfp4& f, const uint8_t* q, const 
   f.scale = gl2(sc + ((size_t)step * N + n) * 8 + 2 * grp);
 }
 
+// Lane parts of the NVFP4 fragment addresses (column lane%16, group lane/16),
+// computed once: per step only a wave-uniform part is added.
+struct BLane {
+  uint32_t q, s;
+};
+__device__ __forceinline__ BLane blane(int N) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4, n = lane & 15;
+  return BLane{(uint32_t)(grp * N + n) * 16u, (uint32_t)(n * 8 + 2 * grp)};
+}
+// Fragments of column tile cb.. of two matrices (gate and up: the same rows).
+__device__ __forceinline__ void load_frag_gu(FragNvfp4 (&f)[2], const uint8_t* q0,
+                                             const uint8_t* s0, const uint8_t* q1,
+                                             const uint8_t* s1, int N, int cb, int step,
+                                             BLane bl) {
+  const size_t uq = ((size_t)(4 * step) * N + cb) * 16, us = ((size_t)step * N + cb) * 8;
+  f[0].code = gl16(q0 + uq + bl.q);
+  f[1].code = gl16(q1 + uq + bl.q);
+  f[0].scale = gl2(s0 + us + bl.s) | (gl2(s1 + us + bl.s) << 16);  // both tiles' scales
+  f[1].scale = 0;
+}
+// Column tiles cb.. and cb + 16.. of one matrix: the second pair of addresses
+// is the first plus a constant, folded into the load offsets.
+__device__ __forceinline__ void load_frag_pair(FragNvfp4 (&f)[2], const uint8_t* q,
+                                               const uint8_t* sc, int N, int cb, int step,
+                                               BLane bl) {
+  // The empty asm makes the lane offsets opaque, so the compiler rebuilds the
+  // addresses here (2 adds) rather than keeping them live across the loop.
+  uint32_t oq = bl.q, os = bl.s;
+  __asm__ volatile("" : "+v"(oq), "+v"(os));
+  const uint8_t* pq = q + ((size_t)(4 * step) * N + cb) * 16 + oq;
+  const uint8_t* ps = sc + ((size_t)step * N + cb) * 8 + os;
+  f[0].code = gl16(pq);
+  f[1].code = gl16(pq + 16 * 16);
+  f[0].scale = gl2(ps) | (gl2(ps + 16 * 8) << 16);  // both tiles' scales
+  f[1].scale = 0;
+}
+
 // Sub-step s: 8 exact bf16 values (E2M1 x E4M3 has at most 6 significant bits).
 template <int S>
 __device__ __forceinline__ v8bf_t dequant_frag(const FragNvfp4& f) {
@@ -197,9 +237,11 @@ __device__ __forceinline__ v8bf_t dequant_frag(const FragNvfp4& f) {
 // The same 8 values as fp16 -- also exact (E2M1 x E4M3 lies in [2^-10, 2688]
 // with at most 5 significant bits): the codes convert to fp16 pairs and one
 // packed fp16 multiply applies the block scale, 2 VALU per pair instead of 4.
-template <int S>
-__device__ __forceinline__ v8h_t dequant_frag_h(const FragNvfp4& f) {
-  const v2h_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.scale, 1.0f, false);
+// The fp16 path keeps the scale bytes of both column tiles of a wave in one
+// register (tile j in 16-bit half j), so J selects the half.
+template <int S, int J>
+__device__ __forceinline__ v8h_t dequant_frag_h(const FragNvfp4& f, uint32_t scale2) {
+  const v2h_t s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scale2, 1.0f, J != 0);
   const _Float16 sc = s2[S >> 1];
   const v2h_t ss = {sc, sc};
   const uint32_t w = S == 0 ? f.code.x : S == 1 ? f.code.y : S == 2 ? f.code.z : f.code.w;
@@ -335,8 +377,9 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
     if constexpr (F16) {
       static_assert(FMT == MOE_FMT_NVFP4, "fp16 operands: NVFP4 weights");
       v8h_t bf[NC];
-#pragma unroll
-      for (int j = 0; j < NC; ++j) bf[j] = dequant_frag_h<S>(bcur[j]);
+      static_assert(NC == 2, "fp16 path: two column tiles, scales paired in bcur[0]");
+      bf[0] = dequant_frag_h<S, 0>(bcur[0], bcur[0].scale);
+      bf[1] = dequant_frag_h<S, 1>(bcur[1], bcur[0].scale);
       __builtin_amdgcn_sched_barrier(0);
       issue(S_);
       __builtin_amdgcn_sched_barrier(0);
@@ -378,6 +421,17 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
   sub(std::integral_constant<int, 3>{});
 }
 
+// fp16 h of a token is stored as h * 2^hexp, hexp = -21 - 2e where 2^e is the
+// token's x row scale (2^-e * max|x| in [2^14, 2^15)): h grows like |x|^2, so
+// the stored values sit near 2^8 * h / max|x|^2 whatever the activations'
+// magnitude, far from both ends of the fp16 range.  Exact powers of two.
+__device__ __forceinline__ int h_exp(float xscale) {
+  const int e = (int)((__float_as_uint(xscale) >> 23) & 0xffu) - 127;
+  const int k = -21 - 2 * e;
+  return k < -126 ? -126 : (k > 126 ? 126 : k);
+}
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
 // Tiles of this workgroup.  Workgroup w runs on XCD w % 8 (all workgroups of
 // the grid are resident, dispatched round robin); each XCD takes a contiguous
 // 1/8 of the logical tiles, in which consecutive tiles are the column tiles of
@@ -398,11 +452,21 @@ __device__ __forceinline__ TileRange tile_range(int n_logical) {
 // Tile columns: 128 consecutive rows n0.. of gate and the same rows of up;
 // wave w takes gate rows n0 + 16w .. +16 (tile j = 0) and the same up rows
 // (tile j = 1), so each lane holds matching g and u values.
+//
+// h goes out as fp16 when the down projection is NVFP4 (its GEMM then runs on
+// fp16 operands, whose dequant is half the work) and as bf16 otherwise.  fp16
+// keeps 3 more mantissa bits than bf16 but tops out at 65504: a value beyond
+// that is saturated and raises the call's overflow flag, and then the
+// FALLBACK instance (launched right after, idle unless the flag is set)
+// recomputes all of h as bf16 for a bf16 down GEMM, so the range is bf16's.
 
+template <bool HF16, bool FALLBACK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_gateup_nvfp4(
     const uint16_t* __restrict__ xh, int H, int I, size_t off_gq, size_t off_gs, size_t off_uq,
     size_t off_us, const TileRec* __restrict__ recs, const uint32_t* __restrict__ toff,
-    const float* __restrict__ rsc, const int* __restrict__ n_tiles, uint16_t* __restrict__ hout) {
+    const float* __restrict__ rsc, const int* __restrict__ n_tiles, int* ovf,
+    uint16_t* __restrict__ hout) {
+  if (FALLBACK && *ovf == 0) return;
   __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
   __shared__ uint32_t st_off[3][GBM];  // row tables of up to 3 tiles in flight
   __shared__ float st_rs[3][GBM];
@@ -445,10 +509,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   uint32_t off[4];
   read_rows(0, off);
   FragNvfp4 bnext[2];
+  const BLane bl = blane(I);
   load_a_tile(xh, off, 0, As, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_frag(bnext[0], P[0].p[0], P[0].p[1], I, cb + (lane & 15), 0);
-  load_frag(bnext[1], P[1].p[0], P[1].p[1], I, cb + (lane & 15), 0);
+  load_frag_gu(bnext, P[0].p[0], P[0].p[1], P[1].p[0], P[1].p[1], I, cb, 0, bl);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<4>();  // step 0's rows are in LDS (its weight loads may still fly)
   __syncthreads();
@@ -488,8 +552,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         constexpr int S = decltype(S_)::value;
         if (!ld) return;
         if constexpr (S == 0) {
-          load_frag(bnext[0], P[0].p[0], P[0].p[1], I, cbl + (lane & 15), stn);
-          load_frag(bnext[1], P[1].p[0], P[1].p[1], I, cbl + (lane & 15), stn);
+          load_frag_gu(bnext, P[0].p[0], P[0].p[1], P[1].p[0], P[1].p[1], I, cbl, stn, bl);
         } else if constexpr (S == 1) {
           load_a_half(xh, off, stn * GBK, Anext, wave, lane, 0);
         } else if constexpr (S == 2) {
@@ -510,18 +573,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const int r = 16 * i + (lane & 15);
       if (r < cur.nrows) {
         const float rs = st_rs[slot][r];
+        const float hs = HF16 ? pow2f(h_exp(rs)) : 1.0f;
         uint32_t hv[2];
+        bool big = false;
 #pragma unroll
         for (int q = 0; q < 4; q += 2) {
           float h2[2];
 #pragma unroll
           for (int d = 0; d < 2; ++d) {
             const float g = acc[i][0][q + d] * (tg * rs), u = acc[i][1][q + d] * (tu * rs);
-            h2[d] = swiglu(g, u);
+            h2[d] = swiglu(g, u) * hs;
           }
-          hv[q >> 1] = (uint32_t)f32_to_bf16_rne(h2[0]) | ((uint32_t)f32_to_bf16_rne(h2[1]) << 16);
+          if constexpr (HF16) {
+            big |= fabsf(h2[0]) > 65504.0f || fabsf(h2[1]) > 65504.0f;
+            const _Float16 a = (_Float16)fminf(fmaxf(h2[0], -65504.0f), 65504.0f);
+            const _Float16 b = (_Float16)fminf(fmaxf(h2[1], -65504.0f), 65504.0f);
+            hv[q >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, a) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+          } else {
+            hv[q >> 1] = (uint32_t)f32_to_bf16_rne(h2[0]) | ((uint32_t)f32_to_bf16_rne(h2[1]) << 16);
+          }
         }
         *reinterpret_cast<uint2*>(hout + (size_t)(cur.srow + r) * I + c0) = make_uint2(hv[0], hv[1]);
+        if (HF16 && big) *ovf = 1;
       }
     }
     if (!has_next) break;
@@ -534,12 +608,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // wave w takes columns n0 + 32w .. +32 (tiles j = 0, 1).  The A rows are the
 // tile's rows of h, contiguous in bucket order.
 
-template <int FMT, bool OUT_BF16>
+// AF16: h is fp16 (NVFP4 weights only).  RUN: 0 always; 1 only when the
+// call's fp16 h overflow flag is clear; 2 only when it is set.
+template <int FMT, bool OUT_BF16, bool AF16, int RUN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_down(
     const uint16_t* __restrict__ h, int H, int I, size_t off_a, size_t off_b, size_t off_c,
-    size_t off_d, const TileRec* __restrict__ recs, const int* __restrict__ n_tiles,
-    void* __restrict__ y) {
+    size_t off_d, const TileRec* __restrict__ recs, const float* __restrict__ rsc,
+    const int* __restrict__ n_tiles, const int* ovf, void* __restrict__ y) {
+  static_assert(!AF16 || FMT == MOE_FMT_NVFP4, "fp16 h pairs with NVFP4 weights");
+  if (RUN == 1 && *ovf != 0) return;
+  if (RUN == 2 && *ovf == 0) return;
   __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
+  __shared__ float st_rs[AF16 ? 3 : 1][GBM];  // x row scales of up to 3 tiles (fp16 h)
   const int NT = H / 256;
   const TileRange tr = tile_range(*n_tiles * NT);
   if (tr.first >= tr.end) return;
@@ -558,8 +638,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   auto planes_of = [&](const uint8_t* blob, Planes& P) {
     P.p[0] = blob + off_a; P.p[1] = blob + off_b; P.p[2] = blob + off_c; P.p[3] = blob + off_d;
   };
+  // Row scales of row block mt into LDS slot s (waves 0-1, async), fp16 h only.
+  auto stage_rs = [&](int mt, int s) {
+    if (AF16 && wave < 2)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(rsc + (size_t)mt * GBM + 64 * wave + lane),
+          (void __attribute__((address_space(3)))*)&st_rs[s][64 * wave], 4, 0, 0);
+  };
 
-  int L = tr.first, buf = 0;
+  int L = tr.first, buf = 0, slot = 0;
   const int mt = L / NT;
   int cb = (L - mt * NT) * 256 + 32 * wave;
   TileRec cur = recs[mt];
@@ -567,11 +654,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   planes_of((const uint8_t*)cur.ref.blob, P);
   uint32_t off[4];
   rows_of(cur, off);
+  stage_rs(mt, 0);
   FragOf<FMT> bnext[2];
+  const BLane bl = blane(H);
   load_a_tile(h, off, 0, As, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  load_b_tile<FMT>(bnext[0], P, H, cb + (lane & 15), 0);
-  load_b_tile<FMT>(bnext[1], P, H, cb + 16 + (lane & 15), 0);
+  if constexpr (AF16) {
+    load_frag_pair(bnext, P.p[0], P.p[1], H, cb, 0, bl);
+  } else {
+    load_b_tile<FMT>(bnext[0], P, H, cb + (lane & 15), 0);
+    load_b_tile<FMT>(bnext[1], P, H, cb + 16 + (lane & 15), 0);
+  }
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<2 * kB>();
   __syncthreads();
@@ -581,8 +674,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int Ln = L + tr.stride;
     const bool has_next = Ln < tr.end;
     const int mtn = Ln / NT, cbn = (Ln - mtn * NT) * 256 + 32 * wave;
+    const int slotn = slot == 2 ? 0 : slot + 1;
     TileRec nxt = cur;
-    if (has_next) nxt = recs[mtn];
+    if (has_next) {
+      nxt = recs[mtn];
+      stage_rs(mtn, slotn);  // read in the tile's epilogue, after its steps' barriers
+    }
     v4f_t acc[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -597,10 +694,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const bool ld = more || has_next;
       const int stn = more ? st + 1 : 0;
       uint16_t* Anext = As + (buf ^ 1) * GBM * ARB;
-      step_mfma<FMT, 2, false>(bcur, As + buf * GBM * ARB, lane, acc, [&](auto S_) {
+      step_mfma<FMT, 2, AF16>(bcur, As + buf * GBM * ARB, lane, acc, [&](auto S_) {
         constexpr int S = decltype(S_)::value;
         if (!ld) return;
-        if constexpr (S == 0) {
+        if constexpr (AF16) {  // spread over the step (see gate/up)
+          if constexpr (S == 0) {
+            load_frag_pair(bnext, P.p[0], P.p[1], H, cbl, stn, bl);
+          } else if constexpr (S == 1) {
+            load_a_half(h, off, stn * GBK, Anext, wave, lane, 0);
+          } else if constexpr (S == 2) {
+            load_a_half(h, off, stn * GBK, Anext, wave, lane, 1);
+          }
+        } else if constexpr (S == 0) {  // all at once: fewer live registers
           load_b_tile<FMT>(bnext[0], P, H, cbl + (lane & 15), stn);
           load_b_tile<FMT>(bnext[1], P, H, cbl + 16 + (lane & 15), stn);
           load_a_tile(h, off, stn * GBK, Anext, wave, lane);
@@ -619,9 +724,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const int r = 16 * i + (lane & 15);
       if (r < cur.nrows) {
         const size_t o = (size_t)(cur.srow + r) * H + cb + 4 * (lane >> 4);
+        const float tr_s = AF16 ? ts * pow2f(-h_exp(st_rs[slot][r])) : ts;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const v4f_t v = acc[i][j] * ts;
+          const v4f_t v = acc[i][j] * tr_s;
           if (OUT_BF16) {
             const uint32_t a = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
             const uint32_t b = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
@@ -634,7 +740,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       }
     }
     if (!has_next) break;
-    L = Ln; cb = cbn; cur = nxt;
+    L = Ln; cb = cbn; cur = nxt; slot = slotn;
   }
 }
 
@@ -644,11 +750,11 @@ int g_gemm_slots = 0;  // workgroups of a persistent launch: 2 per CU
 
 size_t gemm_tiles_bytes(int E, int64_t A) {
   const size_t mt = (size_t)(A / BM + E + 1);
-  return align_up(mt * sizeof(int2)) + align_up(sizeof(int)) + align_up(mt * sizeof(TileRec)) +
+  return align_up(mt * sizeof(int2)) + align_up(2 * sizeof(int)) + align_up(mt * sizeof(TileRec)) +
          2 * align_up(mt * GBM * sizeof(uint32_t));
 }
 
-// Grouped-GEMM expert FFN.  hbuf: bf16 [A][I]; xh: fp16 [T][H]; xscale: [T];
+// Grouped-GEMM expert FFN.  hbuf: h [A][I] (fp16 or bf16, see gate/up); xh: fp16 [T][H]; xscale: [T];
 // tiles_ws: gemm_tiles_bytes().
 hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                            const moe_buckets* b, uint16_t* hbuf, uint16_t* xh, float* xscale,
@@ -659,8 +765,9 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
   char* w = (char*)tiles_ws;
   int2* tiles = (int2*)w;
   w += align_up(mtmax * sizeof(int2));
-  int* n_tiles = (int*)w;
-  w += align_up(sizeof(int));
+  int* n_tiles = (int*)w;  // [0]: row blocks, [1]: fp16 h overflow flag
+  int* ovf = n_tiles + 1;
+  w += align_up(2 * sizeof(int));
   TileRec* recs = (TileRec*)w;
   w += align_up(mtmax * sizeof(TileRec));
   uint32_t* toff = (uint32_t*)w;
@@ -685,25 +792,31 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
                      toff, rsc);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const dim3 grid((unsigned)g_gemm_slots), block(kThreads);
-  hipLaunchKernelGGL(k_gemm_gateup_nvfp4, grid, block, 0, s, xh, L->H, L->I, lay.gate_q, lay.gate_s,
-                     lay.up_q, lay.up_s, recs, toff, rsc, n_tiles, hbuf);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   const bool bf = (y_dtype == MOE_DTYPE_BF16);
+#define GU_ARGS                                                                                   \
+  xh, L->H, L->I, lay.gate_q, lay.gate_s, lay.up_q, lay.up_s, recs, toff, rsc, n_tiles, ovf, hbuf
+#define DOWN(F, B, A16, R, P0, P1, P2, P3)                                                        \
+  hipLaunchKernelGGL((k_gemm_down<F, B, A16, R>), grid, block, 0, s, hbuf, L->H, L->I, P0, P1, P2, \
+                     P3, recs, rsc, n_tiles, ovf, y)
   if (L->fmt_down == MOE_FMT_NVFP4) {
-    if (bf)
-      hipLaunchKernelGGL((k_gemm_down<MOE_FMT_NVFP4, true>), grid, block, 0, s, hbuf, L->H, L->I,
-                         lay.down_q, lay.down_s, (size_t)0, (size_t)0, recs, n_tiles, y);
-    else
-      hipLaunchKernelGGL((k_gemm_down<MOE_FMT_NVFP4, false>), grid, block, 0, s, hbuf, L->H, L->I,
-                         lay.down_q, lay.down_s, (size_t)0, (size_t)0, recs, n_tiles, y);
+    // fp16 h; on overflow the bf16 instances redo the layer's FFN (see above)
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<true, false>), grid, block, 0, s, GU_ARGS);
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<false, true>), grid, block, 0, s, GU_ARGS);
+    const size_t q = lay.down_q, sc = lay.down_s, z = 0;
+    if (bf) {
+      DOWN(MOE_FMT_NVFP4, true, true, 1, q, sc, z, z);
+      DOWN(MOE_FMT_NVFP4, true, false, 2, q, sc, z, z);
+    } else {
+      DOWN(MOE_FMT_NVFP4, false, true, 1, q, sc, z, z);
+      DOWN(MOE_FMT_NVFP4, false, false, 2, q, sc, z, z);
+    }
   } else {
-    if (bf)
-      hipLaunchKernelGGL((k_gemm_down<MOE_FMT_Q6K, true>), grid, block, 0, s, hbuf, L->H, L->I,
-                         lay.down_ql, lay.down_qh, lay.down_sc, lay.down_d, recs, n_tiles, y);
-    else
-      hipLaunchKernelGGL((k_gemm_down<MOE_FMT_Q6K, false>), grid, block, 0, s, hbuf, L->H, L->I,
-                         lay.down_ql, lay.down_qh, lay.down_sc, lay.down_d, recs, n_tiles, y);
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<false, false>), grid, block, 0, s, GU_ARGS);
+    if (bf) DOWN(MOE_FMT_Q6K, true, false, 0, lay.down_ql, lay.down_qh, lay.down_sc, lay.down_d);
+    else DOWN(MOE_FMT_Q6K, false, false, 0, lay.down_ql, lay.down_qh, lay.down_sc, lay.down_d);
   }
+#undef GU_ARGS
+#undef DOWN
   return hipGetLastError();
 }
 

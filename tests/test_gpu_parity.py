@@ -8,7 +8,7 @@ import pytest
 
 import moegen
 import oracle
-from parity_util import check_buckets, check_layer, check_route, run_gpu
+from parity_util import check_buckets, check_layer, check_route, rel_l2, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -146,3 +146,28 @@ def test_mixed_prefill_q6k_down_sampled():
     w, L = layer("mixed")
     x = moegen.make_tokens(w, 4096, step=1)
     check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
+
+
+@pytest.mark.parametrize("x_std,w_std", [
+    (3e5, 0.02),   # token rows beyond the fp16 range: per-row scaled fp16 copy
+    (1e-3, 0.02),  # small activations: h scaled by the token's row scale
+    (1.0, 4.0),    # |h| beyond fp16 even after scaling: bf16 recompute
+])
+def test_gemm_activation_magnitudes(x_std, w_std):
+    """The grouped GEMM multiplies fp16 operands; the token rows and h carry
+    per-row power-of-two scales and an h overflow redoes the FFN with bf16 h.
+    Results stay within the relative bars at any activation magnitude (the
+    absolute bar of the other tests is for unit-scale activations)."""
+    w, L = layer("gemm_mag", E=16, k=4, H=512, I=384, T=300, x_std=x_std, w_std=w_std)
+    x = moegen.make_tokens(w, w.T)
+    g = run_gpu(L, x, ffn_mode=2)
+    logits, idx, wt = check_route(g, L, x)
+    ob = check_buckets(g["buckets"], idx, L.E)
+    toks = list(range(0, w.T, 3))
+    o_out, o_y = oracle.ffn_combine(L, x, idx, wt, None, toks, want_y=True)
+    rows = [t * L.k + j for t in toks for j in range(L.k)]
+    gy = g["y"][ob["asg_pos"][rows]]
+    assert rel_l2(gy, o_y[rows]) <= GEMM_Y_REL, rel_l2(gy, o_y[rows])
+    got = moegen.bf16_to_f32(g["out"][toks])
+    ref = moegen.bf16_to_f32(o_out[toks])
+    assert rel_l2(got, ref) <= 5e-3, rel_l2(got, ref)
