@@ -432,6 +432,17 @@ __device__ __forceinline__ int h_exp(float xscale) {
 }
 __device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
 
+// Two values rounded to bf16 (hardware round-to-nearest-even) in one word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, to_v2bf(a, b));
+}
+// Two values rounded to fp16 (round-to-nearest-even), clamped to +-65504.
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float a, float b) {
+  const v2f_t f = {__builtin_amdgcn_fmed3f(a, -65504.0f, 65504.0f),
+                   __builtin_amdgcn_fmed3f(b, -65504.0f, 65504.0f)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h_t));
+}
+
 // Tiles of this workgroup.  Workgroup w runs on XCD w % 8 (all workgroups of
 // the grid are resident, dispatched round robin); each XCD takes a contiguous
 // 1/8 of the logical tiles, in which consecutive tiles are the column tiles of
@@ -585,13 +596,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             h2[d] = swiglu(g, u) * hs;
           }
           if constexpr (HF16) {
-            big |= fabsf(h2[0]) > 65504.0f || fabsf(h2[1]) > 65504.0f;
-            const _Float16 a = (_Float16)fminf(fmaxf(h2[0], -65504.0f), 65504.0f);
-            const _Float16 b = (_Float16)fminf(fmaxf(h2[1], -65504.0f), 65504.0f);
-            hv[q >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, a) |
-                         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+            big |= fmaxf(fabsf(h2[0]), fabsf(h2[1])) > 65504.0f;
+            hv[q >> 1] = pack_f16x2_sat(h2[0], h2[1]);
           } else {
-            hv[q >> 1] = (uint32_t)f32_to_bf16_rne(h2[0]) | ((uint32_t)f32_to_bf16_rne(h2[1]) << 16);
+            hv[q >> 1] = pack_bf16x2(h2[0], h2[1]);
           }
         }
         *reinterpret_cast<uint2*>(hout + (size_t)(cur.srow + r) * I + c0) = make_uint2(hv[0], hv[1]);
@@ -729,9 +737,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         for (int j = 0; j < 2; ++j) {
           const v4f_t v = acc[i][j] * tr_s;
           if (OUT_BF16) {
-            const uint32_t a = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-            const uint32_t b = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + o + 16 * j) = make_uint2(a, b);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + o + 16 * j) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           } else {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + o + 16 * j) =
                 make_float4(v[0], v[1], v[2], v[3]);
