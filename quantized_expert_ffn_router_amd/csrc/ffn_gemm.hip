@@ -1,30 +1,30 @@
 // ffn_gemm.hip -- expert FFNs for prefill-sized batches: grouped GEMM on
-// MFMA with the block-quantized weights dequantized into LDS.
+// MFMA with the block-quantized weights dequantized in registers.
 //
 // With thousands of tokens the routed experts (NVFP4; Q6_K in the DQ6_K
 // packs: basalt.jgulfo.com, "Models" and "Quick start") are a real dense
 // contraction per expert: the m_e tokens routed to expert e (rows of x in
-// bucket order) times the expert's weights.  One launch covers all experts:
-//   - tiles: (expert, 128 token rows) x (128 output columns); the tile list is
-//     built on the device from the bucket counts (no host round trip), and the
-//     grid is sized for the worst case -- workgroups past the list exit;
-//   - tile order is XCD-aware: consecutive workgroup ids go to different XCDs
-//     (8), so logical tiles are laid out XCD-major and the column tiles of one
-//     token block share that XCD's L2 for the re-read token rows;
-//   - per K step of 128: the A tile (gathered bf16 token rows, or the bf16 h
-//     rows of the down projection) is copied to LDS; each wave reads its B
-//     fragments from the packed weight blob (one 16-byte granule per lane and
-//     column tile, see "B fragments") and dequantizes them in registers,
-//     exactly to bf16 (E2M1 x E4M3 has at most 6 significant bits; Q6_K
-//     d*sc*(q-32) has up to 24 and is rounded to bf16 -- see the design
-//     notes); the next K step's global data is loaded into registers while
-//     the MFMAs of this one run;
-//   - 4 waves, each a 64 x 64 sub-tile = 4 x 4 v_mfma_f32_16x16x32_bf16 tiles
+// bucket order) times the expert's weights.  One launch per projection covers
+// all experts:
+//   - row blocks (expert, 128 rows) are listed on the device from the bucket
+//     counts (no host round trip); each gets a record and tables of token row
+//     offsets and row scales;
+//   - persistent workgroups (two per CU) walk tiles (row block x column
+//     tile); each XCD takes a contiguous range, so the column tiles of a row
+//     block share that XCD's L2 for the re-read token rows;
+//   - per K step of 128: the A tile (token rows, or h rows for the down
+//     projection) is copied global -> LDS by the load unit; each wave loads
+//     its B fragments from the packed weight blob (one 16-byte granule per
+//     lane and column tile, see "B fragments") and dequantizes them in
+//     registers;
+//   - operands are fp16 (NVFP4 weights are exact in fp16; token rows carry
+//     an exact per-row power-of-two scale, see k_rows_to_f16) except for the
+//     Q6_K down projection and the bf16 recompute path, which use bf16;
+//   - 8 waves, each 128 rows x 32 columns = 8 x 2 v_mfma_f32_16x16x32 tiles
 //     with fp32 accumulation;
-//   - gate/up: the 128 B columns are 64 gate rows and the same 64 up rows of
-//     the weights, so each lane holds matching g and u values and the SwiGLU
-//     epilogue h = silu(g*ts_g) * (u*ts_u) runs in registers; h is stored as
-//     bf16.  Down: y = acc * ts_d in bf16 or fp32.
+//   - gate/up: each wave's two column tiles are the same 16 rows of gate and
+//     of up, so SwiGLU runs in registers; h is stored in 16 bits.  Down:
+//     y = acc * ts_d in bf16 or fp32.
 #include <type_traits>
 
 #include "gemv_common.h"
