@@ -62,15 +62,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.md")
 
 
 def sources_digest():
-    """sha256 over the library's kernel sources: counter readings are only
-    used while the kernels they were taken on are unchanged."""
+    """sha256 over the library's kernel sources with comments and blank space
+    removed: counter readings are only used while the code they were taken on
+    is unchanged (a comment edit keeps them)."""
     import hashlib
+    import re
     d = os.path.join(ROOT, "quantized_expert_ffn_router_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".h")):
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+            with open(os.path.join(d, f), encoding="utf-8") as fh:
+                code = fh.read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
+            code = " ".join(code.split())
+            h.update(f.encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 
