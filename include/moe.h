@@ -213,6 +213,18 @@ moe_status moe_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, floa
 moe_status moe_bucket(const moe_layer_desc* L, const int32_t* topk_idx, int64_t T,
                       const moe_buckets* b, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Gating step in one call: moe_route, then moe_bucket, then (when hist is
+ * not NULL) moe_expert_hist, with the same arguments and the same results
+ * bit for bit.  For E <= 256, T <= 64 and T*k <= 256 (decode-sized steps) top-k,
+ * bucketing and the histogram update run as one single-workgroup kernel
+ * after the router logits, two launches instead of four.
+ * hist: uint32 [E] or NULL; shifts as for moe_expert_hist (checked only when
+ * hist is not NULL).  ws: as for moe_bucket. */
+moe_status moe_route_bucket(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                            float* logits, int32_t* topk_idx, float* topk_w, const moe_buckets* b,
+                            void* ws, size_t ws_bytes, uint32_t* hist, int32_t decay_shift,
+                            int32_t unit_shift, hipStream_t stream);
+
 /* Expert FFNs with fused dequantization (SwiGLU):
  *   for each assignment a of expert e (token t = a / k), at sorted position
  *   p = b->asg_pos[a]:

@@ -302,6 +302,38 @@ moe_status moe_combine(const moe_layer_desc* L, const void* y, int32_t y_dtype,
                                            out, stream));
 }
 
+moe_status moe_route_bucket(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                            float* logits, int32_t* topk_idx, float* topk_w, const moe_buckets* b,
+                            void* ws, size_t ws_bytes, uint32_t* hist, int32_t decay_shift,
+                            int32_t unit_shift, hipStream_t stream) {
+  const char* W = "moe_route_bucket";
+  moe_status st = check_layer(L, W);
+  if (st != MOE_OK) return st;
+  if ((st = check_T(T, L->k, W)) != MOE_OK) return st;
+  if ((st = check_buckets(L, b, T, W)) != MOE_OK) return st;
+  if (hist && (decay_shift < 0 || decay_shift > 31 || unit_shift < 0 || unit_shift > 31))
+    return fail(MOE_ERR_INVALID_ARG, "%s: shifts (%d, %d) must be in [0, 31]", W, decay_shift,
+                unit_shift);
+  if (T == 0) return MOE_OK;
+  CHECK_PTR(x, W); CHECK_PTR(logits, W); CHECK_PTR(topk_idx, W); CHECK_PTR(topk_w, W);
+  CHECK_PTR(L->w_router, W);
+  const size_t need = moe::bucket_ws_bytes(L->E, T * L->k);
+  if (need > 0) {
+    CHECK_PTR(ws, W);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
+  }
+  hipError_t e = moe::launch_router(x, T, L->H, L->w_router, L->router_bias, L->E, logits, stream);
+  if (e != hipSuccess) return hip_status(W, e);
+  if (moe::gate_fused_fits(T, L->E, L->k))
+    return hip_status(W, moe::launch_gate_fused(logits, T, L->E, L->k, L->renormalize, topk_idx,
+                                                 topk_w, b, hist, decay_shift, unit_shift, stream));
+  e = moe::launch_topk(logits, T, L->E, L->k, L->renormalize, topk_idx, topk_w, stream);
+  if (e == hipSuccess) e = moe::launch_bucket(topk_idx, T * L->k, L->E, b, ws, stream);
+  if (e == hipSuccess && hist)
+    e = moe::launch_hist(b->counts, L->E, hist, decay_shift, unit_shift, stream);
+  return hip_status(W, e);
+}
+
 moe_status moe_expert_hist(const moe_layer_desc* L, const moe_buckets* b, uint32_t* hist,
                            int32_t decay_shift, int32_t unit_shift, hipStream_t stream) {
   const char* W = "moe_expert_hist";

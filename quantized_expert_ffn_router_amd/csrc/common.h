@@ -112,6 +112,12 @@ hipError_t launch_pack_granules(const uint8_t* src, int E, size_t src_expert_str
 hipError_t launch_router(const uint16_t* x, int64_t T, int H, const float* Wr,
                          const float* bias, int E, float* logits, hipStream_t s);
 
+// Top-k + bucketing (+ histogram when hist is not null) in one launch, for
+// E <= 256 and T * k <= 256 (gate_fused_fits).
+bool gate_fused_fits(int64_t T, int E, int k);
+hipError_t launch_gate_fused(const float* logits, int64_t T, int E, int k, int renorm,
+                             int32_t* idx, float* w, const moe_buckets* b, uint32_t* hist, int ds,
+                             int us, hipStream_t s);
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renorm, int32_t* idx,
                        float* w, hipStream_t s);
 

@@ -207,15 +207,12 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   i = __builtin_amdgcn_readlane(i, 63);
 }
 
-// One wavefront per token (E <= 64*NV): k rounds of a DPP wave arg-max.
+// Top-k of one token's logits l[0..E) by one wavefront (E <= 64*NV): k
+// rounds of a DPP wave arg-max.  Lane j < k gets the j-th expert and its
+// weight.
 template <int NV>
-__global__ __launch_bounds__(256) void k_topk_dpp(const float* __restrict__ logits, int T, int E,
-                                                  int k, int renorm, int32_t* __restrict__ idx,
-                                                  float* __restrict__ wout) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* l = logits + (size_t)t * E;
+__device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, int renorm,
+                                          int lane, int* e_out, float* w_out) {
   float v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = l[min(lane + 64 * i, E - 1)];  // clamped, unconditional
@@ -250,9 +247,120 @@ __global__ __launch_bounds__(256) void k_topk_dpp(const float* __restrict__ logi
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+  *e_out = my_e;
+  *w_out = ex / den;
+}
+
+// One wavefront per token.
+template <int NV>
+__global__ __launch_bounds__(256) void k_topk_dpp(const float* __restrict__ logits, int T, int E,
+                                                  int k, int renorm, int32_t* __restrict__ idx,
+                                                  float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int e;
+  float w;
+  topk_wave<NV>(logits + (size_t)t * E, E, k, renorm, lane, &e, &w);
   if (lane < k) {
-    idx[(size_t)t * k + lane] = my_e;
-    wout[(size_t)t * k + lane] = ex / den;
+    idx[(size_t)t * k + lane] = e;
+    wout[(size_t)t * k + lane] = w;
+  }
+}
+
+// Wave-wide inclusive prefix sum with DPP (rows of 16 by shifts 1, 2, 4, 8,
+// then row broadcasts 15 and 31 carry the row totals up).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+// Decode-sized gating step in one workgroup (E <= 256, T*k <= 256, T <= 64):
+// top-k of every token (a wavefront per token), then the same bucketing as
+// moe_bucket, computed in parallel: each token's wavefront sets bit t of
+// tmask[e] for its k experts (LDS atomics; a token's experts are distinct),
+// so counts[e] = popcount(tmask[e]) and assignment (t, j) of expert e sits
+// at offsets[e] + popcount(tmask[e] below bit t) -- ascending t within an
+// expert, which is ascending a = t*k + j, the stable order.  The usage
+// histogram is updated from the counts.  Two launches fewer than route top-k
+// + bucket + histogram.
+template <int NV>
+__global__ __launch_bounds__(1024) void k_gate_fused(
+    const float* __restrict__ logits, int T, int E, int k, int renorm,
+    int32_t* __restrict__ idx, float* __restrict__ wout, uint32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ pos, uint32_t* __restrict__ hist, int ds,
+    int us) {
+  __shared__ int keys[256];
+  __shared__ unsigned long long tmask[256];
+  __shared__ int s_off[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  // The histogram words are loaded now, so their latency hides behind top-k
+  // (E <= 256 <= 4 * blockDim.x).
+  uint32_t hv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid + j * (int)blockDim.x;
+    hv[j] = (hist != nullptr && e < E) ? hist[e] : 0u;
+  }
+  for (int e = tid; e < E; e += blockDim.x) tmask[e] = 0ull;
+  __syncthreads();
+  for (int t = wave; t < T; t += nw) {
+    int e;
+    float w;
+    topk_wave<NV>(logits + (size_t)t * E, E, k, renorm, lane, &e, &w);
+    if (lane < k) {
+      idx[(size_t)t * k + lane] = e;
+      wout[(size_t)t * k + lane] = w;
+      keys[t * k + lane] = e;
+      atomicOr(&tmask[e], 1ull << t);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // counts, offsets and the active list: lane owns experts 4*lane .. +4
+    int c[4], sc = 0, sa = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      c[i] = (e < E) ? __popcll(tmask[e]) : 0;
+      sc += c[i];
+      sa += c[i] > 0;
+    }
+    const int ic = wave_incl_scan(sc), ia = wave_incl_scan(sa);
+    int run = ic - sc, arun = ia - sa;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        counts[e] = (uint32_t)c[i];
+        offsets[e] = run;
+        s_off[e] = run;
+        if (c[i] > 0) active[arun++] = e;
+        run += c[i];
+      }
+    }
+    if (lane == 63) {
+      offsets[E] = ic;
+      *n_active = ia;
+    }
+  }
+  __syncthreads();
+  for (int a = tid; a < T * k; a += blockDim.x) {
+    const int t = a / k, e = keys[a];
+    const int p = s_off[e] + __popcll(tmask[e] & ((1ull << t) - 1ull));
+    sorted[p] = a;
+    pos[a] = p;
+  }
+  if (hist == nullptr) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid + j * (int)blockDim.x;
+    if (e < E) hist[e] = hv[j] - (hv[j] >> ds) + ((uint32_t)__popcll(tmask[e]) << us);
   }
 }
 
@@ -279,6 +387,25 @@ hipError_t launch_router(const uint16_t* x, int64_t T, int H, const float* Wr,
   if (tb_max >= 16) return launch_router_t<16, 4>(x, T, H, Wr, bias, E, logits, s);
   if (tb_max >= 8) return launch_router_t<8, 8>(x, T, H, Wr, bias, E, logits, s);
   return launch_router_t<4, 16>(x, T, H, Wr, bias, E, logits, s);
+}
+
+bool gate_fused_fits(int64_t T, int E, int k) {
+  return E <= 256 && T <= 64 && T * k <= 256;
+}
+
+hipError_t launch_gate_fused(const float* logits, int64_t T, int E, int k, int renorm,
+                             int32_t* idx, float* w, const moe_buckets* b, uint32_t* hist, int ds,
+                             int us, hipStream_t s) {
+  const unsigned threads = (unsigned)(64 * (T < 16 ? T : 16));
+#define GF(NV)                                                                                   \
+  hipLaunchKernelGGL(k_gate_fused<NV>, dim3(1), dim3(threads), 0, s, logits, (int)T, E, k,      \
+                     renorm, idx, w, b->counts, b->offsets, b->active, b->n_active,      \
+                     b->sorted_asg, b->asg_pos, hist, ds, us)
+  if (E <= 64) GF(1);
+  else if (E <= 128) GF(2);
+  else GF(4);
+#undef GF
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int renorm, int32_t* idx,

@@ -141,3 +141,23 @@ def test_tier_create_rejects_small_budget_before_any_hip_call():
     with pytest.raises(q.MoeError) as ei:
         q.moe_tier_create(desc)
     assert ei.value.status == q.MOE_ERR_INVALID_ARG
+
+
+def test_route_bucket_checks_before_launch():
+    d = _desc()
+    lib = q.lib()
+    n = q.moe_buckets_bytes(8, 4, 2)
+    buf = np.zeros(n + 256, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    b = q.moe_buckets_carve(base, n, 8, 4, 2)
+    f = lib.moe_route_bucket
+    assert f(ctypes.byref(d), None, 0, None, None, None, ctypes.byref(b), None, 0, None, 0, 0,
+             None) == q.MOE_OK
+    assert f(ctypes.byref(d), None, 4, 0x20, 0x30, 0x40, ctypes.byref(b), None, 0, None, 0, 0,
+             None) == q.MOE_ERR_INVALID_ARG
+    assert "x is NULL" in q.last_error()
+    assert f(ctypes.byref(d), 0x10, 4, 0x20, 0x30, 0x40, ctypes.byref(b), None, 0, 0x50, 40, 10,
+             None) == q.MOE_ERR_INVALID_ARG
+    assert "shifts" in q.last_error()
+    assert f(ctypes.byref(d), 0x10, 5, 0x20, 0x30, 0x40, ctypes.byref(b), None, 0, None, 0, 0,
+             None) == q.MOE_ERR_WORKSPACE
