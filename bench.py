@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--batches", type=str, default="1,2,4,8")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-mixed", action="store_true")
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--tiered-steps", type=int, default=2048,
                    help="steps of the 48-layer tiered stack (0: skip)")
@@ -226,6 +227,8 @@ def main():
     prefill = None if args.no_prefill else measure_prefill(args, q, moegen, torch, dev)
     del layers, buf
     torch.cuda.empty_cache()
+    mixed = None if args.no_mixed else measure_mixed(args, q, moegen, torch, dev)
+    torch.cuda.empty_cache()
     tiered = None if args.tiered_steps <= 0 else measure_tiered(args, q, moegen, torch)
 
     head = results[Bmax]
@@ -266,6 +269,7 @@ def main():
             for b in batches
         ],
         "prefill": prefill,
+        "mixed": mixed,
         "tiered": tiered,
         "cpu_baseline": cpu,
         "setup_s": round(gen_s, 1),
@@ -323,6 +327,79 @@ def measure_prefill(args, q, moegen, torch, dev):
         "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
                         "mean": float(counts.mean())},
     }
+
+
+def measure_mixed(args, q, moegen, torch, dev):
+    """The mixed-format layer (256 experts, top-8, hidden 2048, intermediate
+    512; NVFP4 gate/up, Q6_K-style down): decode batch 8 expert FFN (GB/s over
+    the active experts' bytes, four layer copies cycled so the Infinity Cache
+    cannot hold them) and the 4096-token prefill FFN (TFLOP/s), HIP events on
+    the launch stream around moe_expert_ffn."""
+    W = moegen.WORKLOADS["mixed"]
+    n_layers = 4
+    layers = [q.DeviceLayer(moegen.make_layer(W, layer=200 + l)) for l in range(n_layers)]
+    expert_bytes = layers[0].blob_bytes + 8
+    stream = torch.cuda.Stream()
+    out = {"workload": "mixed layer: 256 experts, top-8, hidden 2048, intermediate 512, "
+                       "NVFP4 gate/up, Q6_K-style down"}
+    # decode, batch 8
+    B = 8
+    buf = q.StepBuffers(layers[0], B)
+    bk = buf.buckets
+    na_off = bk.n_active - buf.bucket_buf.data_ptr()
+    n_active_view = buf.bucket_buf[na_off:na_off + 4].view(torch.int32)
+    xs = [torch.from_numpy(moegen.make_tokens(W, B, step=s, layer=300).view(np.int16).copy()).to(dev)
+          for s in range(X_POOL)]
+    n = 256
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    nact = torch.zeros(n, dtype=torch.int32, device=dev)
+    with torch.cuda.stream(stream):
+        for i in range(16 + n):
+            L = layers[i % n_layers]
+            x = xs[i % X_POOL]
+            q.moe_route_bucket(L.desc, x, B, buf.logits, buf.idx, buf.w, buf.buckets, buf.ws,
+                               buf.ws_bytes, None, 0, 0, stream)
+            if i >= 16:
+                ev[i - 16][0].record(stream)
+            q.moe_expert_ffn(L.desc, x, B, buf.buckets, buf.y, buf.y_dtype, buf.ws, buf.ws_bytes,
+                             stream)
+            if i >= 16:
+                ev[i - 16][1].record(stream)
+                nact[i - 16:i - 15].copy_(n_active_view)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    na = nact.cpu().numpy().astype(np.float64)
+    gbs = float((na * expert_bytes).sum() / (ms.sum() * 1e-3) / 1e9)
+    out["decode_b8"] = {"ffn_us": round(float(ms.mean() * 1e3), 3),
+                        "active_experts": round(float(na.mean()), 2),
+                        "ffn_GBps": round(gbs, 1), "ffn_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del buf
+    # prefill, 4096 tokens
+    T = W.extra["prefill_T"]
+    L = layers[0]
+    buf = q.StepBuffers(L, T, q.MOE_DTYPE_BF16)
+    x = torch.from_numpy(moegen.make_tokens(W, T, step=1).view(np.int16).copy()).to(dev)
+    n = 10
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    with torch.cuda.stream(stream):
+        q.moe_route_bucket(L.desc, x, T, buf.logits, buf.idx, buf.w, buf.buckets, buf.ws,
+                           buf.ws_bytes, None, 0, 0, stream)
+        for i in range(2 + n):
+            if i >= 2:
+                ev[i - 2][0].record(stream)
+            q.moe_expert_ffn(L.desc, x, T, buf.buckets, buf.y, buf.y_dtype, buf.ws, buf.ws_bytes,
+                             stream)
+            if i >= 2:
+                ev[i - 2][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 6.0 * T * W.k * W.H * W.I
+    tf = flops / (ms * 1e-3) / 1e12
+    out["prefill_4096"] = {"ffn_ms": round(ms, 4), "ffn_tflops": round(tf, 2),
+                           "frac_of_2500": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return out
 
 
 def measure_tiered(args, q, moegen, torch):

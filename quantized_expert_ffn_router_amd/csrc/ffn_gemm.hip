@@ -255,8 +255,7 @@ __device__ __forceinline__ v8h_t dequant_frag_h(const FragNvfp4& f, uint32_t sca
 struct FragQ6k {
   uint4 lo;     // 32 low nibbles: word s = sub-step s
   uint2 hi;     // 32 x 2 high bits: 16 bits per sub-step
-  uint32_t sc;  // the two int8 sub-scales of the granule (low 16 bits)
-  uint32_t d;   // fp16 superblock scale
+  uint32_t sc;  // the two int8 sub-scales of the granule (low 16 bits), fp16 d (high 16)
 };
 
 __device__ __forceinline__ void load_frag_q6k(FragQ6k& f, const uint8_t* ql, const uint8_t* qh,
@@ -266,13 +265,12 @@ __device__ __forceinline__ void load_frag_q6k(FragQ6k& f, const uint8_t* ql, con
   const int c = 4 * step + grp, sb = c >> 3;
   f.lo = gl16(ql + ((size_t)c * N + n) * 16);
   f.hi = gl8(qh + ((size_t)(c >> 1) * N + n) * 16 + 8 * (c & 1));
-  f.sc = gl2(sc + ((size_t)sb * N + n) * 16 + 2 * (c & 7));
-  f.d = gl2(dd + ((size_t)sb * N + n) * 2);
+  f.sc = gl2(sc + ((size_t)sb * N + n) * 16 + 2 * (c & 7)) | (gl2(dd + ((size_t)sb * N + n) * 2) << 16);
 }
 
 template <int S>
 __device__ __forceinline__ v8bf_t dequant_frag_q6k(const FragQ6k& f) {
-  const float s = f16_to_f32((uint16_t)f.d) * (float)(int8_t)((f.sc >> (8 * (S >> 1))) & 0xffu);
+  const float s = f16_to_f32((uint16_t)(f.sc >> 16)) * (float)(int8_t)((f.sc >> (8 * (S >> 1))) & 0xffu);
   const uint32_t lo = S == 0 ? f.lo.x : S == 1 ? f.lo.y : S == 2 ? f.lo.z : f.lo.w;
   const uint32_t h16 = ((S < 2 ? f.hi.x : f.hi.y) >> (16 * (S & 1))) & 0xffffu;
   v8bf_t r;
@@ -284,6 +282,42 @@ __device__ __forceinline__ v8bf_t dequant_frag_q6k(const FragQ6k& f) {
     const v2bf_t b = to_v2bf((float)(q0 - 32) * s, (float)(q1 - 32) * s);
     r[2 * p] = b[0];
     r[2 * p + 1] = b[1];
+  }
+  return r;
+}
+
+// The same 8 weights as fp16 for the fp16 path.  The six-bit codes are built
+// in byte lanes (even values of the sub-step in qe, odd in qo), then each pair
+// is placed by one byte permute as two fp16 subnormals q * 2^-24; one packed
+// fma gives (q - 32) * 2^-10 exactly and one packed multiply applies
+// d * sc * 2^10 (rounded once to fp16, then the product once: about 2^-11
+// relative, finer than the bf16 path's 2^-9).  Needs fp16 denormals, the
+// default mode.
+template <int S>
+__device__ __forceinline__ v8h_t dequant_frag_q6k_h(const FragQ6k& f) {
+  const float s32 = f16_to_f32((uint16_t)(f.sc >> 16)) * 1024.0f *
+                    (float)(int8_t)((f.sc >> (8 * (S >> 1))) & 0xffu);
+  const _Float16 sh = (_Float16)s32;
+  const v2h_t ss = {sh, sh};
+  const uint32_t lo = S == 0 ? f.lo.x : S == 1 ? f.lo.y : S == 2 ? f.lo.z : f.lo.w;
+  const uint32_t h16 = ((S < 2 ? f.hi.x : f.hi.y) >> (16 * (S & 1))) & 0xffffu;
+  // nibble p of h16 (high bits of values 2p, 2p+1) into byte p
+  uint32_t t = (h16 | (h16 << 8)) & 0x00ff00ffu;
+  t = (t | (t << 4)) & 0x0f0f0f0fu;
+  const uint32_t qe = (lo & 0x0f0f0f0fu) | ((t & 0x03030303u) << 4);
+  const uint32_t qo = ((lo >> 4) & 0x0f0f0f0fu) | (((t >> 2) & 0x03030303u) << 4);
+  const v2h_t k14 = {(_Float16)16384.0f, (_Float16)16384.0f};
+  const v2h_t m32 = {(_Float16)-0.03125f, (_Float16)-0.03125f};
+  v8h_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    // bytes [qe.p, 0, qo.p, 0]: selector 0..3 picks qe (second operand), 4..7 qo
+    const uint32_t sel = 0x0c000c00u | (uint32_t)p | ((uint32_t)(4 + p) << 16);
+    const uint32_t raw = __builtin_amdgcn_perm(qo, qe, sel);
+    const v2h_t q = __builtin_bit_cast(v2h_t, raw);
+    const v2h_t v = __builtin_elementwise_fma(q, k14, m32) * ss;
+    r[2 * p] = v[0];
+    r[2 * p + 1] = v[1];
   }
   return r;
 }
@@ -375,11 +409,15 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
   auto sub = [&](auto S_) {
     constexpr int S = decltype(S_)::value;
     if constexpr (F16) {
-      static_assert(FMT == MOE_FMT_NVFP4, "fp16 operands: NVFP4 weights");
       v8h_t bf[NC];
-      static_assert(NC == 2, "fp16 path: two column tiles, scales paired in bcur[0]");
-      bf[0] = dequant_frag_h<S, 0>(bcur[0], bcur[0].scale);
-      bf[1] = dequant_frag_h<S, 1>(bcur[1], bcur[0].scale);
+      static_assert(NC == 2, "fp16 path: two column tiles");
+      if constexpr (FMT == MOE_FMT_NVFP4) {  // scales of both tiles paired in bcur[0]
+        bf[0] = dequant_frag_h<S, 0>(bcur[0], bcur[0].scale);
+        bf[1] = dequant_frag_h<S, 1>(bcur[1], bcur[0].scale);
+      } else {
+        bf[0] = dequant_frag_q6k_h<S>(bcur[0]);
+        bf[1] = dequant_frag_q6k_h<S>(bcur[1]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       issue(S_);
       __builtin_amdgcn_sched_barrier(0);
@@ -623,7 +661,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const uint16_t* __restrict__ h, int H, int I, size_t off_a, size_t off_b, size_t off_c,
     size_t off_d, const TileRec* __restrict__ recs, const float* __restrict__ rsc,
     const int* __restrict__ n_tiles, const int* ovf, void* __restrict__ y) {
-  static_assert(!AF16 || FMT == MOE_FMT_NVFP4, "fp16 h pairs with NVFP4 weights");
   if (RUN == 1 && *ovf != 0) return;
   if (RUN == 2 && *ovf == 0) return;
   __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
@@ -667,7 +704,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const BLane bl = blane(H);
   load_a_tile(h, off, 0, As, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (AF16) {
+  if constexpr (AF16 && FMT == MOE_FMT_NVFP4) {
     load_frag_pair(bnext, P.p[0], P.p[1], H, cb, 0, bl);
   } else {
     load_b_tile<FMT>(bnext[0], P, H, cb + (lane & 15), 0);
@@ -707,7 +744,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         if (!ld) return;
         if constexpr (AF16) {  // spread over the step (see gate/up)
           if constexpr (S == 0) {
-            load_frag_pair(bnext, P.p[0], P.p[1], H, cbl, stn, bl);
+            if constexpr (FMT == MOE_FMT_NVFP4) {
+              load_frag_pair(bnext, P.p[0], P.p[1], H, cbl, stn, bl);
+            } else {
+              load_b_tile<FMT>(bnext[0], P, H, cbl + (lane & 15), stn);
+              load_b_tile<FMT>(bnext[1], P, H, cbl + 16 + (lane & 15), stn);
+            }
           } else if constexpr (S == 1) {
             load_a_half(h, off, stn * GBK, Anext, wave, lane, 0);
           } else if constexpr (S == 2) {
@@ -818,9 +860,16 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
       DOWN(MOE_FMT_NVFP4, false, false, 2, q, sc, z, z);
     }
   } else {
-    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<false, false>), grid, block, 0, s, GU_ARGS);
-    if (bf) DOWN(MOE_FMT_Q6K, true, false, 0, lay.down_ql, lay.down_qh, lay.down_sc, lay.down_d);
-    else DOWN(MOE_FMT_Q6K, false, false, 0, lay.down_ql, lay.down_qh, lay.down_sc, lay.down_d);
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<true, false>), grid, block, 0, s, GU_ARGS);
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<false, true>), grid, block, 0, s, GU_ARGS);
+    const size_t a = lay.down_ql, b2 = lay.down_qh, c = lay.down_sc, d = lay.down_d;
+    if (bf) {
+      DOWN(MOE_FMT_Q6K, true, true, 1, a, b2, c, d);
+      DOWN(MOE_FMT_Q6K, true, false, 2, a, b2, c, d);
+    } else {
+      DOWN(MOE_FMT_Q6K, false, true, 1, a, b2, c, d);
+      DOWN(MOE_FMT_Q6K, false, false, 2, a, b2, c, d);
+    }
   }
 #undef GU_ARGS
 #undef DOWN

@@ -148,17 +148,21 @@ def test_mixed_prefill_q6k_down_sampled():
     check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
 
 
-@pytest.mark.parametrize("x_std,w_std", [
-    (3e5, 0.02),   # token rows beyond the fp16 range: per-row scaled fp16 copy
-    (1e-3, 0.02),  # small activations: h scaled by the token's row scale
-    (1.0, 4.0),    # |h| beyond fp16 even after scaling: bf16 recompute
+@pytest.mark.parametrize("x_std,w_std,fmt_down", [
+    (3e5, 0.02, 1),   # token rows beyond the fp16 range: per-row scaled fp16 copy
+    (1e-3, 0.02, 1),  # small activations: h scaled by the token's row scale
+    (1.0, 4.0, 1),    # |h| beyond fp16 even after scaling: bf16 recompute
+    (1e-3, 0.02, 2),  # the same with the Q6_K-style down projection
+    (1.0, 4.0, 2),
 ])
-def test_gemm_activation_magnitudes(x_std, w_std):
+def test_gemm_activation_magnitudes(x_std, w_std, fmt_down):
     """The grouped GEMM multiplies fp16 operands; the token rows and h carry
     per-row power-of-two scales and an h overflow redoes the FFN with bf16 h.
     Results stay within the relative bars at any activation magnitude (the
     absolute bar of the other tests is for unit-scale activations)."""
-    w, L = layer("gemm_mag", E=16, k=4, H=512, I=384, T=300, x_std=x_std, w_std=w_std)
+    I = 384 if fmt_down == 1 else 512  # Q6_K needs I % 256 == 0
+    w, L = layer("gemm_mag", E=16, k=4, H=512, I=I, T=300, x_std=x_std, w_std=w_std,
+                 fmt_down=fmt_down)
     x = moegen.make_tokens(w, w.T)
     g = run_gpu(L, x, ffn_mode=2)
     logits, idx, wt = check_route(g, L, x)
