@@ -481,6 +481,19 @@ __device__ __forceinline__ uint32_t pack_f16x2_sat(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2h_t));
 }
 
+// Lane groups g = lane / 16 hold 4 consecutive outputs of a row each (the
+// transposed accumulator).  With rows of two 16-lane groups swapped between
+// two registers (a of the odd group <-> b of the even group below it), lane
+// group g ends up with 8 consecutive outputs in (a, b): the even group keeps
+// its a and gets the odd group's a, the odd group gets the even group's b and
+// keeps its b.  One 16-byte store then replaces two 8-byte ones, so a store
+// instruction covers 64-byte instead of 32-byte pieces of each row.
+__device__ __forceinline__ void swap_row_pairs(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
 // Tiles of this workgroup.  Workgroup w runs on XCD w % 8 (all workgroups of
 // the grid are resident, dispatched round robin); each XCD takes a contiguous
 // 1/8 of the logical tiles, in which consecutive tiles are the column tiles of
@@ -615,16 +628,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 
     // SwiGLU epilogue: lane holds row 16i + lane%16, columns cb + 4*(lane/16) .. +4.
+    // Row sets 2p and 2p+1 are computed for every lane (rows past nrows are
+    // never stored), then swapped so that lane group g stores columns
+    // cb + 8*(g/2) .. +8 of row set 2p + g%2.
     const float tg = cur.ref.ts_gate, tu = cur.ref.ts_up;
-    const int c0 = cb + 4 * (lane >> 4);
+    const int grp = lane >> 4;
+    bool big = false;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 16 * i + (lane & 15);
-      if (r < cur.nrows) {
+    for (int p = 0; p < 4; ++p) {
+      uint32_t hv[2][2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int i = 2 * p + s2;
+        const int r = 16 * i + (lane & 15);
         const float rs = st_rs[slot][r];
         const float hs = HF16 ? pow2f(h_exp(rs)) : 1.0f;
-        uint32_t hv[2];
-        bool big = false;
 #pragma unroll
         for (int q = 0; q < 4; q += 2) {
           float h2[2];
@@ -634,16 +652,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             h2[d] = swiglu(g, u) * hs;
           }
           if constexpr (HF16) {
-            big |= fmaxf(fabsf(h2[0]), fabsf(h2[1])) > 65504.0f;
-            hv[q >> 1] = pack_f16x2_sat(h2[0], h2[1]);
+            big |= (r < cur.nrows) && fmaxf(fabsf(h2[0]), fabsf(h2[1])) > 65504.0f;
+            hv[s2][q >> 1] = pack_f16x2_sat(h2[0], h2[1]);
           } else {
-            hv[q >> 1] = pack_bf16x2(h2[0], h2[1]);
+            hv[s2][q >> 1] = pack_bf16x2(h2[0], h2[1]);
           }
         }
-        *reinterpret_cast<uint2*>(hout + (size_t)(cur.srow + r) * I + c0) = make_uint2(hv[0], hv[1]);
-        if (HF16 && big) *ovf = 1;
       }
+      swap_row_pairs(hv[0][0], hv[1][0]);
+      swap_row_pairs(hv[0][1], hv[1][1]);
+      const int r = 16 * (2 * p + (grp & 1)) + (lane & 15);
+      if (r < cur.nrows)
+        *reinterpret_cast<uint4*>(hout + (size_t)(cur.srow + r) * I + cb + 8 * (grp >> 1)) =
+            make_uint4(hv[0][0], hv[0][1], hv[1][0], hv[1][1]);
     }
+    if (HF16 && big) *ovf = 1;
     if (!has_next) break;
     L = Ln; cb = cbn; slot = slotn; cur = nxt;
   }
@@ -768,24 +791,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 
     // Epilogue: lane holds row 16i + lane%16, columns cb + 16j + 4*(lane/16) .. +4.
+    // bf16: the two column tiles are swapped between lane groups so that
+    // group g stores columns cb + 8*(g/2) + 16*(g%2) .. +8 of its row.
     const float ts = (FMT == MOE_FMT_NVFP4) ? cur.ref.ts_down : 1.0f;
+    const int grp = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 16 * i + (lane & 15);
-      if (r < cur.nrows) {
-        const size_t o = (size_t)(cur.srow + r) * H + cb + 4 * (lane >> 4);
-        const float tr_s = AF16 ? ts * pow2f(-h_exp(st_rs[slot][r])) : ts;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const v4f_t v = acc[i][j] * tr_s;
-          if (OUT_BF16) {
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + o + 16 * j) =
-                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          } else {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + o + 16 * j) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          }
-        }
+      const float tr_s = AF16 ? ts * pow2f(-h_exp(st_rs[slot][r])) : ts;
+      const v4f_t v0 = acc[i][0] * tr_s, v1 = acc[i][1] * tr_s;
+      if constexpr (OUT_BF16) {
+        uint32_t a0 = pack_bf16x2(v0[0], v0[1]), a1 = pack_bf16x2(v0[2], v0[3]);
+        uint32_t b0 = pack_bf16x2(v1[0], v1[1]), b1 = pack_bf16x2(v1[2], v1[3]);
+        swap_row_pairs(a0, b0);
+        swap_row_pairs(a1, b1);
+        if (r < cur.nrows)
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + (size_t)(cur.srow + r) * H + cb +
+                                    8 * (grp >> 1) + 16 * (grp & 1)) = make_uint4(a0, a1, b0, b1);
+      } else if (r < cur.nrows) {
+        float* yo = reinterpret_cast<float*>(y) + (size_t)(cur.srow + r) * H + cb + 4 * grp;
+        *reinterpret_cast<float4*>(yo) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+        *reinterpret_cast<float4*>(yo + 16) = make_float4(v1[0], v1[1], v1[2], v1[3]);
       }
     }
     if (!has_next) break;

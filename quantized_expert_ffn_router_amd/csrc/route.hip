@@ -119,6 +119,144 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
   }
 }
 
+// Router logits for batches past decode size.  A wavefront computes 8 tokens x
+// 8 experts: per h, a lane converts the 8 activations and the 8 router weights
+// of its h to double once and does 64 fmas, so conversions cost a quarter of
+// the fma count.  The workgroup's 8 tokens are staged in LDS as fp32,
+// transposed to [h][8], so a lane reads them with two 16-byte LDS reads; the
+// four waves of a workgroup take 32 consecutive experts.  H is walked in
+// chunks of at most kRtChunk so the tile fits in 64 KiB; every lane still adds
+// its terms in ascending h, as in the file comment, and the result is
+// bit-identical to k_router_logits.
+//
+// Workgroup w runs on XCD w % 8.  The expert groups of one token block are
+// given to workgroups w, w + 8, w + 16, ..., all on one XCD, so the block's
+// activations are read from HBM once and then hit that XCD's L2.
+constexpr int kRtTok = 8, kRtExp = 8, kRtWaves = 4, kRtChunk = 2048;
+
+struct RtOperands {
+  float4 x0, x1;      // 8 activations (fp32) of one h
+  float w[kRtExp];    // 8 router weights of the same h
+};
+
+// Operands of one lane h-step.  The router rows are wave-uniform base
+// pointers plus a 32-bit byte offset kept opaque to the compiler, so each load
+// is one instruction on a scalar base instead of a 64-bit vector address.
+__device__ __forceinline__ void rt_load(RtOperands& o, const float4* xs, const float* const* wq,
+                                        uint32_t boff, int i) {
+  uint32_t off = boff + 256u * (uint32_t)i;
+  asm volatile("" : "+v"(off));
+  o.x0 = xs[128 * i];
+  o.x1 = xs[128 * i + 1];
+#pragma unroll
+  for (int q = 0; q < kRtExp; ++q)
+    o.w[q] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(wq[q]) + off);
+}
+
+__device__ __forceinline__ void rt_fma(double* acc, const RtOperands& o) {
+  double wd[kRtExp];
+#pragma unroll
+  for (int q = 0; q < kRtExp; ++q) wd[q] = (double)o.w[q];
+  const float xv[kRtTok] = {o.x0.x, o.x0.y, o.x0.z, o.x0.w, o.x1.x, o.x1.y, o.x1.z, o.x1.w};
+#pragma unroll
+  for (int t = 0; t < kRtTok; ++t) {
+    const double xd = (double)xv[t];
+#pragma unroll
+    for (int q = 0; q < kRtExp; ++q) acc[t * kRtExp + q] = __fma_rn(xd, wd[q], acc[t * kRtExp + q]);
+  }
+}
+
+__global__ __launch_bounds__(kRtWaves * 64) void k_router_logits_blk(
+    const uint16_t* __restrict__ x, int T, int H, const float* __restrict__ Wr,
+    const float* __restrict__ bias, int E, float* __restrict__ logits, int n_tb, int n_eg) {
+  extern __shared__ float4 xs4[];  // [h][8] fp32: two float4 per h
+  const int wg = blockIdx.x;
+  const int j = wg >> 3;
+  const int tb = (j / n_eg) * 8 + (wg & 7);
+  if (tb >= n_tb) return;  // whole workgroup: no barrier has been reached
+  const int eg = j % n_eg;
+  const int t0 = tb * kRtTok;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e0 = (eg * kRtWaves + wave) * kRtExp;
+  const bool live = e0 < E;  // wave-uniform; dead waves still take the barriers
+
+  const float* wq[kRtExp];  // wave-uniform row pointers
+#pragma unroll
+  for (int q = 0; q < kRtExp; ++q) wq[q] = Wr + (size_t)min(e0 + q, E - 1) * H;
+  // Token rows past T are read from row T - 1 and masked to zero.
+  const uint16_t* xr[kRtTok];
+  uint32_t xmask[kRtTok];
+#pragma unroll
+  for (int t = 0; t < kRtTok; ++t) {
+    xr[t] = x + (size_t)min(t0 + t, T - 1) * H;
+    xmask[t] = (t0 + t < T) ? 0xffffffffu : 0u;
+  }
+
+  double acc[kRtTok * kRtExp];
+#pragma unroll
+  for (int v = 0; v < kRtTok * kRtExp; ++v) acc[v] = 0.0;
+
+  for (int hc0 = 0; hc0 < H; hc0 += kRtChunk) {
+    const int hc = min(kRtChunk, H - hc0);  // multiple of 128
+    if (hc0 > 0) __syncthreads();           // previous chunk fully read
+    // Stage: thread p takes the h pair (2p, 2p+1) of all 8 tokens; rows past T
+    // are zero.  bf16 -> fp32 is exact (bits << 16).
+    for (int p = tid; p < hc / 2; p += kRtWaves * 64) {
+      uint32_t v[kRtTok];
+#pragma unroll
+      for (int t = 0; t < kRtTok; ++t)
+        v[t] = *reinterpret_cast<const uint32_t*>(xr[t] + hc0 + 2 * p) & xmask[t];
+      float lo[kRtTok], hi[kRtTok];
+#pragma unroll
+      for (int t = 0; t < kRtTok; ++t) {
+        lo[t] = __uint_as_float(v[t] << 16);
+        hi[t] = __uint_as_float(v[t] & 0xffff0000u);
+      }
+      xs4[4 * p + 0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
+      xs4[4 * p + 1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
+      xs4[4 * p + 2] = make_float4(hi[0], hi[1], hi[2], hi[3]);
+      xs4[4 * p + 3] = make_float4(hi[4], hi[5], hi[6], hi[7]);
+    }
+    __syncthreads();
+    if (live) {
+      // Lane h-steps i = 0 .. hc/64 - 1 (h = hc0 + lane + 64 i), operands
+      // loaded two steps ahead.
+      const float4* xl = xs4 + 2 * lane;
+      const uint32_t boff = 4u * (uint32_t)(hc0 + lane);
+      const int n = hc / 64;  // even
+      // Each step's operands are loaded one step ahead, into the register set
+      // the previous step has finished with; past the last step the loads
+      // repeat step n - 1 (in bounds, unused).
+      // Scheduling fences keep each group of loads ahead of the fmas that do
+      // not need it (the scheduler would otherwise pull every load to the top
+      // of the loop and wait on it at once).
+      RtOperands a, b;
+      rt_load(a, xl, wq, boff, 0);
+      for (int i = 0; i < n; i += 2) {
+        rt_load(b, xl, wq, boff, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        rt_fma(acc, a);
+        __builtin_amdgcn_sched_barrier(0);
+        rt_load(a, xl, wq, boff, min(i + 2, n - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        rt_fma(acc, b);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if (!live) return;
+
+  // 64 values, 64 lanes: after the transposed butterfly value v is on lane v.
+  tb_level<kRtTok * kRtExp, 32>(acc, lane);
+  const int t = t0 + lane / kRtExp, e = e0 + lane % kRtExp;
+  if (t < T && e < E) {
+    double s = acc[0];
+    if (bias) s += (double)bias[e];
+    logits[(size_t)t * E + e] = (float)s;
+  }
+}
+
 // One wavefront per token: k rounds of a wave-wide arg-max with key
 // (logit desc, expert asc), then the gate weights.
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E,
@@ -378,15 +516,17 @@ hipError_t launch_router_t(const uint16_t* x, int64_t T, int H, const float* Wr,
 
 hipError_t launch_router(const uint16_t* x, int64_t T, int H, const float* Wr,
                          const float* bias, int E, float* logits, hipStream_t s) {
-  // The x tile of TB tokens stays within 64 KiB of LDS: TB * H <= 32768.
-  const int tb_max = 32768 / H;  // >= 4 for H <= 8192
   // Decode-sized batches: one (token, expert) pair per wavefront -- many short
   // waves finish sooner than a few long ones.
   if (T <= 64) return launch_router_t<1, 1>(x, T, H, Wr, bias, E, logits, s);
-  // Larger batches: TB tokens x EB experts per wavefront, TB * EB = 64.
-  if (tb_max >= 16) return launch_router_t<16, 4>(x, T, H, Wr, bias, E, logits, s);
-  if (tb_max >= 8) return launch_router_t<8, 8>(x, T, H, Wr, bias, E, logits, s);
-  return launch_router_t<4, 16>(x, T, H, Wr, bias, E, logits, s);
+  // Larger batches: 8 tokens x 8 experts per wavefront (H % 128 == 0).
+  const int n_tb = (int)((T + kRtTok - 1) / kRtTok);
+  const int n_eg = (E + kRtWaves * kRtExp - 1) / (kRtWaves * kRtExp);
+  const int64_t n_wg = (int64_t)((n_tb + 7) / 8) * 8 * n_eg;
+  const size_t lds = (size_t)min(H, kRtChunk) * kRtTok * sizeof(float);
+  hipLaunchKernelGGL(k_router_logits_blk, dim3((unsigned)n_wg), dim3(kRtWaves * 64), lds, s, x,
+                     (int)T, H, Wr, bias, E, logits, n_tb, n_eg);
+  return hipGetLastError();
 }
 
 bool gate_fused_fits(int64_t T, int E, int k) {
