@@ -75,6 +75,18 @@ def test_no_renormalisation_and_k_equals_E():
     check_layer(L, x)
 
 
+@pytest.mark.parametrize("T", [5, 70])
+def test_more_than_eight_experts_per_token(T):
+    """k = 12: the combine takes a token's assignments in a group of 8 and a
+    partial group of 4, with one-wavefront blocks (T <= 64) and 256-thread
+    blocks (T > 64)."""
+    w, L = layer("k12", E=32, k=12, H=256, I=128, T=T)
+    x = moegen.make_tokens(w, T, step=4)
+    res = moegen.make_residual(w, T)
+    print("k12", T, flush=True)
+    check_layer(L, x, residual=res)
+
+
 # The grouped GEMM rounds h (and Q6_K weights) to bf16 before the MFMAs, so
 # its fp32 expert outputs are compared at the layer tolerance (rel L2 5e-3).
 GEMM_Y_REL = 5e-3
