@@ -317,43 +317,56 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   }
 }
 
-// Wave-wide arg-max of (value, index) under the order (value desc, index
-// asc), with DPP moves (a few cycles each, unlike LDS-routed shuffles):
-// lane pairs, quads, rows of 16 (rotate by 4 and 8), then row broadcasts; the
-// winner ends in lane 63 and is broadcast with readlane.
-__device__ __forceinline__ void better(float& v, int& i, float ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+// Orderable key of a logit: signed-integer order equals float order, -0
+// and +0 get the same key (they compare equal as floats), NaN gets the
+// lowest key.  key_to_float inverts it (a -0 comes back as +0, which gives
+// the same gate weights).
+__device__ __forceinline__ int logit_key(float f) {
+  int b = __float_as_int(f);
+  b = (b == (int)0x80000000) ? 0 : b;
+  const int k = b ^ ((b >> 31) & 0x7fffffff);
+  return (f != f) ? INT_MIN : k;
+}
+__device__ __forceinline__ float key_to_float(int k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7fffffff));
 }
 
+// Wave-wide maximum with DPP moves (a few cycles each, unlike LDS-routed
+// shuffles): lane pairs, quads, rows of 16 (rotate by 4 and 8), then row
+// broadcasts; lane 63 ends with the maximum, broadcast with readlane.
+// Lanes a row mask leaves out read INT_MIN (the identity of max), which lets
+// the compiler fold the move into one v_max_i32 with a DPP source.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_step(float& v, int& i) {
-  const float ov = __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
-                                         CTRL, ROW_MASK, 0xf, false));
-  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false);
-  better(v, i, ov, oi);
+__device__ __forceinline__ int dpp_max(int v) {
+  return max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, CTRL, ROW_MASK, 0xf, false));
 }
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  dpp_step<0xb1, 0xf>(v, i);   // quad_perm [1,0,3,2]
-  dpp_step<0x4e, 0xf>(v, i);   // quad_perm [2,3,0,1]
-  dpp_step<0x124, 0xf>(v, i);  // row_ror:4
-  dpp_step<0x128, 0xf>(v, i);  // row_ror:8 -> every lane holds its row's best
-  dpp_step<0x142, 0xa>(v, i);  // row_bcast:15 into rows 1 and 3
-  dpp_step<0x143, 0xc>(v, i);  // row_bcast:31 into rows 2 and 3 -> lane 63 holds the best
-  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-  i = __builtin_amdgcn_readlane(i, 63);
+__device__ __forceinline__ int wave_max(int v) {
+  v = dpp_max<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x124, 0xf>(v);  // row_ror:4
+  v = dpp_max<0x128, 0xf>(v);  // row_ror:8 -> every lane holds its row's maximum
+  v = dpp_max<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3 -> lane 63 holds the maximum
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Top-k of one token's logits l[0..E) by one wavefront (E <= 64*NV): k
-// rounds of a DPP wave arg-max.  Lane j < k gets the j-th expert and its
-// weight.
+// rounds.  Expert e sits in slot e / 64 of lane e % 64.  A round takes the
+// wave-wide maximum key m among the logits not yet taken, then the lowest
+// expert index holding m among them (ballot per slot, lowest slot first,
+// lowest set bit): the arg-max under the order (logit desc, index asc).
+// Lane j < k gets the j-th expert and its weight.
 template <int NV>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, int renorm,
                                           int lane, int* e_out, float* w_out) {
   float v[NV];
+  int key[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = l[min(lane + 64 * i, E - 1)];  // clamped, unconditional
+  for (int i = 0; i < NV; ++i) {
+    v[i] = l[min(lane + 64 * i, E - 1)];  // clamped, unconditional
+    key[i] = logit_key(v[i]);
+  }
   uint32_t taken = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
@@ -362,15 +375,21 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
   float my_v = 0.0f, top = 0.0f;
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    int bk = INT_MIN;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      if (!(taken & (1u << i))) better(bv, be, v[i], lane + 64 * i);
-    wave_argmax(bv, be);
+      if (!(taken & (1u << i))) bk = max(bk, key[i]);
+    const int m = wave_max(bk);
+    int be = -1;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const unsigned long long b = __ballot(!(taken & (1u << i)) && key[i] == m);
+      if (be < 0 && b != 0ull) be = 64 * i + __ffsll((long long)b) - 1;
+    }
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (j == 0) top = bv;
-    if (lane == j) { my_v = bv; my_e = be; }
+    const float mv = key_to_float(m);
+    if (j == 0) top = mv;
+    if (lane == j) { my_v = mv; my_e = be; }
   }
 
   float ex = (lane < k) ? expf(my_v - top) : 0.0f;
