@@ -46,6 +46,42 @@ __device__ __forceinline__ void tb_level(double* acc, int lane) {
   }
 }
 
+// The 64-lane tree sum of one double per lane (lane j adds lane j + w for
+// w = 32, 16, ..., 1), result in lane 0, without LDS-routed shuffles: the
+// two cross-row levels swap register halves between lane groups
+// (v_permlane32_swap, v_permlane16_swap; each lane then adds its partner's
+// value, and lanes below w get exactly p[j] + p[j + w]), the levels within a
+// row of 16 use DPP row shifts left (lane j reads lane j + w).
+template <int W>
+__device__ __forceinline__ double row_shl_f64(double v) {
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  uint2 r;
+  r.x = __builtin_amdgcn_update_dpp(0u, u.x, 0x100 | W, 0xf, 0xf, true);  // row_shl:W
+  r.y = __builtin_amdgcn_update_dpp(0u, u.y, 0x100 | W, 0xf, 0xf, true);
+  return __builtin_bit_cast(double, r);
+}
+__device__ __forceinline__ double tree_sum_lane0(double v) {
+  uint2 u = __builtin_bit_cast(uint2, v);
+  {  // w = 32
+    const auto lo = __builtin_amdgcn_permlane32_swap(u.x, u.x, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(u.y, u.y, false, false);
+    v = __builtin_bit_cast(double, make_uint2(lo[0], hi[0])) +
+        __builtin_bit_cast(double, make_uint2(lo[1], hi[1]));
+  }
+  u = __builtin_bit_cast(uint2, v);
+  {  // w = 16
+    const auto lo = __builtin_amdgcn_permlane16_swap(u.x, u.x, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(u.y, u.y, false, false);
+    v = __builtin_bit_cast(double, make_uint2(lo[0], hi[0])) +
+        __builtin_bit_cast(double, make_uint2(lo[1], hi[1]));
+  }
+  v = v + row_shl_f64<8>(v);
+  v = v + row_shl_f64<4>(v);
+  v = v + row_shl_f64<2>(v);
+  v = v + row_shl_f64<1>(v);
+  return v;
+}
+
 template <int TB, int EB>
 __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
     const uint16_t* __restrict__ x, int T, int H, const float* __restrict__ Wr,
@@ -55,6 +91,31 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
   extern __shared__ uint16_t xs[];  // [TB][H] bf16 bits
   const int t0 = blockIdx.x * TB;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int e0 = (blockIdx.y * kRouterWaves + wave) * EB;
+
+  const float* wrow[EB];
+#pragma unroll
+  for (int q = 0; q < EB; ++q) wrow[q] = Wr + (size_t)min(e0 + q, E - 1) * H;
+
+  // Router weights are fetched CH strides at a time (all loads in flight
+  // before the first use); terms are still added in ascending h.  The first
+  // batch is issued before the token rows are staged, so the two memory
+  // round trips overlap.
+  constexpr int CH = (EB == 1) ? 32 : 8;
+  float wv[CH][EB];
+  auto load_w = [&](int h0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // Unconditional loads from a clamped (in-bounds) index keep every load
+      // of the batch in flight; out-of-range strides are never added below.
+      const int hc = min(h0 + 64 * c, H - 1);
+#pragma unroll
+      for (int q = 0; q < EB; ++q) wv[c][q] = wrow[q][hc];
+    }
+  };
+  load_w(lane);
+
   // Stage the token block (rows past T are zero) with 16-byte loads.
   const int vec_per_row = H / 8;
   for (int i = tid; i < TB * vec_per_row; i += blockDim.x) {
@@ -64,32 +125,14 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
     *reinterpret_cast<uint4*>(xs + (size_t)r * H + 8 * c) = v;
   }
   __syncthreads();
-
-  const int wave = tid >> 6, lane = tid & 63;
-  const int e0 = (blockIdx.y * kRouterWaves + wave) * EB;
   if (e0 >= E) return;
 
   double acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.0;
 
-  const float* wrow[EB];
-#pragma unroll
-  for (int q = 0; q < EB; ++q) wrow[q] = Wr + (size_t)min(e0 + q, E - 1) * H;
-
-  // Router weights are fetched CH strides at a time (all loads in flight
-  // before the first use); terms are still added in ascending h.
-  constexpr int CH = (EB == 1) ? 32 : 8;
   for (int h0 = lane; h0 < H; h0 += 64 * CH) {
-    float wv[CH][EB];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      // Unconditional loads from a clamped (in-bounds) index keep every load
-      // of the batch in flight; out-of-range strides are never added below.
-      const int hc = min(h0 + 64 * c, H - 1);
-#pragma unroll
-      for (int q = 0; q < EB; ++q) wv[c][q] = wrow[q][hc];
-    }
+    if (h0 != lane) load_w(h0);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int h = h0 + 64 * c;
@@ -105,6 +148,15 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
     }
   }
 
+  if constexpr (V == 1) {
+    const double s0 = tree_sum_lane0(acc[0]);
+    if (lane == 0 && t0 < T) {
+      double s = s0;
+      if (bias) s += (double)bias[e0];
+      logits[(size_t)t0 * E + e0] = (float)s;
+    }
+    return;
+  }
   // Transposed butterfly (see file comment).
   tb_level<V, 32>(acc, lane);
   constexpr int kShift = (V == 1) ? 6 : (V == 2) ? 5 : (V == 4) ? 4 : (V == 8) ? 3 : (V == 16) ? 2 : (V == 32) ? 1 : 0;
