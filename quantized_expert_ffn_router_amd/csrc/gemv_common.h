@@ -155,6 +155,23 @@ __device__ __forceinline__ bool slot_info(const int32_t* __restrict__ active,
   return true;
 }
 
+// Activations are read with wave-uniform addresses through the scalar cache,
+// one 128-element group at a time, each group's reads waiting on the
+// previous ones; a first read that misses the cache costs a round trip per
+// group.  touch_lines reads one word of each of NL consecutive 64-byte lines
+// at p (wave-uniform) right after a pass's weight loads are issued, so the
+// lines are in the scalar cache by the time the groups are consumed: one
+// round trip, under the weights' own latency.  The xor of the words goes to
+// keep_scalar, which only makes the compiler keep (and wait for) the loads.
+template <int NL>
+__device__ __forceinline__ uint32_t touch_lines(const uint32_t* __restrict__ p) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int l = 0; l < NL; ++l) t ^= p[16 * l];
+  return t;
+}
+__device__ __forceinline__ void keep_scalar(uint32_t v) { asm volatile("" ::"s"(v)); }
+
 // E4M3 scale bytes 2i, 2i+1 (lo) or 2i+2, 2i+3 (hi) of a word -> fp32 pair, exact
 // (gfx950 converts OCP E4M3).
 template <bool HI>

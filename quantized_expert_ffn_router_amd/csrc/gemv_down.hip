@@ -176,6 +176,16 @@ __global__ __launch_bounds__(512) void k_gemv_down(
     for (int sg = 0; sg < gps_total; sg += GP) {
       Group<FMT> r[GP];
       dn_issue<FMT, GP, D>(r, P, H, nc, gb + sg);
+      {  // the pass's h values of the first 4 tokens (4 lines per group)
+        uint32_t tch = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (t < mt)
+            tch ^= touch_lines<4 * GP>(reinterpret_cast<const uint32_t*>(
+                                           h + (size_t)(si.base + c0 + t) * I) +
+                                       64 * (gb + sg));
+        keep_scalar(tch);
+      }
       dn_consume<FMT, GP, D>(r, h, si.base + c0, H, I, nc, P, ts, gb + sg, mt, acc);
     }
     __syncthreads();

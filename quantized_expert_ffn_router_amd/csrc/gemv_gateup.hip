@@ -139,6 +139,17 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_nvfp4(
     for (int sg = 0; sg < gps_total; sg += GPS) {  // passes of GPS groups
       GURing<GPS> R;
       gu_issue<GPS, D>(R, pq, ps, I, nc, gb + sg);
+      {  // the pass's activations of the first 4 tokens (4 lines per group)
+        uint32_t tch = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (t < mt)
+            tch ^= touch_lines<4 * GPS>(
+                reinterpret_cast<const uint32_t*>(
+                    x + token_row(sorted_asg, si.base + c0 + t, ktop, kshift, H)) +
+                64 * (gb + sg));
+        keep_scalar(tch);
+      }
       gu_consume<GPS, D>(R, x, sorted_asg, si.base + c0, ktop, kshift, H, I, nc, pq, ps, gb + sg,
                          mt, acc);
     }
