@@ -131,27 +131,27 @@ __device__ __forceinline__ void stage_rows_f32(const float* __restrict__ hin, in
 }
 
 // Per-slot header shared by the kernels: expert id, token count and offset.
-struct SlotInfo {
-  int e, cnt, base;
-  moe_expert_ref ref;
-};
-
-__device__ __forceinline__ bool slot_info(const int32_t* __restrict__ active,
-                                          const int32_t* __restrict__ n_active,
-                                          const uint32_t* __restrict__ counts,
-                                          const int32_t* __restrict__ offsets,
-                                          const moe_expert_ref* __restrict__ experts,
-                                          SlotInfo* si) {
+// The expert of this workgroup's slot (blockIdx.y) and its table entry: false
+// for a slot past n_active.  The expert's token count and first sorted
+// position are loaded separately by the caller, after it has issued its
+// first weight loads: they were just written by the gating step, while the
+// table entry is usually in L2, so the weights need not wait for them.
+__device__ __forceinline__ bool slot_expert(const int32_t* __restrict__ active,
+                                            const int32_t* __restrict__ n_active,
+                                            const moe_expert_ref* __restrict__ experts, int* e,
+                                            moe_expert_ref* ref) {
   const int slot = blockIdx.y;
   // Both loads in one round trip: active[] has E >= gridDim.y entries, so
   // active[slot] is in bounds even for a slot past n_active (then unused).
   const int na = __builtin_nontemporal_load(n_active);
-  const int e = __builtin_nontemporal_load(active + slot);
+  const int ee = __builtin_nontemporal_load(active + slot);
+  // Both values (and the table's address, a kernel argument) are consumed
+  // here, so both loads are issued before the first wait (left alone, the
+  // compiler tests na first and then loads active[slot]: two round trips).
+  asm volatile("" ::"s"(na), "s"(ee), "s"(experts));
   if (slot >= na) return false;
-  si->e = e;
-  si->cnt = (int)counts[si->e];
-  si->base = offsets[si->e];
-  si->ref = experts[si->e];
+  *e = ee;
+  *ref = experts[ee];
   return true;
 }
 

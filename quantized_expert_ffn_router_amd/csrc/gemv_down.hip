@@ -155,38 +155,50 @@ __global__ __launch_bounds__(512) void k_gemv_down(
     const int32_t* __restrict__ n_active, void* __restrict__ y) {
   extern __shared__ __align__(16) float red[];  // [S][kDnMT][64]
 
-  SlotInfo si;
-  if (!slot_info(active, n_active, counts, offsets, experts, &si)) return;
+  int e;
+  moe_expert_ref ref;
+  if (!slot_expert(active, n_active, experts, &e, &ref)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int nthreads = S * 64;
   const int n = blockIdx.x * 64 + lane;
   const size_t nc = (n < H) ? (size_t)n : 0;  // rows past the end read row 0, never stored
-  const uintptr_t blob = (uintptr_t)si.ref.blob;
+  const uintptr_t blob = (uintptr_t)ref.blob;
   const Planes P = {(const uint8_t*)(blob + (uintptr_t)P0.a), (const uint8_t*)(blob + (uintptr_t)P0.b),
                     (const uint8_t*)(blob + (uintptr_t)P0.c), (const uint8_t*)(blob + (uintptr_t)P0.d)};
-  const float ts = (FMT == MOE_FMT_NVFP4) ? si.ref.ts_down : 1.0f;
+  const float ts = (FMT == MOE_FMT_NVFP4) ? ref.ts_down : 1.0f;
   const int gb = wave * gps_total;
   float* acc = red + (size_t)wave * kDnMT * 64;
 
-  for (int c0 = 0; c0 < si.cnt; c0 += kDnMT) {
-    const int mt = min(kDnMT, si.cnt - c0);
-    __syncthreads();  // the previous batch's reads of red are done
-    for (int t = 0; t < mt; ++t) acc[t * 64 + lane] = 0.0f;  // this wave's slice only
+  // Batches of kDnMT tokens.  An active expert has at least one token, so the
+  // first batch always runs; its first pass's weights are requested before
+  // the token count and offset are read (see slot_expert).
+  int cnt = 1, base = 0, mt = 0;
+  for (int c0 = 0; c0 < cnt; c0 += kDnMT) {
+    if (c0 > 0) __syncthreads();  // the previous batch's reads of red are done
     for (int sg = 0; sg < gps_total; sg += GP) {
       Group<FMT> r[GP];
       dn_issue<FMT, GP, D>(r, P, H, nc, gb + sg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (sg == 0) {
+        if (c0 == 0) {
+          cnt = (int)counts[e];
+          base = offsets[e];
+        }
+        mt = min(kDnMT, cnt - c0);
+        for (int t = 0; t < mt; ++t) acc[t * 64 + lane] = 0.0f;  // this wave's slice only
+      }
       {  // the pass's h values of the first 4 tokens (4 lines per group)
         uint32_t tch = 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           if (t < mt)
             tch ^= touch_lines<4 * GP>(reinterpret_cast<const uint32_t*>(
-                                           h + (size_t)(si.base + c0 + t) * I) +
+                                           h + (size_t)(base + c0 + t) * I) +
                                        64 * (gb + sg));
         keep_scalar(tch);
       }
-      dn_consume<FMT, GP, D>(r, h, si.base + c0, H, I, nc, P, ts, gb + sg, mt, acc);
+      dn_consume<FMT, GP, D>(r, h, base + c0, H, I, nc, P, ts, gb + sg, mt, acc);
     }
     __syncthreads();
     for (int o = tid; o < mt * 64; o += nthreads) {
@@ -195,7 +207,7 @@ __global__ __launch_bounds__(512) void k_gemv_down(
       if (n2 < H) {
         float sum = 0.0f;
         for (int w = 0; w < S; ++w) sum += red[((size_t)w * kDnMT + t) * 64 + rr];
-        store_y<BF16>(y, (size_t)(si.base + c0 + t) * H + n2, sum);
+        store_y<BF16>(y, (size_t)(base + c0 + t) * H + n2, sum);
       }
     }
   }

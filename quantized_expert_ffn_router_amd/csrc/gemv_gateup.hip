@@ -118,27 +118,39 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_nvfp4(
     const int32_t* __restrict__ n_active, uint16_t* __restrict__ hout) {
   __shared__ float red[8][kGuMT][64];  // [wave][token][row] partial sums over K
 
-  SlotInfo si;
-  if (!slot_info(active, n_active, counts, offsets, experts, &si)) return;
+  int e;
+  moe_expert_ref ref;
+  if (!slot_expert(active, n_active, experts, &e, &ref)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int nthreads = 2 * S * 64;
   const int mat = wave / S, ks = wave - mat * S;
   const int n = blockIdx.x * 64 + lane;
   const size_t nc = (n < I) ? (size_t)n : 0;  // rows past the end read row 0, never stored
-  const uint8_t* blob = (const uint8_t*)si.ref.blob;
+  const uint8_t* blob = (const uint8_t*)ref.blob;
   const uint8_t* pq = blob + (mat ? off_uq : off_gq);
   const uint8_t* ps = blob + (mat ? off_us : off_gs);
   const int gb = ks * gps_total;
   float* acc = &red[wave][0][0];
 
-  for (int c0 = 0; c0 < si.cnt; c0 += kGuMT) {
-    const int mt = min(kGuMT, si.cnt - c0);
-    __syncthreads();  // the previous batch's reads of red are done
-    for (int t = 0; t < mt; ++t) acc[t * 64 + lane] = 0.0f;  // this wave's slice only
+  // Batches of kGuMT tokens.  An active expert has at least one token, so the
+  // first batch always runs; its first pass's weights are requested before
+  // the token count and offset are read (see slot_expert).
+  int cnt = 1, base = 0, mt = 0;
+  for (int c0 = 0; c0 < cnt; c0 += kGuMT) {
+    if (c0 > 0) __syncthreads();  // the previous batch's reads of red are done
     for (int sg = 0; sg < gps_total; sg += GPS) {  // passes of GPS groups
       GURing<GPS> R;
       gu_issue<GPS, D>(R, pq, ps, I, nc, gb + sg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (sg == 0) {
+        if (c0 == 0) {
+          cnt = (int)counts[e];
+          base = offsets[e];
+        }
+        mt = min(kGuMT, cnt - c0);
+        for (int t = 0; t < mt; ++t) acc[t * 64 + lane] = 0.0f;  // this wave's slice only
+      }
       {  // the pass's activations of the first 4 tokens (4 lines per group)
         uint32_t tch = 0;
 #pragma unroll
@@ -146,11 +158,11 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_nvfp4(
           if (t < mt)
             tch ^= touch_lines<4 * GPS>(
                 reinterpret_cast<const uint32_t*>(
-                    x + token_row(sorted_asg, si.base + c0 + t, ktop, kshift, H)) +
+                    x + token_row(sorted_asg, base + c0 + t, ktop, kshift, H)) +
                 64 * (gb + sg));
         keep_scalar(tch);
       }
-      gu_consume<GPS, D>(R, x, sorted_asg, si.base + c0, ktop, kshift, H, I, nc, pq, ps, gb + sg,
+      gu_consume<GPS, D>(R, x, sorted_asg, base + c0, ktop, kshift, H, I, nc, pq, ps, gb + sg,
                          mt, acc);
     }
     __syncthreads();
@@ -163,10 +175,10 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_nvfp4(
           gsum += red[w][t][r];
           usum += red[S + w][t][r];
         }
-        gsum *= si.ref.ts_gate;
-        usum *= si.ref.ts_up;
+        gsum *= ref.ts_gate;
+        usum *= ref.ts_up;
         const float h = swiglu(gsum, usum);
-        hout[(size_t)(si.base + c0 + t) * I + n2] = f32_to_bf16_rne(h);
+        hout[(size_t)(base + c0 + t) * I + n2] = f32_to_bf16_rne(h);
       }
     }
   }
