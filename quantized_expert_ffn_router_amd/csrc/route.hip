@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
 
   // Stage the token block (rows past T are zero) with 16-byte loads.
   const int vec_per_row = H / 8;
-  for (int i = tid; i < TB * vec_per_row; i += blockDim.x) {
+  for (int i = tid; i < TB * vec_per_row; i += kRouterWaves * 64) {
     int r = i / vec_per_row, c = i % vec_per_row;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (t0 + r < T) v = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + r) * H + 8 * c);
@@ -410,15 +410,17 @@ __device__ __forceinline__ int wave_max(int v) {
 // lowest set bit): the arg-max under the order (logit desc, index asc).
 // Lane j < k gets the j-th expert and its weight.
 template <int NV>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, int renorm,
-                                          int lane, int* e_out, float* w_out) {
-  float v[NV];
+__device__ __forceinline__ void topk_load(const float* __restrict__ l, int E, int lane, float* v) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = l[min(lane + 64 * i, E - 1)];  // clamped, unconditional
+}
+
+template <int NV>
+__device__ __forceinline__ void topk_select(const float* v, int E, int k, int renorm, int lane,
+                                            int* e_out, float* w_out) {
   int key[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    v[i] = l[min(lane + 64 * i, E - 1)];  // clamped, unconditional
-    key[i] = logit_key(v[i]);
-  }
+  for (int i = 0; i < NV; ++i) key[i] = logit_key(v[i]);
   uint32_t taken = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
@@ -458,6 +460,14 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
   *e_out = my_e;
   *w_out = ex / den;
+}
+
+template <int NV>
+__device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, int renorm,
+                                          int lane, int* e_out, float* w_out) {
+  float v[NV];
+  topk_load<NV>(l, E, lane, v);
+  topk_select<NV>(v, E, k, renorm, lane, e_out, w_out);
 }
 
 // One wavefront per token.
@@ -504,25 +514,37 @@ __global__ __launch_bounds__(1024) void k_gate_fused(
     int32_t* __restrict__ idx, float* __restrict__ wout, uint32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
     int32_t* __restrict__ sorted, int32_t* __restrict__ pos, uint32_t* __restrict__ hist, int ds,
-    int us) {
+    int us, int nthr) {
   __shared__ int keys[256];
   __shared__ unsigned long long tmask[256];
   __shared__ int s_off[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  // nthr = blockDim.x, passed as an argument so that no dispatch-packet field is read.
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = nthr >> 6;
   // The histogram words are loaded now, so their latency hides behind top-k
-  // (E <= 256 <= 4 * blockDim.x).
+  // (E <= 256 <= 4 * nthr).
   uint32_t hv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int e = tid + j * (int)blockDim.x;
+    const int e = tid + j * nthr;
     hv[j] = (hist != nullptr && e < E) ? hist[e] : 0u;
   }
-  for (int e = tid; e < E; e += blockDim.x) tmask[e] = 0ull;
+  // The first token's logits of each wave are requested before the LDS
+  // clear and its barrier.
+  float v0[NV];
+  topk_load<NV>(logits + (size_t)min(wave, T - 1) * E, E, lane, v0);
+  for (int e = tid; e < E; e += nthr) tmask[e] = 0ull;
   __syncthreads();
   for (int t = wave; t < T; t += nw) {
     int e;
     float w;
-    topk_wave<NV>(logits + (size_t)t * E, E, k, renorm, lane, &e, &w);
+    float v[NV];
+    if (t == wave) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[i] = v0[i];
+    } else {
+      topk_load<NV>(logits + (size_t)t * E, E, lane, v);
+    }
+    topk_select<NV>(v, E, k, renorm, lane, &e, &w);
     if (lane < k) {
       idx[(size_t)t * k + lane] = e;
       wout[(size_t)t * k + lane] = w;
@@ -559,7 +581,7 @@ __global__ __launch_bounds__(1024) void k_gate_fused(
     }
   }
   __syncthreads();
-  for (int a = tid; a < T * k; a += blockDim.x) {
+  for (int a = tid; a < T * k; a += nthr) {
     const int t = a / k, e = keys[a];
     const int p = s_off[e] + __popcll(tmask[e] & ((1ull << t) - 1ull));
     sorted[p] = a;
@@ -568,7 +590,7 @@ __global__ __launch_bounds__(1024) void k_gate_fused(
   if (hist == nullptr) return;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int e = tid + j * (int)blockDim.x;
+    const int e = tid + j * nthr;
     if (e < E) hist[e] = hv[j] - (hv[j] >> ds) + ((uint32_t)__popcll(tmask[e]) << us);
   }
 }
@@ -611,7 +633,7 @@ hipError_t launch_gate_fused(const float* logits, int64_t T, int E, int k, int r
 #define GF(NV)                                                                                   \
   hipLaunchKernelGGL(k_gate_fused<NV>, dim3(1), dim3(threads), 0, s, logits, (int)T, E, k,      \
                      renorm, idx, w, b->counts, b->offsets, b->active, b->n_active,      \
-                     b->sorted_asg, b->asg_pos, hist, ds, us)
+                     b->sorted_asg, b->asg_pos, hist, ds, us, (int)threads)
   if (E <= 64) GF(1);
   else if (E <= 128) GF(2);
   else GF(4);
