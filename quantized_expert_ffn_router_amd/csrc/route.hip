@@ -28,7 +28,31 @@ constexpr int kRouterWaves = 4;
 // remaining levels are plain pairwise sums.  All indices are compile time.
 template <int NV, int W>
 __device__ __forceinline__ void tb_level(double* acc, int lane) {
-  if constexpr (W >= 1) {
+  if constexpr ((W == 32 || W == 16) && NV > 1) {
+    // Across 32- or 16-lane groups the exchange is a register-half swap:
+    // permlane{32,16}_swap(a, b) gives the lower group (a, partner's a) and
+    // the upper group (partner's b, b), so a + b is keep + partner's copy on
+    // both sides, as in the generic step below.
+    constexpr int HALF = NV / 2;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+      const uint2 a = __builtin_bit_cast(uint2, acc[i]), b = __builtin_bit_cast(uint2, acc[i + HALF]);
+      uint2 na, nb;
+      if constexpr (W == 32) {
+        const auto lo = __builtin_amdgcn_permlane32_swap(a.x, b.x, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(a.y, b.y, false, false);
+        na = make_uint2(lo[0], hi[0]);
+        nb = make_uint2(lo[1], hi[1]);
+      } else {
+        const auto lo = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+        na = make_uint2(lo[0], hi[0]);
+        nb = make_uint2(lo[1], hi[1]);
+      }
+      acc[i] = __builtin_bit_cast(double, na) + __builtin_bit_cast(double, nb);
+    }
+    tb_level<HALF, W / 2>(acc, lane);
+  } else if constexpr (W >= 1) {
     if constexpr (NV > 1) {
       constexpr int HALF = NV / 2;
       const bool upper = (lane & W) != 0;
