@@ -147,9 +147,13 @@ __global__ __launch_bounds__(kThreads) void k_bucket_scan(const uint32_t* __rest
                                                           int32_t* __restrict__ base) {
   __shared__ int sm[kWaves + 1];
   const int e = threadIdx.x;
+  // Both passes over the blocks are unrolled so that 8 loads are in flight
+  // per round trip.
   int tot = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int b = 0; b < nb; ++b) tot += (int)blockcnt[(size_t)b * E + e];
+  }
   int total, nact;
   int off = block_exclusive_scan(tot, sm, &total);
   int apos = block_exclusive_scan((e < E && tot > 0) ? 1 : 0, sm, &nact);
@@ -158,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void k_bucket_scan(const uint32_t* __rest
     offsets[e] = off;
     if (tot > 0) active[apos] = e;
     int run = off;
+#pragma unroll 8
     for (int b = 0; b < nb; ++b) {
       base[(size_t)b * E + e] = run;
       run += (int)blockcnt[(size_t)b * E + e];
