@@ -78,22 +78,40 @@ __device__ __forceinline__ void decode_group(const Group<MOE_FMT_NVFP4>& r, floa
   }
 }
 
+// The codes of 8 values (one 32-bit word of low nibbles, 16 high bits) in
+// byte lanes: byte p of qe = value 2p, of qo = value 2p + 1.
+__device__ __forceinline__ void q6_bytes(uint32_t lo, uint32_t h16, uint32_t& qe, uint32_t& qo) {
+  uint32_t t = (h16 | (h16 << 8)) & 0x00ff00ffu;  // nibble p of h16 into byte p
+  t = (t | (t << 4)) & 0x0f0f0f0fu;
+  qe = (lo & 0x0f0f0f0fu) | ((t & 0x03030303u) << 4);
+  qo = ((lo >> 4) & 0x0f0f0f0fu) | (((t >> 2) & 0x03030303u) << 4);
+}
+
+// Code byte p of a word -> q - 32 as an exact float: one byte permute puts
+// the code in bits 16..21 under the exponent byte 0x43, which is the float
+// 128 + q; subtracting 160 leaves q - 32.
+template <int P>
+__device__ __forceinline__ float q6_value(uint32_t q) {
+  // result bytes: [0, 0, byte P of q, 0x43] (selector 0..3: q, 4..7: 0x43.., 0x0c: zero)
+  const uint32_t bits = __builtin_amdgcn_perm(0x43434343u, q, 0x04000c0cu | ((uint32_t)P << 16));
+  return __uint_as_float(bits) - 160.0f;
+}
+
 __device__ __forceinline__ void decode_group(const Group<MOE_FMT_Q6K>& r, float /*ts*/,
                                              v2bf_t (*w)[8], float* sc) {
   const float d = f16_to_f32((uint16_t)r.d);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     sc[j] = d * (float)(int8_t)((((j < 4) ? r.sc.x : r.sc.y) >> (8 * (j & 3))) & 0xffu);
-    const uint32_t lo0 = word_of(r.ql[j >> 1], (j & 1) * 2);      // elements 0..7
-    const uint32_t lo1 = word_of(r.ql[j >> 1], (j & 1) * 2 + 1);  // elements 8..15
-    const uint32_t hi = word_of(r.qh[j >> 2], j & 3);             // 2 bits per element
+    const uint32_t hi = word_of(r.qh[j >> 2], j & 3);  // 2 bits per element
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const uint32_t lw = (p < 4) ? lo0 : lo1;
-      const uint32_t byte = (lw >> (8 * (p & 3))) & 0xffu;
-      const int q0 = (int)((byte & 15u) | (((hi >> (4 * p)) & 3u) << 4));
-      const int q1 = (int)((byte >> 4) | (((hi >> (4 * p + 2)) & 3u) << 4));
-      w[j][p] = to_v2bf((float)(q0 - 32), (float)(q1 - 32));
+    for (int hw = 0; hw < 2; ++hw) {  // elements 8hw .. 8hw + 8
+      uint32_t qe, qo;
+      q6_bytes(word_of(r.ql[j >> 1], (j & 1) * 2 + hw), (hi >> (16 * hw)) & 0xffffu, qe, qo);
+      w[j][4 * hw + 0] = to_v2bf(q6_value<0>(qe), q6_value<0>(qo));
+      w[j][4 * hw + 1] = to_v2bf(q6_value<1>(qe), q6_value<1>(qo));
+      w[j][4 * hw + 2] = to_v2bf(q6_value<2>(qe), q6_value<2>(qo));
+      w[j][4 * hw + 3] = to_v2bf(q6_value<3>(qe), q6_value<3>(qo));
     }
   }
 }
@@ -148,7 +166,7 @@ __device__ __forceinline__ void dn_consume(Group<FMT> (&r)[GP], const uint16_t* 
 }
 
 template <int FMT, int GP, int D, bool BF16>
-__global__ __launch_bounds__(512) void k_gemv_down(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_down(
     const uint16_t* __restrict__ h, int H, int I, int S, int gps_total, Planes P0,
     const moe_expert_ref* __restrict__ experts, const uint32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
