@@ -33,8 +33,11 @@ def test_tiny_layer_full_parity():
     check_layer(L, x, residual=res)
 
 
-@pytest.mark.parametrize("B", [1, 2, 4, 8])
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32])
 def test_decode_layer_parity(B):
+    """Decode batches of 1-8 tokens and verification-sized batches of 16 and
+    32 (a few slots with draft tokens): dequant-fused GEMV path, fused gating
+    (T * k <= 256)."""
     w, L = layer("decode")
     x = moegen.make_tokens(w, B, step=B)
     print("decode B", B)
