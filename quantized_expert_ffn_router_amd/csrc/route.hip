@@ -113,10 +113,15 @@ __global__ __launch_bounds__(kRouterWaves * 64) void k_router_logits(
   constexpr int V = TB * EB;
   static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "TB*EB must be a power of two <= 64");
   extern __shared__ uint16_t xs[];  // [TB][H] bf16 bits
-  const int t0 = blockIdx.x * TB;
+  // blockIdx.x = expert group, blockIdx.y = token block: the token blocks of
+  // one expert group are 8-aligned strides of the linear workgroup id apart,
+  // so they run on the same XCD (workgroup w on XCD w % 8) and share its L2
+  // for the group's router rows.
+  const int t0 = blockIdx.y * TB;
+  if ((int)blockIdx.x * kRouterWaves * EB >= E) return;  // padding group: whole workgroup
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int e0 = (blockIdx.y * kRouterWaves + wave) * EB;
+  const int e0 = (blockIdx.x * kRouterWaves + wave) * EB;
 
   const float* wrow[EB];
 #pragma unroll
@@ -622,7 +627,9 @@ __global__ __launch_bounds__(1024) void k_gate_fused(
 template <int TB, int EB>
 hipError_t launch_router_t(const uint16_t* x, int64_t T, int H, const float* Wr,
                            const float* bias, int E, float* logits, hipStream_t s) {
-  dim3 grid((unsigned)((T + TB - 1) / TB), (unsigned)((E + EB * kRouterWaves - 1) / (EB * kRouterWaves)));
+  // x: expert groups rounded up to a multiple of 8 (see the kernel), y: token blocks
+  const unsigned n_eg = (unsigned)((E + EB * kRouterWaves - 1) / (EB * kRouterWaves));
+  dim3 grid((n_eg + 7u) & ~7u, (unsigned)((T + TB - 1) / TB));
   size_t lds = (size_t)TB * H * sizeof(uint16_t);
   hipLaunchKernelGGL((k_router_logits<TB, EB>), grid, dim3(kRouterWaves * 64), lds, s, x, (int)T,
                      H, Wr, bias, E, logits);
