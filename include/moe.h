@@ -281,10 +281,16 @@ moe_status moe_expert_hist(const moe_layer_desc* L, const moe_buckets* b, uint32
  * (bit for bit) what the same step computes with every expert resident.
  * Entries of inactive, non-resident experts are set to blob = NULL.
  *
+ * Copies: when every host blob is mapped for the device (hipHostMalloc
+ * memory is), one kernel on the copy stream moves a call's experts and the
+ * table, reading the pinned memory directly (expert-sized pieces then move at
+ * the large-transfer rate); otherwise one runtime copy per expert is issued.
+ *
  * Ownership: host blobs (pinned, e.g. hipHostMalloc), the HBM pool, the
  * device tables and both streams belong to the caller and must outlive the
  * tier.  The tier owns only host metadata, a few pinned bytes for the active
- * list and table staging, and two events.  A tier is not thread-safe.
+ * list, the table staging and the copy list, and two events.  A tier is not
+ * thread-safe.
  */
 typedef struct moe_tier_desc {
   int32_t L;                      /* layers */

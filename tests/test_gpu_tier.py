@@ -55,6 +55,25 @@ def test_tiered_stack_equals_all_resident_bit_exact():
     tiered.close()
 
 
+def test_runtime_copy_path_equals_all_resident_bit_exact():
+    """Host blobs in pageable memory are not mapped for the device, so the
+    tier copies with one runtime copy per expert instead of its copy kernel;
+    the results are the same bits."""
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    w, sets, routers, bias = _stack_inputs(L=2)
+    ref = LayerStack(sets, routers, bias, L=2, k=w.k)
+    tiered = LayerStack(sets, routers, bias, L=2, k=w.k,
+                        tiered={"resident": 16, "staging": 32, "pinned": False})
+    a = _run(ref, w, 4)
+    b = _run(tiered, w, 4, rebalance_every=2)
+    for st, (u, v) in enumerate(zip(a, b)):
+        assert np.array_equal(u, v), f"step {st} differs"
+    import quantized_expert_ffn_router_amd as q
+    stats, _ = q.moe_tier_stats_get(tiered.tier)
+    assert stats["misses"] > 0 and stats["promotions"] > 0
+    tiered.close()
+
+
 def test_rebalance_keeps_top_R_by_histogram():
     import torch
     import quantized_expert_ffn_router_amd as q
