@@ -20,6 +20,7 @@ _LIB = os.path.join(_HERE, "libmoegen.so")
 
 FMT_NVFP4 = 1
 FMT_Q6K = 2
+FMT_Q8_0 = 3
 
 # stream tags
 TAG_X = 1
@@ -62,6 +63,8 @@ def lib():
         L.moegen_quant_q6k.argtypes = [vp, i64, i64, vp]
         L.moegen_nvfp4_normal.argtypes = [u64, i64, i64, dbl, vp, vp, vp, vp]
         L.moegen_q6k_normal.argtypes = [u64, i64, i64, dbl, vp, vp]
+        L.moegen_quant_q8_0.argtypes = [vp, i64, i64, vp]
+        L.moegen_q8_0_normal.argtypes = [u64, i64, i64, dbl, vp, vp]
         L.moegen_permutation.argtypes = [u64, i32, vp]
         L.moegen_zipf_bias.argtypes = [u64, i32, dbl, dbl, vp, vp]
         L.moegen_threads.restype = ctypes.c_int
@@ -116,6 +119,16 @@ def quant_q6k(W: np.ndarray) -> np.ndarray:
     assert K % 256 == 0
     out = np.empty((N, K // 256 * 210), np.uint8)
     lib().moegen_quant_q6k(_p(W), N, K, _p(out))
+    return out
+
+
+def quant_q8_0(W: np.ndarray) -> np.ndarray:
+    """fp32 [N][K] -> Q8_0-style blocks u8 [N][K/32*34]."""
+    W = np.ascontiguousarray(W, np.float32)
+    N, K = W.shape
+    assert K % 32 == 0
+    out = np.empty((N, K // 32 * 34), np.uint8)
+    lib().moegen_quant_q8_0(_p(W), N, K, _p(out))
     return out
 
 
@@ -194,7 +207,7 @@ class LayerWeights:
     up_q: np.ndarray
     up_s: np.ndarray
     up_ts: np.ndarray
-    down_q: np.ndarray              # NVFP4 u8 [E][H][I/2] or Q6K u8 [E][H][I/256*210]
+    down_q: np.ndarray              # NVFP4 u8 [E][H][I/2], Q6K u8 [E][H][I/256*210], Q8_0 u8 [E][H][I/32*34]
     down_s: np.ndarray | None       # NVFP4 u8 [E][H][I/16]
     down_ts: np.ndarray | None      # NVFP4 f32 [E]
     renormalize: int = 1
@@ -220,6 +233,10 @@ def make_layer(w: Workload, layer: int = 0, seed: int | None = None) -> LayerWei
         dq = np.empty((E, H, I // 2), np.uint8)
         ds = np.empty((E, H, I // 16), np.uint8)
         dts = np.empty(E, np.float32)
+    elif w.fmt_down == FMT_Q8_0:
+        dq = np.empty((E, H, I // 32 * 34), np.uint8)
+        ds = None
+        dts = None
     else:
         dq = np.empty((E, H, I // 256 * 210), np.uint8)
         ds = None
@@ -236,6 +253,9 @@ def make_layer(w: Workload, layer: int = 0, seed: int | None = None) -> LayerWei
             L.moegen_nvfp4_normal(key(seed, (TAG_DOWN << 20) | e, layer), H, I, w.w_std,
                                   _p(scratch), _p(dq[e]), _p(ds[e]), _p(ts))
             dts[e] = ts[0]
+        elif w.fmt_down == FMT_Q8_0:
+            L.moegen_q8_0_normal(key(seed, (TAG_DOWN << 20) | e, layer), H, I, w.w_std,
+                                 _p(scratch), _p(dq[e]))
         else:
             L.moegen_q6k_normal(key(seed, (TAG_DOWN << 20) | e, layer), H, I, w.w_std,
                                 _p(scratch), _p(dq[e]))

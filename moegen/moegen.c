@@ -249,6 +249,35 @@ void moegen_quant_q6k(const float* W, int64_t N, int64_t K, uint8_t* out) {
   }
 }
 
+/* Quantize fp32 W[N][K] to Q8_0-style blocks of 32: d = fp16(amax/127),
+ * q = clamp(rne(w/d), -127, 127); a block is d (fp16 little-endian, 2 bytes)
+ * then the 32 int8 codes. */
+void moegen_quant_q8_0(const float* W, int64_t N, int64_t K, uint8_t* out) {
+  const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* w = W + n * K + b * 32;
+      uint8_t* blk = out + (n * nb + b) * 34;
+      double a = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        double v = fabs((double)w[i]);
+        if (v > a) a = v;
+      }
+      uint16_t dbits = f64_to_f16_rne(a / 127.0);
+      double d = f16_bits_to_f64(dbits);
+      blk[0] = (uint8_t)(dbits & 0xff);
+      blk[1] = (uint8_t)(dbits >> 8);
+      for (int i = 0; i < 32; ++i) {
+        double r = (d > 0) ? nearbyint((double)w[i] / d) : 0.0;
+        if (r > 127) r = 127;
+        if (r < -127) r = -127;
+        blk[2 + i] = (uint8_t)(int8_t)r;
+      }
+    }
+  }
+}
+
 /* Gaussian N(0, std) fp32 matrix quantized to NVFP4 in one call. */
 void moegen_nvfp4_normal(uint64_t key, int64_t N, int64_t K, double std,
                          float* scratch, uint8_t* codes, uint8_t* scales, float* ts) {
@@ -260,6 +289,12 @@ void moegen_q6k_normal(uint64_t key, int64_t N, int64_t K, double std,
                        float* scratch, uint8_t* out) {
   moegen_normal_f32(key, N * K, std, scratch);
   moegen_quant_q6k(scratch, N, K, out);
+}
+
+void moegen_q8_0_normal(uint64_t key, int64_t N, int64_t K, double std,
+                        float* scratch, uint8_t* out) {
+  moegen_normal_f32(key, N * K, std, scratch);
+  moegen_quant_q8_0(scratch, N, K, out);
 }
 
 /* Seeded permutation of 0..n-1 (Fisher-Yates driven by the stream). */

@@ -24,6 +24,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 FMT_NVFP4 = 1
 FMT_Q6K = 2
+FMT_Q8_0 = 3
 
 
 def build(force: bool = True) -> str:
@@ -80,6 +81,9 @@ def lib():
                                          vp, vp, i64, vp, vp]
         L.oracle_decode_nvfp4.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp]
         L.oracle_decode_q6k.argtypes = [vp, i64, i64, vp]
+        L.oracle_q8_0_weight.restype = ctypes.c_double
+        L.oracle_q8_0_weight.argtypes = [vp, i64, i64, i64]
+        L.oracle_decode_q8_0.argtypes = [vp, i64, i64, vp]
         _lib = L
     return _lib
 
@@ -126,6 +130,14 @@ def decode_q6k(blocks: np.ndarray, K: int) -> np.ndarray:
     N = blocks.shape[0]
     out = np.empty((N, K), np.float64)
     lib().oracle_decode_q6k(_p(np.ascontiguousarray(blocks)), N, K, _p(out))
+    return out
+
+
+def decode_q8_0(blocks: np.ndarray, K: int) -> np.ndarray:
+    """Q8_0-style rows [N][K/32*34] -> float64 [N][K] (d * q per 32-block)."""
+    N = blocks.shape[0]
+    out = np.empty((N, K), np.float64)
+    lib().oracle_decode_q8_0(_p(np.ascontiguousarray(blocks)), N, K, _p(out))
     return out
 
 

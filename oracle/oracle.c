@@ -12,7 +12,9 @@
  *     can move without becoming free").
  *   - Routed experts are stored as NVIDIA's NVFP4, and packs such as
  *     NVFP4-DQ6_K carry GGUF Q6_K tensors (basalt.jgulfo.com, sections
- *     "Models", "Quick start" and "All the numbers" / engine notes).
+ *     "Models", "Quick start" and "All the numbers" / engine notes); the
+ *     Basalt pack keeps its dense projections in Q8_0 (same page, "All the
+ *     numbers", "Engines: commit, and what is not NVIDIA's weights").
  * The pages give no formula; the readings used here (all listed in the design
  * notes) are: router logits in fp64 accumulation rounded once to fp32;
  * selection on logits by (logit desc, index asc); softmax renormalised over the
@@ -234,11 +236,21 @@ void oracle_hist(const uint32_t* counts, int64_t E, int decay_shift, int unit_sh
     hist[e] = hist[e] - (hist[e] >> decay_shift) + (counts[e] << unit_shift);
 }
 
+/* Q8_0-style weight (n, k): block b = k/32 of row n is 34 bytes:
+ * d fp16 little-endian[2] | q int8[32];  value = d * q[k % 32].
+ * (The pages name Q8_0 without its bytes; this is the GGUF block as
+ * published: one fp16 scale per 32 signed 8-bit values.) */
+double oracle_q8_0_weight(const uint8_t* blocks, int64_t K, int64_t n, int64_t k) {
+  const uint8_t* b = blocks + (n * (K / 32) + k / 32) * 34;
+  uint16_t dbits = (uint16_t)(b[0] | (b[1] << 8));
+  return oracle_f16(dbits) * (double)(int8_t)b[2 + k % 32];
+}
+
 /* ------------------------------------------------------------------ */
 /* Expert FFN and combine                                               */
 /* ------------------------------------------------------------------ */
 
-enum { ORACLE_FMT_NVFP4 = 1, ORACLE_FMT_Q6K = 2 };
+enum { ORACLE_FMT_NVFP4 = 1, ORACLE_FMT_Q6K = 2, ORACLE_FMT_Q8_0 = 3 };
 
 /* Expert weights in the canonical layouts, stacked over experts. */
 typedef struct oracle_experts {
@@ -249,7 +261,7 @@ typedef struct oracle_experts {
   const uint8_t* up_q;
   const uint8_t* up_s;
   const float* up_ts;
-  const uint8_t* down_q;   /* NVFP4 [E][H][I/2], or Q6_K [E][H][I/256*210] */
+  const uint8_t* down_q;   /* NVFP4 [E][H][I/2], Q6_K [E][H][I/256*210] or Q8_0 [E][H][I/32*34] */
   const uint8_t* down_s;   /* NVFP4 [E][H][I/16], NULL for Q6_K */
   const float* down_ts;    /* NVFP4 [E], NULL for Q6_K */
 } oracle_experts;
@@ -258,6 +270,8 @@ static double down_weight(const oracle_experts* X, int64_t e, int64_t n, int64_t
   int64_t H = X->H, I = X->I;
   if (X->fmt_down == ORACLE_FMT_Q6K)
     return oracle_q6k_weight(X->down_q + e * H * (I / 256) * 210, I, n, i);
+  if (X->fmt_down == ORACLE_FMT_Q8_0)
+    return oracle_q8_0_weight(X->down_q + e * H * (I / 32) * 34, I, n, i);
   return oracle_nvfp4_weight(X->down_q + e * H * (I / 2), X->down_s + e * H * (I / 16),
                              X->down_ts[e], I, n, i);
 }
@@ -330,4 +344,9 @@ void oracle_decode_nvfp4(const uint8_t* codes, const uint8_t* scales, float ts, 
 void oracle_decode_q6k(const uint8_t* blocks, int64_t N, int64_t K, double* out) {
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) out[n * K + k] = oracle_q6k_weight(blocks, K, n, k);
+}
+
+void oracle_decode_q8_0(const uint8_t* blocks, int64_t N, int64_t K, double* out) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) out[n * K + k] = oracle_q8_0_weight(blocks, K, n, k);
 }

@@ -108,6 +108,38 @@ def test_q6k_decode_closed_form():
             assert got[n, k] == exp
 
 
+def test_q8_0_decode_closed_form():
+    """Pack random int8 codes and fp16 scales by the documented byte layout
+    (d little-endian, then 32 codes per block); decode must equal d * q from
+    the integers and numpy's float16 decoding of d."""
+    rng = np.random.default_rng(6)
+    N, K = 3, 256
+    q = rng.integers(-128, 128, size=(N, K))
+    d = (rng.standard_normal((N, K // 32)) * 1e-3).astype(np.float16)
+    blocks = np.zeros((N, K // 32, 34), np.uint8)
+    for n in range(N):
+        for b in range(K // 32):
+            blocks[n, b, 0:2] = np.frombuffer(d[n, b].tobytes(), np.uint8)
+            blocks[n, b, 2:] = q[n, 32 * b:32 * b + 32].astype(np.int8).view(np.uint8)
+    got = oracle.decode_q8_0(blocks.reshape(N, -1), K)
+    for n in range(N):
+        for k in range(K):
+            assert got[n, k] == float(d[n, k // 32]) * float(q[n, k])
+
+
+def test_q8_0_generator_roundtrip_on_grid():
+    """Blocks whose values are d * integers with |q| <= 127 and one |q| = 127
+    (so amax / 127 = d, an exact fp16 power of two) survive quantize -> decode
+    exactly."""
+    rng = np.random.default_rng(7)
+    N, K = 4, 128
+    qi = rng.integers(-127, 128, size=(N, K))
+    qi[:, ::32] = 127 * np.where(rng.integers(0, 2, size=(N, K // 32)) > 0, 1, -1)
+    W = (qi * 2.0 ** -9).astype(np.float32)
+    dec = oracle.decode_q8_0(moegen.quant_q8_0(W), K)
+    np.testing.assert_array_equal(dec, W.astype(np.float64))
+
+
 def test_generator_quantizers_roundtrip_on_grid():
     """Values already on the NVFP4 / Q6_K grids survive quantize->decode."""
     e2m1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
@@ -256,6 +288,8 @@ def _dense_reference(L, x, w_idx, w_val, residual=None):
         Wu = dq(L.up_q[e], L.up_s[e], L.up_ts[e])
         if L.fmt_down == moegen.FMT_NVFP4:
             Wd = dq(L.down_q[e], L.down_s[e], L.down_ts[e])
+        elif L.fmt_down == moegen.FMT_Q8_0:
+            Wd = oracle.decode_q8_0(L.down_q[e], L.I)
         else:
             Wd = oracle.decode_q6k(L.down_q[e], L.I)
         g = xf @ Wg.T
@@ -291,6 +325,19 @@ def test_ffn_tiny_dense_fp64_reference():
 
 def test_ffn_q6k_down_dense_reference():
     W = moegen.Workload("q6", E=4, k=2, H=256, I=256, T=3, fmt_down=moegen.FMT_Q6K)
+    L = moegen.make_layer(W)
+    x = moegen.make_tokens(W, W.T)
+    _, idx, w = oracle.route(x, L)
+    out, y = oracle.ffn_combine(L, x, idx, w, want_y=True)
+    ref, ys = _dense_reference(L, x, idx, w)
+    for t in range(W.T):
+        for j in range(W.k):
+            np.testing.assert_allclose(y[t * W.k + j], ys[idx[t, j]][t], rtol=1e-12, atol=1e-15)
+    _bf16_close(out, ref)
+
+
+def test_ffn_q8_0_down_dense_reference():
+    W = moegen.Workload("q8", E=4, k=2, H=256, I=256, T=3, fmt_down=moegen.FMT_Q8_0)
     L = moegen.make_layer(W)
     x = moegen.make_tokens(W, W.T)
     _, idx, w = oracle.route(x, L)
