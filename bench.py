@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-mixed", action="store_true")
+    p.add_argument("--no-q8", action="store_true")
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--tiered-steps", type=int, default=2048,
                    help="steps of the 48-layer tiered stack (0: skip)")
@@ -232,7 +233,8 @@ def main():
     prefill = None if args.no_prefill else measure_prefill(args, q, moegen, torch, dev)
     del layers, buf
     torch.cuda.empty_cache()
-    mixed = None if args.no_mixed else measure_mixed(args, q, moegen, torch, dev)
+    mixed = None if args.no_mixed else measure_format(args, q, moegen, torch, dev, "mixed")
+    q8 = None if args.no_q8 else measure_format(args, q, moegen, torch, dev, "q8")
     torch.cuda.empty_cache()
     tiered = None if args.tiered_steps <= 0 else measure_tiered(args, q, moegen, torch)
 
@@ -276,6 +278,7 @@ def main():
         ],
         "prefill": prefill,
         "mixed": mixed,
+        "q8_0": q8,
         "tiered": tiered,
         "cpu_baseline": cpu,
         "setup_s": round(gen_s, 1),
@@ -335,19 +338,27 @@ def measure_prefill(args, q, moegen, torch, dev):
     }
 
 
-def measure_mixed(args, q, moegen, torch, dev):
-    """The mixed-format layer (256 experts, top-8, hidden 2048, intermediate
-    512; NVFP4 gate/up, Q6_K-style down): decode batch 8 expert FFN (GB/s over
-    the active experts' bytes, four layer copies cycled so the Infinity Cache
-    cannot hold them) and the 4096-token prefill FFN (TFLOP/s), HIP events on
-    the launch stream around moe_expert_ffn."""
-    W = moegen.WORKLOADS["mixed"]
+FORMAT_LAYERS = {
+    "mixed": "mixed layer: 256 experts, top-8, hidden 2048, intermediate 512, "
+             "NVFP4 gate/up, Q6_K-style down",
+    "q8": "Q8_0-down layer: 128 experts, top-8, hidden 2048, intermediate 768, "
+          "NVFP4 gate/up, Q8_0 down",
+}
+
+
+def measure_format(args, q, moegen, torch, dev, name):
+    """A layer with another down-projection format (the mixed layer: 256
+    experts, top-8, hidden 2048, intermediate 512, Q6_K-style down; the Q8_0
+    layer: the decode layer's shape with Q8_0 down): decode batch 8 expert FFN
+    (GB/s over the active experts' bytes, four layer copies cycled so the
+    Infinity Cache cannot hold them) and the 4096-token prefill FFN (TFLOP/s),
+    HIP events on the launch stream around moe_expert_ffn."""
+    W = moegen.WORKLOADS[name]
     n_layers = 4
     layers = [q.DeviceLayer(moegen.make_layer(W, layer=200 + l)) for l in range(n_layers)]
     expert_bytes = layers[0].blob_bytes + 8
     stream = torch.cuda.Stream()
-    out = {"workload": "mixed layer: 256 experts, top-8, hidden 2048, intermediate 512, "
-                       "NVFP4 gate/up, Q6_K-style down"}
+    out = {"workload": FORMAT_LAYERS[name]}
     # decode, batch 8
     B = 8
     buf = q.StepBuffers(layers[0], B)

@@ -2,7 +2,7 @@
  * moe.h -- C ABI of libmoe, a single-GPU (MI355X / gfx950) implementation of
  * the mixture-of-experts layer of a Basalt-style local inference engine:
  * router logits, softmax top-k gating, token-to-expert bucketing, block-
- * quantized (NVFP4, Q6_K-style) SwiGLU expert FFNs with the dequantization
+ * quantized (NVFP4, Q6_K-style, Q8_0) SwiGLU expert FFNs with the dequantization
  * fused into the matmuls, the gate-weighted combine, and the per-step expert
  * usage histogram that decides which experts stay resident.
  *
@@ -18,7 +18,11 @@
  *   - 1 to 8 concurrent request slots, so decode batches of 1..8 tokens --
  *     aiopssre.com, section "Concurrency divides context unless you pay for
  *     more cache"; devotd.net (en), section "--parallel slots and KV cache
- *     allocation".
+ *     allocation";
+ *   - Q8_0 is the 8-bit GGUF format the pages measure quality against and
+ *     keep for Basalt's dense projections -- basalt.jgulfo.com, "All the
+ *     numbers" (the quality table and the engine notes); here it is offered
+ *     as a down-projection format of the experts.
  * The pages give no formula.  The arithmetic below is the plainest reading;
  * each entry point states it.
  *
@@ -38,7 +42,8 @@
  *   - bf16 values are passed as uint16_t bit patterns.
  *
  * Supported shapes: 1 <= k <= min(E, 64), E <= 1024, H % 128 == 0,
- * 128 <= H <= 8192, I % 128 == 0 (NVFP4) or I % 256 == 0 (Q6_K), I <= 8192.
+ * 128 <= H <= 8192, I % 128 == 0 (NVFP4, Q8_0) or I % 256 == 0 (Q6_K),
+ * I <= 8192.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -67,6 +72,7 @@ typedef enum moe_status {
 /* Weight formats. */
 #define MOE_FMT_NVFP4 1  /* E2M1 codes, E4M3 scale per 16 along K, fp32 per-tensor scale */
 #define MOE_FMT_Q6K 2    /* 256-element superblocks: 16 x int8 sub-scales, fp16 scale, 6-bit codes */
+#define MOE_FMT_Q8_0 3   /* 32-element blocks: fp16 scale, 32 int8 codes (down projection only) */
 
 /* Element types of the expert-output buffer y. */
 #define MOE_DTYPE_F32 0
@@ -110,6 +116,9 @@ const char* moe_last_error(void);
  *     (high 2 bits of element i: bits 2*(i&3) of byte i/4), sc int8[16]
  *     (sub-block i/16), d fp16 little-endian[2];
  *     w = d * sc[i/16] * (q - 32), q = low | high << 4 in 0..63.
+ *   Q8_0 matrix W[N][K]: row n is K/32 blocks of 34 bytes: d fp16
+ *     little-endian[2], then the int8 codes q[32] of elements 32b..32b+31;
+ *     w = d * q.
  *   Gate and up are [I][H] (K = H); down is [H][I] (K = I).
  *
  * The GPU kernels read a packed "blob" per expert (a device-friendly
@@ -123,7 +132,7 @@ typedef struct moe_expert_ref {
   const void* blob;   /* device pointer to the packed expert (256-byte aligned) */
   float ts_gate;      /* NVFP4 per-tensor scales */
   float ts_up;
-  float ts_down;      /* ignored when the down projection is Q6_K */
+  float ts_down;      /* ignored when the down projection is Q6_K or Q8_0 */
   uint32_t reserved;  /* 0 */
 } moe_expert_ref;
 
@@ -132,8 +141,9 @@ size_t moe_expert_blob_bytes(int32_t H, int32_t I, int32_t fmt_gate_up, int32_t 
 
 /* Pack E experts from the canonical layouts (device arrays stacked over
  * experts: gate_q [E][I][H/2], gate_s [E][I][H/16], up likewise, down_q
- * [E][H][I/2] and down_s [E][H][I/16] for NVFP4, or down_q [E][H][I/256*210]
- * and down_s == NULL for Q6_K) into E blobs at blobs + e * blob_stride.
+ * [E][H][I/2] and down_s [E][H][I/16] for NVFP4, down_q [E][H][I/256*210]
+ * for Q6_K or down_q [E][H][I/32*34] for Q8_0, down_s == NULL for both) into
+ * E blobs at blobs + e * blob_stride.
  * blob_stride >= moe_expert_blob_bytes(...) and a multiple of 256. */
 moe_status moe_pack_experts(int32_t E, int32_t H, int32_t I, int32_t fmt_gate_up,
                             int32_t fmt_down, const uint8_t* gate_q, const uint8_t* gate_s,
@@ -152,7 +162,7 @@ typedef struct moe_layer_desc {
   int32_t H;            /* hidden size */
   int32_t I;            /* expert intermediate size */
   int32_t fmt_gate_up;  /* MOE_FMT_NVFP4 */
-  int32_t fmt_down;     /* MOE_FMT_NVFP4 or MOE_FMT_Q6K */
+  int32_t fmt_down;     /* MOE_FMT_NVFP4, MOE_FMT_Q6K or MOE_FMT_Q8_0 */
   int32_t renormalize;  /* 1: softmax renormalised over the selected k; 0: full softmax */
   int32_t reserved;     /* 0 */
   const moe_expert_ref* experts;  /* device [E] */

@@ -185,6 +185,9 @@ WORKLOADS = {
     # 256 experts, top-8, hidden 2048, intermediate 512; down in Q6_K-style
     "mixed": Workload("mixed", E=256, k=8, H=2048, I=512, T=8, fmt_down=FMT_Q6K,
                       extra={"prefill_T": 4096}),
+    # the decode layer with its down projection in Q8_0 (8-bit blocks of 32)
+    "q8": Workload("q8", E=128, k=8, H=2048, I=768, T=8, fmt_down=FMT_Q8_0,
+                   extra={"prefill_T": 4096}),
     # 48 stacked mixed layers with 96 of 256 experts resident per layer
     "tiered": Workload("tiered", E=256, k=8, H=2048, I=512, T=8, fmt_down=FMT_Q6K,
                        zipf_s=1.2, zipf_alpha=ZIPF_ALPHA["tiered"],

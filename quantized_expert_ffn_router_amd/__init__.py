@@ -25,6 +25,7 @@ MOE_ERR_HOST_ALLOC = -6
 
 MOE_FMT_NVFP4 = 1
 MOE_FMT_Q6K = 2
+MOE_FMT_Q8_0 = 3
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 

@@ -36,7 +36,7 @@ moe_status check_shape(int E, int k, int H, int I, int fmt_gu, int fmt_down, con
     return fail(MOE_ERR_UNSUPPORTED, "%s: H=%d must be a multiple of 128 and <= 8192", where, H);
   if (fmt_gu != MOE_FMT_NVFP4)
     return fail(MOE_ERR_UNSUPPORTED, "%s: gate/up format %d (only NVFP4)", where, fmt_gu);
-  if (fmt_down == MOE_FMT_NVFP4) {
+  if (fmt_down == MOE_FMT_NVFP4 || fmt_down == MOE_FMT_Q8_0) {
     if (I % 128 != 0 || I > 8192)
       return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d must be a multiple of 128 and <= 8192", where, I);
   } else if (fmt_down == MOE_FMT_Q6K) {
@@ -173,6 +173,12 @@ moe_status moe_pack_experts(int32_t E, int32_t H, int32_t I, int32_t fmt_gate_up
     // down: N = H rows, K = I
     e = moe::launch_pack_granules(down_q, E, (size_t)H * I / 2, H, I / 32, 16, I / 2, 1, 16, 0, d + lay.down_q, blob_stride, stream);
     if (e == hipSuccess) e = moe::launch_pack_granules(down_s, E, (size_t)H * I / 16, H, I / 128, 8, I / 16, 1, 8, 0, d + lay.down_s, blob_stride, stream);
+  } else if (fmt_down == MOE_FMT_Q8_0) {
+    // 34-byte blocks: codes in two 16-byte granules per block, the 4 scales of
+    // a 128-element group gathered into one 8-byte granule
+    const size_t row = (size_t)(I / 32) * 34, ex = (size_t)H * row;
+    e = moe::launch_pack_granules(down_q, E, ex, H, I / 16, 16, row, 2, 34, 2, d + lay.down_q, blob_stride, stream);
+    if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 128, 2, row, 1, 34, 0, d + lay.down_s, blob_stride, stream, 4);
   } else {
     const size_t row = (size_t)(I / 256) * 210, ex = (size_t)H * row;
     e = moe::launch_pack_granules(down_q, E, ex, H, I / 32, 16, row, 8, 210, 0, d + lay.down_ql, blob_stride, stream);

@@ -16,8 +16,13 @@
 //                         64c..64c+63 (superblock c/4, qh bytes 16*(c%4)..);
 //                         sc granule (s, n), s < K/256: the 16 int8 sub-scales;
 //                         d  granule (s, n), s < K/256: the fp16 scale (2 bytes).
+//   Q8_0 matrix [N][K]:   codes  granule (c, n), c < K/16, 16 bytes = the int8
+//                         codes of elements 16c..16c+15 (block c/2, code
+//                         bytes 16*(c%2)..);
+//                         scales granule (g, n), g < K/128, 8 bytes = the fp16
+//                         scales of blocks 4g..4g+3.
 //
-// Blob = gate, up (NVFP4, [I][H]) then down ([H][I], NVFP4 or Q6_K); each
+// Blob = gate, up (NVFP4, [I][H]) then down ([H][I], NVFP4, Q6_K or Q8_0); each
 // section starts on a 256-byte boundary.
 #pragma once
 
@@ -34,7 +39,7 @@ inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a
 
 struct BlobLayout {
   size_t gate_q, gate_s, up_q, up_s;
-  size_t down_q, down_s;             // NVFP4 down
+  size_t down_q, down_s;             // NVFP4 or Q8_0 down
   size_t down_ql, down_qh, down_sc, down_d;  // Q6_K down
   size_t total;
 };
@@ -53,6 +58,9 @@ inline BlobLayout blob_layout(int64_t H, int64_t I, int fmt_down) {
   b.up_s = take((size_t)I * H / 16);
   if (fmt_down == MOE_FMT_NVFP4) {
     b.down_q = take((size_t)H * I / 2);
+    b.down_s = take((size_t)H * I / 16);
+  } else if (fmt_down == MOE_FMT_Q8_0) {
+    b.down_q = take((size_t)H * I);
     b.down_s = take((size_t)H * I / 16);
   } else {
     b.down_ql = take((size_t)H * I / 2);
@@ -107,7 +115,7 @@ namespace moe {
 hipError_t launch_pack_granules(const uint8_t* src, int E, size_t src_expert_stride,
                                 int64_t N, int64_t G, int gsz, size_t row_stride,
                                 int per_sb, size_t sb_stride, size_t inner, uint8_t* dst,
-                                size_t dst_expert_stride, hipStream_t s);
+                                size_t dst_expert_stride, hipStream_t s, int pieces = 1);
 
 hipError_t launch_router(const uint16_t* x, int64_t T, int H, const float* Wr,
                          const float* bias, int E, float* logits, hipStream_t s);

@@ -322,6 +322,73 @@ __device__ __forceinline__ v8h_t dequant_frag_q6k_h(const FragQ6k& f) {
   return r;
 }
 
+// Q8_0: a lane group's 32 values of a K step are exactly one block of 32
+// (block 4 * step + lane/16), so one fp16 scale per fragment.
+struct FragQ8 {
+  uint4 lo, hi;  // the block's 32 int8 codes: sub-steps 0, 1 in lo, 2, 3 in hi
+  uint32_t sc;   // fp16 scale d (low 16 bits)
+};
+
+__device__ __forceinline__ void load_frag_q8(FragQ8& f, const uint8_t* q, const uint8_t* sc, int N,
+                                             int n, int step) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  const int c = 4 * step + grp;  // block of 32
+  f.lo = gl16(q + ((size_t)(2 * c) * N + n) * 16);
+  f.hi = gl16(q + ((size_t)(2 * c + 1) * N + n) * 16);
+  f.sc = gl2(sc + ((size_t)step * N + n) * 8 + 2 * grp);
+}
+
+template <int S>
+__device__ __forceinline__ void q8_words(const FragQ8& f, uint32_t& w0, uint32_t& w1) {
+  const uint4& v = S < 2 ? f.lo : f.hi;
+  w0 = (S & 1) ? v.z : v.x;
+  w1 = (S & 1) ? v.w : v.y;
+}
+
+template <int S>
+__device__ __forceinline__ v8bf_t dequant_frag_q8(const FragQ8& f) {
+  const float d = f16_to_f32((uint16_t)(f.sc & 0xffffu));
+  uint32_t w[2];
+  q8_words<S>(f, w[0], w[1]);
+  v8bf_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t v = w[p >> 1] >> (16 * (p & 1));
+    const v2bf_t b = to_v2bf((float)(int8_t)v * d, (float)(int8_t)(v >> 8) * d);
+    r[2 * p] = b[0];
+    r[2 * p + 1] = b[1];
+  }
+  return r;
+}
+
+// fp16 path: the codes, offset to unsigned bytes u = q + 128, are placed by
+// one byte permute under the fp16 exponent of 1024 (0x64: 1024 + u exactly),
+// one packed add leaves q and one packed multiply applies d * 2^4 (d is fp16,
+// so exact), rounding the product once.  The 2^4 keeps weights down to about
+// 2^-17 clear of fp16 subnormals; the epilogue takes it out.  Range: the
+// fp16 product needs |w| < 4096.
+constexpr float kQ8Pre = 16.0f;
+template <int S>
+__device__ __forceinline__ v8h_t dequant_frag_q8_h(const FragQ8& f) {
+  const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(f.sc & 0xffffu)) * (_Float16)kQ8Pre;
+  const v2h_t ds = {dh, dh};
+  const v2h_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  uint32_t w[2];
+  q8_words<S>(f, w[0], w[1]);
+  v8h_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t u = w[p >> 1] ^ 0x80808080u;
+    const uint32_t b0 = 2 * (p & 1);
+    // bytes [u.b0, 0x64, u.b0+1, 0x64] (selector 0..3: u, 4: 0x64)
+    const uint32_t raw = __builtin_amdgcn_perm(0x64646464u, u, 0x04000400u | b0 | ((b0 + 1) << 16));
+    const v2h_t v = (__builtin_bit_cast(v2h_t, raw) + off) * ds;
+    r[2 * p] = v[0];
+    r[2 * p + 1] = v[1];
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- main loop
 // Persistent workgroups of 8 waves.  A tile is 128 token rows x 8*NC*16
 // columns; wave w owns all 128 rows and column tiles j < NC (NC = 2: 64
@@ -361,12 +428,15 @@ struct Planes {
 };
 
 template <int FMT>
-using FragOf = typename std::conditional<FMT == MOE_FMT_NVFP4, FragNvfp4, FragQ6k>::type;
+using FragOf = typename std::conditional<
+    FMT == MOE_FMT_NVFP4, FragNvfp4,
+    typename std::conditional<FMT == MOE_FMT_Q8_0, FragQ8, FragQ6k>::type>::type;
 
 template <int FMT>
 __device__ __forceinline__ void load_b_tile(FragOf<FMT>& f, const Planes& P, int N, int n,
                                             int step) {
   if constexpr (FMT == MOE_FMT_NVFP4) load_frag(f, P.p[0], P.p[1], N, n, step);
+  else if constexpr (FMT == MOE_FMT_Q8_0) load_frag_q8(f, P.p[0], P.p[1], N, n, step);
   else load_frag_q6k(f, P.p[0], P.p[1], P.p[2], P.p[3], N, n, step);
 }
 
@@ -414,6 +484,9 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
       if constexpr (FMT == MOE_FMT_NVFP4) {  // scales of both tiles paired in bcur[0]
         bf[0] = dequant_frag_h<S, 0>(bcur[0], bcur[0].scale);
         bf[1] = dequant_frag_h<S, 1>(bcur[1], bcur[0].scale);
+      } else if constexpr (FMT == MOE_FMT_Q8_0) {
+        bf[0] = dequant_frag_q8_h<S>(bcur[0]);
+        bf[1] = dequant_frag_q8_h<S>(bcur[1]);
       } else {
         bf[0] = dequant_frag_q6k_h<S>(bcur[0]);
         bf[1] = dequant_frag_q6k_h<S>(bcur[1]);
@@ -442,6 +515,7 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         if constexpr (FMT == MOE_FMT_NVFP4) bf[j] = dequant_frag<S>(bcur[j]);
+        else if constexpr (FMT == MOE_FMT_Q8_0) bf[j] = dequant_frag_q8<S>(bcur[j]);
         else bf[j] = dequant_frag_q6k<S>(bcur[j]);
       }
 #pragma unroll
@@ -694,7 +768,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nsteps = I / GBK;
-  constexpr int kB = (FMT == MOE_FMT_NVFP4) ? 2 : 4;  // weight loads per column tile
+  constexpr int kB = (FMT == MOE_FMT_NVFP4) ? 2 : (FMT == MOE_FMT_Q8_0 ? 3 : 4);  // weight loads per column tile
 
   auto rows_of = [&](const TileRec& t, uint32_t (&off)[4]) {
 #pragma unroll
@@ -793,7 +867,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // Epilogue: lane holds row 16i + lane%16, columns cb + 16j + 4*(lane/16) .. +4.
     // bf16: the two column tiles are swapped between lane groups so that
     // group g stores columns cb + 8*(g/2) + 16*(g%2) .. +8 of its row.
-    const float ts = (FMT == MOE_FMT_NVFP4) ? cur.ref.ts_down : 1.0f;
+    const float ts = (FMT == MOE_FMT_NVFP4)  ? cur.ref.ts_down
+                     : (FMT == MOE_FMT_Q8_0) ? (AF16 ? 1.0f / kQ8Pre : 1.0f)
+                                             : 1.0f;
     const int grp = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -884,6 +960,17 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
     } else {
       DOWN(MOE_FMT_NVFP4, false, true, 1, q, sc, z, z);
       DOWN(MOE_FMT_NVFP4, false, false, 2, q, sc, z, z);
+    }
+  } else if (L->fmt_down == MOE_FMT_Q8_0) {
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<true, false>), grid, block, 0, s, GU_ARGS);
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<false, true>), grid, block, 0, s, GU_ARGS);
+    const size_t q = lay.down_q, sc = lay.down_s, z = 0;
+    if (bf) {
+      DOWN(MOE_FMT_Q8_0, true, true, 1, q, sc, z, z);
+      DOWN(MOE_FMT_Q8_0, true, false, 2, q, sc, z, z);
+    } else {
+      DOWN(MOE_FMT_Q8_0, false, true, 1, q, sc, z, z);
+      DOWN(MOE_FMT_Q8_0, false, false, 2, q, sc, z, z);
     }
   } else {
     hipLaunchKernelGGL((k_gemm_gateup_nvfp4<true, false>), grid, block, 0, s, GU_ARGS);

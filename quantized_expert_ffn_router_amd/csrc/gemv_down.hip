@@ -5,8 +5,10 @@
 //     256-element superblocks, 6-bit codes q in a low-nibble plane and a
 //     2-bit plane, int8 sub-scale per 16 elements, fp16 scale d:
 //     w = d * sc * (q - 32).
+//   Q8_0 (the 8-bit GGUF blocks of basalt.jgulfo.com, "All the numbers"):
+//     32-element blocks, fp16 scale d, int8 codes q: w = d * q.
 // Weights are decoded exactly to bf16 (E2M1 has 2 significant bits, q - 32 is
-// a 6-bit integer) and meet h (bf16, from the gate/up kernel) in
+// a 6-bit integer, an int8 code has at most 8) and meet h (bf16, from the gate/up kernel) in
 // v_dot2_f32_bf16 with fp32 accumulation.  Each 16-element block sum is scaled
 // by its block scale (E4M3, or d * sc).  A workgroup owns 64 rows of one
 // active expert; its S waves split K into 128-element groups (gemv_common.h),
@@ -41,9 +43,15 @@ struct Group<MOE_FMT_Q6K> {
   uint32_t d;   // fp16 superblock scale
 };
 
+template <>
+struct Group<MOE_FMT_Q8_0> {
+  uint4 c[8];  // 128 int8 codes, 16 per granule
+  uint2 s;     // fp16 scales of the group's 4 blocks of 32
+};
+
 struct Planes {
-  const uint8_t* a;  // NVFP4 codes | Q6_K ql
-  const uint8_t* b;  // NVFP4 scales | Q6_K qh
+  const uint8_t* a;  // NVFP4 codes | Q6_K ql | Q8_0 codes
+  const uint8_t* b;  // NVFP4 scales | Q6_K qh | Q8_0 scales
   const uint8_t* c;  // Q6_K sc
   const uint8_t* d;  // Q6_K d
 };
@@ -64,6 +72,13 @@ __device__ __forceinline__ void load_group(Group<MOE_FMT_Q6K>& r, const Planes& 
   for (int q = 0; q < 2; ++q) r.qh[q] = ld16(P.b + (((size_t)(2 * g + q)) * H + nc) * 16);
   r.sc = ld8(P.c + ((size_t)sb * H + nc) * 16 + 8 * half);
   r.d = ld2(P.d + ((size_t)sb * H + nc) * 2);
+}
+
+__device__ __forceinline__ void load_group(Group<MOE_FMT_Q8_0>& r, const Planes& P, int H,
+                                           size_t nc, int g) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) r.c[q] = ld16(P.a + (((size_t)(8 * g + q)) * H + nc) * 16);
+  r.s = ld8(P.b + ((size_t)g * H + nc) * 8);
 }
 
 // Exact bf16 pairs w[b][0..8) of the 8 blocks of 16 and their fp32 scales.
@@ -116,6 +131,27 @@ __device__ __forceinline__ void decode_group(const Group<MOE_FMT_Q6K>& r, float 
   }
 }
 
+// Half hf of a Q8_0 group: the 4 blocks of 16 codes 4hf..4hf+3 as exact bf16
+// pairs (an int8 is exact in bf16) and their fp32 scales (block 2b covers
+// blocks of 16 2b, 2b + 1).  A signed byte converts to float in one
+// sub-dword conversion.
+template <int HF>
+__device__ __forceinline__ void decode_half_q8(const Group<MOE_FMT_Q8_0>& r, v2bf_t (*w)[8],
+                                               float* sc) {
+  const uint32_t dw = HF ? r.s.y : r.s.x;
+  sc[0] = sc[1] = f16_to_f32((uint16_t)(dw & 0xffffu));
+  sc[2] = sc[3] = f16_to_f32((uint16_t)(dw >> 16));
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t v = word_of(r.c[4 * HF + b], i >> 1);
+      const int sh = 16 * (i & 1);
+      w[b][i] = to_v2bf((float)(int8_t)(v >> sh), (float)(int8_t)(v >> (sh + 8)));
+    }
+  }
+}
+
 // Issue the loads of the first D groups of a pass.
 template <int FMT, int GP, int D>
 __device__ __forceinline__ void dn_issue(Group<FMT> (&r)[GP], const Planes& P, int H, size_t nc,
@@ -144,24 +180,53 @@ __device__ __forceinline__ void dn_consume(Group<FMT> (&r)[GP], const uint16_t* 
       __builtin_amdgcn_sched_barrier(0);
     }
     const int g = gb + gi;
-    v2bf_t w[8][8];
-    float sc[8];
-    decode_group(r[gi], ts, w, sc);
+    if constexpr (FMT == MOE_FMT_Q8_0) {
+      // Half a group at a time (the decoded group would not fit beside the
+      // next group's 136 bytes in flight).
+      auto half = [&](auto HF_) {
+        constexpr int HF = decltype(HF_)::value;
+        v2bf_t w[4][8];
+        float sc[4];
+        decode_half_q8<HF>(r[gi], w, sc);
 #pragma unroll 1
-    for (int t = 0; t < mt; ++t) {
-      const uint32_t* hp = reinterpret_cast<const uint32_t*>(h + (size_t)(p0 + t) * I) + 64 * g;
-      float a = 0.0f;
+        for (int t = 0; t < mt; ++t) {
+          const uint32_t* hp =
+              reinterpret_cast<const uint32_t*>(h + (size_t)(p0 + t) * I) + 64 * g + 32 * HF;
+          float a = 0.0f;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        float p = 0.0f;
+          for (int b = 0; b < 4; ++b) {
+            float p = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          p = __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(hp[8 * b + i]), w[b][i], p, false);
-        a = fmaf(p, sc[b], a);
+            for (int i = 0; i < 8; ++i)
+              p = __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(hp[8 * b + i]), w[b][i], p, false);
+            a = fmaf(p, sc[b], a);
+          }
+          acc[t * 64 + lane] += a;
+        }
+      };
+      half(std::integral_constant<int, 0>{});
+      half(std::integral_constant<int, 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      v2bf_t w[8][8];
+      float sc[8];
+      decode_group(r[gi], ts, w, sc);
+#pragma unroll 1
+      for (int t = 0; t < mt; ++t) {
+        const uint32_t* hp = reinterpret_cast<const uint32_t*>(h + (size_t)(p0 + t) * I) + 64 * g;
+        float a = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          float p = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            p = __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(hp[8 * b + i]), w[b][i], p, false);
+          a = fmaf(p, sc[b], a);
+        }
+        acc[t * 64 + lane] += a;
       }
-      acc[t * 64 + lane] += a;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -237,7 +302,7 @@ hipError_t down_t(const moe_layer_desc* L, const uint16_t* h, const moe_buckets*
   constexpr int D = GP < 2 ? GP : 2;
   const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
   Planes P;
-  if (FMT == MOE_FMT_NVFP4) {
+  if (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_Q8_0) {
     P = {(const uint8_t*)lay.down_q, (const uint8_t*)lay.down_s, nullptr, nullptr};
   } else {
     P = {(const uint8_t*)lay.down_ql, (const uint8_t*)lay.down_qh, (const uint8_t*)lay.down_sc,
@@ -266,11 +331,11 @@ hipError_t down_fmt(const moe_layer_desc* L, const uint16_t* h, const moe_bucket
   for (int c = 2; c <= 8; ++c)
     if (NG % c == 0 && NG / c >= 2) S = c;
   const int gps_total = NG / S;
-  const int gp_max = (FMT == MOE_FMT_Q6K) ? 2 : 4;  // register budget (no spills)
+  const int gp_max = (FMT == MOE_FMT_NVFP4) ? 4 : 2;  // register budget (no spills)
   int GP = gps_total > gp_max ? gp_max : gps_total;
   while (gps_total % GP) --GP;
   if (GP == 1) return down_t<FMT, 1>(L, h, b, max_slots, S, gps_total, y, y_dtype, s);
-  if constexpr (FMT == MOE_FMT_Q6K) {
+  if constexpr (FMT != MOE_FMT_NVFP4) {
     return down_t<FMT, 2>(L, h, b, max_slots, S, gps_total, y, y_dtype, s);
   } else {
     switch (GP) {
@@ -286,6 +351,7 @@ hipError_t down_fmt(const moe_layer_desc* L, const uint16_t* h, const moe_bucket
 hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const moe_buckets* b,
                             int max_slots, void* y, int y_dtype, hipStream_t s) {
   if (L->fmt_down == MOE_FMT_Q6K) return down_fmt<MOE_FMT_Q6K>(L, h, b, max_slots, y, y_dtype, s);
+  if (L->fmt_down == MOE_FMT_Q8_0) return down_fmt<MOE_FMT_Q8_0>(L, h, b, max_slots, y, y_dtype, s);
   return down_fmt<MOE_FMT_NVFP4>(L, h, b, max_slots, y, y_dtype, s);
 }
 

@@ -81,6 +81,7 @@ def test_buckets_carve_layout_on_host_buffer():
     (dict(H=200), q.MOE_ERR_UNSUPPORTED, "H=200"),
     (dict(I=100), q.MOE_ERR_UNSUPPORTED, "I=100"),
     (dict(I=384, fmt_down=2), q.MOE_ERR_UNSUPPORTED, "Q6_K"),
+    (dict(I=96, fmt_down=3), q.MOE_ERR_UNSUPPORTED, "I=96"),
     (dict(fmt_down=7), q.MOE_ERR_UNSUPPORTED, "down format"),
     (dict(renorm=2), q.MOE_ERR_INVALID_ARG, "renormalize"),
 ])
@@ -114,6 +115,21 @@ def test_zero_tokens_is_a_noop_and_null_checks():
     assert lib.moe_expert_ffn(ctypes.byref(d), 0x10, 4, ctypes.byref(b), 0x20, 5, 0x30, 1 << 20, None) == q.MOE_ERR_INVALID_ARG
     # histogram shift range
     assert lib.moe_expert_hist(ctypes.byref(d), ctypes.byref(b), 0x10, 40, 10, None) == q.MOE_ERR_INVALID_ARG
+
+
+def test_blob_bytes_per_down_format():
+    """Sections start on 256-byte boundaries: gate and up (NVFP4 codes and
+    scales), then the down projection's planes."""
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    H, I = 2048, 768
+    gu = 2 * (al(I * H // 2) + al(I * H // 16))
+    assert q.moe_expert_blob_bytes(H, I, 1, 1) == gu + al(H * I // 2) + al(H * I // 16)
+    assert q.moe_expert_blob_bytes(H, I, 1, 3) == gu + al(H * I) + al(H * I // 16)
+    I = 512
+    gu = 2 * (al(I * H // 2) + al(I * H // 16))
+    assert q.moe_expert_blob_bytes(H, I, 1, 2) == gu + al(H * I // 2) + al(H * I // 4) + \
+        al(H * I // 16) + al(H * I // 128)
+    assert q.moe_expert_blob_bytes(H, 96, 1, 3) == 0
 
 
 def test_workspace_bytes_cover_hidden_buffers():

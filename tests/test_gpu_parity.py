@@ -163,12 +163,44 @@ def test_mixed_prefill_q6k_down_sampled():
     check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
 
 
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_q8_0_decode_parity(B):
+    """The decode layer with a Q8_0 down projection: dequant-fused GEMV."""
+    w, L = layer("q8")
+    x = moegen.make_tokens(w, B, step=B + 1)
+    print("q8 decode B", B, flush=True)
+    check_layer(L, x)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_q8_0_both_ffn_families_ragged(mode):
+    # 600 tokens x top-8 over 64 experts, I = 384 (3 groups of 128, 3 K steps
+    # of the GEMM): GEMV (mode 1) and grouped GEMM (mode 2) against the oracle.
+    w, L = layer("q8_many", E=64, k=8, H=256, I=384, T=600, fmt_down=moegen.FMT_Q8_0)
+    x = moegen.make_tokens(w, w.T, step=6)
+    res = moegen.make_residual(w, w.T)
+    print("q8 ragged mode", mode, flush=True)
+    check_layer(L, x, residual=res, tokens=list(range(0, 600, 5)), ffn_mode=mode,
+                y_rel=GEMM_Y_REL)
+
+
+def test_q8_0_prefill_sampled():
+    """4096-token prefill of the Q8_0 layer on the grouped GEMM path."""
+    w, L = layer("q8")
+    x = moegen.make_tokens(w, 4096, step=2)
+    print("q8 prefill", flush=True)
+    check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
+
+
 @pytest.mark.parametrize("x_std,w_std,fmt_down", [
     (3e5, 0.02, 1),   # token rows beyond the fp16 range: per-row scaled fp16 copy
     (1e-3, 0.02, 1),  # small activations: h scaled by the token's row scale
     (1.0, 4.0, 1),    # |h| beyond fp16 even after scaling: bf16 recompute
     (1e-3, 0.02, 2),  # the same with the Q6_K-style down projection
     (1.0, 4.0, 2),
+    (3e5, 0.02, 3),   # the same with Q8_0
+    (1e-3, 0.02, 3),
+    (1.0, 4.0, 3),
 ])
 def test_gemm_activation_magnitudes(x_std, w_std, fmt_down):
     """The grouped GEMM multiplies fp16 operands; the token rows and h carry
