@@ -15,11 +15,11 @@
 //   - per K step of 128: the A tile (token rows, or h rows for the down
 //     projection) is copied global -> LDS by the load unit; each wave loads
 //     its B fragments from the packed weight blob (one 16-byte granule per
-//     lane and column tile, see "B fragments") and dequantizes them in
-//     registers;
+//     lane and column tile for NVFP4, see "B fragments"; more for Q6_K and
+//     Q8_0) and dequantizes them in registers;
 //   - operands are fp16 (NVFP4 weights are exact in fp16; token rows carry
-//     an exact per-row power-of-two scale, see k_rows_to_f16) except for the
-//     Q6_K down projection and the bf16 recompute path, which use bf16;
+//     an exact per-row power-of-two scale, see k_rows_to_f16; Q6_K and Q8_0
+//     weights are rounded once to fp16) except for the bf16 recompute path;
 //   - 8 waves, each 128 rows x 32 columns = 8 x 2 v_mfma_f32_16x16x32 tiles
 //     with fp32 accumulation;
 //   - gate/up: each wave's two column tiles are the same 16 rows of gate and
@@ -338,6 +338,23 @@ __device__ __forceinline__ void load_frag_q8(FragQ8& f, const uint8_t* q, const 
   f.sc = gl2(sc + ((size_t)step * N + n) * 8 + 2 * grp);
 }
 
+// Both column tiles n and n + 16 of the fp16 path; their scales share
+// f[0].sc (tile j in the 16-bit half j), one register fewer per step.
+__device__ __forceinline__ void load_frag_q8_pair(FragQ8 (&f)[2], const uint8_t* q,
+                                                  const uint8_t* sc, int N, int n, int step) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  const int c = 4 * step + grp;
+  const uint8_t* p0 = q + ((size_t)(2 * c) * N + n) * 16;
+  const uint8_t* p1 = q + ((size_t)(2 * c + 1) * N + n) * 16;
+  f[0].lo = gl16(p0);
+  f[0].hi = gl16(p1);
+  f[1].lo = gl16(p0 + 16 * 16);
+  f[1].hi = gl16(p1 + 16 * 16);
+  const uint8_t* ps = sc + ((size_t)step * N + n) * 8 + 2 * grp;
+  f[0].sc = gl2(ps) | (gl2(ps + 16 * 8) << 16);
+  f[1].sc = 0;
+}
+
 template <int S>
 __device__ __forceinline__ void q8_words(const FragQ8& f, uint32_t& w0, uint32_t& w1) {
   const uint4& v = S < 2 ? f.lo : f.hi;
@@ -368,9 +385,9 @@ __device__ __forceinline__ v8bf_t dequant_frag_q8(const FragQ8& f) {
 // 2^-17 clear of fp16 subnormals; the epilogue takes it out.  Range: the
 // fp16 product needs |w| < 4096.
 constexpr float kQ8Pre = 16.0f;
-template <int S>
-__device__ __forceinline__ v8h_t dequant_frag_q8_h(const FragQ8& f) {
-  const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(f.sc & 0xffffu)) * (_Float16)kQ8Pre;
+template <int S, int J>
+__device__ __forceinline__ v8h_t dequant_frag_q8_h(const FragQ8& f, uint32_t sc2) {
+  const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(sc2 >> (16 * J))) * (_Float16)kQ8Pre;
   const v2h_t ds = {dh, dh};
   const v2h_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   uint32_t w[2];
@@ -485,8 +502,8 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
         bf[0] = dequant_frag_h<S, 0>(bcur[0], bcur[0].scale);
         bf[1] = dequant_frag_h<S, 1>(bcur[1], bcur[0].scale);
       } else if constexpr (FMT == MOE_FMT_Q8_0) {
-        bf[0] = dequant_frag_q8_h<S>(bcur[0]);
-        bf[1] = dequant_frag_q8_h<S>(bcur[1]);
+        bf[0] = dequant_frag_q8_h<S, 0>(bcur[0], bcur[0].sc);
+        bf[1] = dequant_frag_q8_h<S, 1>(bcur[1], bcur[0].sc);
       } else {
         bf[0] = dequant_frag_q6k_h<S>(bcur[0]);
         bf[1] = dequant_frag_q6k_h<S>(bcur[1]);
@@ -497,11 +514,14 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
       // A fragments are read one row tile ahead of their MFMAs; the fences
       // keep the compiler from serializing read -> wait -> MFMA under the
       // 128-register budget of 4 waves per SIMD.
+      // (Q8_0 fragments take 9 registers per column tile: no A read-ahead,
+      // which would push the K loop into spills.)
+      constexpr bool kPre = FMT != MOE_FMT_Q8_0;
       v8h_t an = *reinterpret_cast<const v8h_t*>(Ab + aswz(r, cq + S));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const v8h_t af = an;
-        if (i + 1 < 8) an = *reinterpret_cast<const v8h_t*>(Ab + aswz(16 * (i + 1) + r, cq + S));
+        const v8h_t af = kPre ? an : *reinterpret_cast<const v8h_t*>(Ab + aswz(16 * i + r, cq + S));
+        if (kPre && i + 1 < 8) an = *reinterpret_cast<const v8h_t*>(Ab + aswz(16 * (i + 1) + r, cq + S));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NC; ++j)
@@ -803,6 +823,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (AF16 && FMT == MOE_FMT_NVFP4) {
     load_frag_pair(bnext, P.p[0], P.p[1], H, cb, 0, bl);
+  } else if constexpr (AF16 && FMT == MOE_FMT_Q8_0) {
+    load_frag_q8_pair(bnext, P.p[0], P.p[1], H, cb + (lane & 15), 0);
   } else {
     load_b_tile<FMT>(bnext[0], P, H, cb + (lane & 15), 0);
     load_b_tile<FMT>(bnext[1], P, H, cb + 16 + (lane & 15), 0);
@@ -839,7 +861,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       step_mfma<FMT, 2, AF16>(bcur, As + buf * GBM * ARB, lane, acc, [&](auto S_) {
         constexpr int S = decltype(S_)::value;
         if (!ld) return;
-        if constexpr (AF16) {  // spread over the step (see gate/up)
+        if constexpr (AF16 && FMT == MOE_FMT_Q8_0) {
+          // weights after sub-step 1's dequant, when this step's first 16
+          // codes are dead: 8 registers fewer live (the compiler's spills in
+          // the K loop drop from 15 scratch operations to 3)
+          if constexpr (S == 0) load_a_half(h, off, stn * GBK, Anext, wave, lane, 0);
+          else if constexpr (S == 1)
+            load_frag_q8_pair(bnext, P.p[0], P.p[1], H, cbl + (lane & 15), stn);
+          else if constexpr (S == 2) load_a_half(h, off, stn * GBK, Anext, wave, lane, 1);
+        } else if constexpr (AF16) {  // spread over the step (see gate/up)
           if constexpr (S == 0) {
             if constexpr (FMT == MOE_FMT_NVFP4) {
               load_frag_pair(bnext, P.p[0], P.p[1], H, cbl, stn, bl);
