@@ -514,9 +514,9 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
       // A fragments are read one row tile ahead of their MFMAs; the fences
       // keep the compiler from serializing read -> wait -> MFMA under the
       // 128-register budget of 4 waves per SIMD.
-      // (Q8_0 fragments take 9 registers per column tile: no A read-ahead,
-      // which would push the K loop into spills.)
-      constexpr bool kPre = FMT != MOE_FMT_Q8_0;
+      // (Q8_0 and Q6_K fragments take 9 and 7 registers per column tile: no
+      // A read-ahead, which would push more of the K loop into spills.)
+      constexpr bool kPre = FMT == MOE_FMT_NVFP4;
       v8h_t an = *reinterpret_cast<const v8h_t*>(Ab + aswz(r, cq + S));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -869,6 +869,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
           else if constexpr (S == 1)
             load_frag_q8_pair(bnext, P.p[0], P.p[1], H, cbl + (lane & 15), stn);
           else if constexpr (S == 2) load_a_half(h, off, stn * GBK, Anext, wave, lane, 1);
+        } else if constexpr (AF16 && FMT == MOE_FMT_Q6K) {  // the same schedule
+          if constexpr (S == 0) load_a_half(h, off, stn * GBK, Anext, wave, lane, 0);
+          else if constexpr (S == 1) {
+            load_b_tile<FMT>(bnext[0], P, H, cbl + (lane & 15), stn);
+            load_b_tile<FMT>(bnext[1], P, H, cbl + 16 + (lane & 15), stn);
+          } else if constexpr (S == 2) load_a_half(h, off, stn * GBK, Anext, wave, lane, 1);
         } else if constexpr (AF16) {  // spread over the step (see gate/up)
           if constexpr (S == 0) {
             if constexpr (FMT == MOE_FMT_NVFP4) {
