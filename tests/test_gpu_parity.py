@@ -8,7 +8,7 @@ import pytest
 
 import moegen
 import oracle
-from parity_util import check_buckets, check_layer, check_route, rel_l2, run_gpu
+from parity_util import Y_REL, check_buckets, check_layer, check_route, rel_l2, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +93,32 @@ def test_more_than_eight_experts_per_token(T):
 # The grouped GEMM rounds h (and Q6_K weights) to bf16 before the MFMAs, so
 # its fp32 expert outputs are compared at the layer tolerance (rel L2 5e-3).
 GEMM_Y_REL = 5e-3
+
+
+@pytest.mark.parametrize("fmt_down,mode", [(1, 1), (1, 2), (2, 1), (2, 2), (3, 1), (3, 2)])
+def test_largest_hidden_and_intermediate(fmt_down, mode):
+    """H = I = 8192, the largest supported sizes, with each down format: the
+    decode GEMVs split K over 4 (gate/up, 16 groups a wave) and 8 (down)
+    waves; the grouped GEMM runs 64 K steps and 32 down column tiles.  The
+    weights' std is halved against the 2048-wide layers (scaled like
+    1/sqrt(fan-in)) so the outputs stay near unit scale, where the absolute
+    bar of 2e-2 is above one bf16 ulp of the output."""
+    w, L = layer("maxhi", E=2, k=2, H=8192, I=8192, T=3, fmt_down=fmt_down, w_std=0.01)
+    x = moegen.make_tokens(w, w.T)
+    print("maxhi", fmt_down, mode, flush=True)
+    check_layer(L, x, ffn_mode=mode, y_rel=GEMM_Y_REL if mode == 2 else Y_REL)
+
+
+@pytest.mark.parametrize("T,mode", [(5, 0), (70, 1), (70, 2)])
+def test_most_experts_and_largest_top_k(T, mode):
+    """E = 1024 and k = 64, the largest supported: the iterative top-k over
+    1024 logits, 64 assignments per token in the combine (8 groups of 8) and,
+    at 70 tokens, 4480 assignments over ~1000 active experts."""
+    w, L = layer("maxe", E=1024, k=64, H=256, I=128, T=70)
+    x = moegen.make_tokens(w, T, step=T)
+    print("maxe", T, mode, flush=True)
+    check_layer(L, x, residual=moegen.make_residual(w, T), ffn_mode=mode,
+                y_rel=GEMM_Y_REL if mode == 2 else Y_REL)
 
 
 def test_prefill_routing_full_size_and_sampled_outputs():
