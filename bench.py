@@ -264,7 +264,7 @@ def main():
             "weights": "nvfp4", "layers_cycled": N_LAYERS, "hip_graph": True,
         },
         "roofline": {
-            "kernel": "expert FFN (k_gemv_gateup_nvfp4 + k_gemv_down_nvfp4)",
+            "kernel": "expert FFN (k_gemv_gateup_nvfp4<4, 2> + k_gemv_down<1, 2, 2, false>, NVFP4)",
             "bound": "hbm",
             "achieved": round(head["ffn_GBps"], 1),
             "peak": HBM_PEAK_GBS,
@@ -329,7 +329,7 @@ def measure_prefill(args, q, moegen, torch, dev):
         "steps": n, "layer_ms": round(layer_ms, 4), "tok_per_s": round(T / (layer_ms * 1e-3), 1),
         "route_bucket_ms": round(route_ms, 4), "ffn_ms": round(ffn_ms, 4),
         "ffn_tflops": round(tflops, 2),
-        "roofline": {"kernel": "grouped GEMM (k_gemm_gateup_nvfp4 + k_gemm_down)", "bound": "mfma",
+        "roofline": {"kernel": "grouped GEMM (k_gemm_gateup_nvfp4<true, false> + k_gemm_down<1, true, true, 1>, NVFP4)", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("prefill_ffn")},
