@@ -326,10 +326,11 @@ hipError_t down_fmt(const moe_layer_desc* L, const uint16_t* h, const moe_bucket
                     int max_slots, void* y, int y_dtype, hipStream_t s) {
   const int NG = L->I / 128;
   // One row block of 64 rows per workgroup; S waves split K (the largest
-  // divisor of NG up to 8 that leaves each wave at least two groups).
+  // divisor of NG up to 8 that leaves each wave at least two groups; Q6_K,
+  // whose decode is VALU-heavy, takes one group per wave up to NG = 4).
   int S = 1;
   for (int c = 2; c <= 8; ++c)
-    if (NG % c == 0 && NG / c >= 2) S = c;
+    if (NG % c == 0 && (NG / c >= 2 || (FMT == MOE_FMT_Q6K && NG <= 4))) S = c;
   const int gps_total = NG / S;
   const int gp_max = (FMT == MOE_FMT_NVFP4) ? 4 : 2;  // register budget (no spills)
   int GP = gps_total > gp_max ? gp_max : gps_total;
