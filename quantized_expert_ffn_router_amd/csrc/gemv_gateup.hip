@@ -109,14 +109,14 @@ __device__ __forceinline__ void gu_consume(GURing<GPS>& R, const uint16_t* __res
   }
 }
 
-template <int GPS, int D>
-__global__ __launch_bounds__(512) void k_gemv_gateup_nvfp4(
+template <int GPS, int D, int W>
+__global__ __launch_bounds__(64 * W) void k_gemv_gateup_nvfp4(
     const uint16_t* __restrict__ x, int H, int I, int ktop, int kshift, int S, int gps_total,
     const moe_expert_ref* __restrict__ experts, size_t off_gq, size_t off_gs, size_t off_uq,
     size_t off_us, const uint32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_asg, const int32_t* __restrict__ active,
     const int32_t* __restrict__ n_active, uint16_t* __restrict__ hout) {
-  __shared__ float red[8][kGuMT][64];  // [wave][token][row] partial sums over K
+  __shared__ float red[W][kGuMT][64];  // [wave][token][row] partial sums over K
 
   int e;
   moe_expert_ref ref;
@@ -195,6 +195,9 @@ hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const 
   // each wave takes NG/S groups in passes of GP <= 8 groups.
   int S = 4;
   while (NG % S) --S;
+  // Grids that leave CUs idle (one workgroup of 16 waves per CU) split K
+  // over 8 waves per matrix.
+  if (NG % 8 == 0 && (int64_t)RB * max_slots <= 256) S = 8;
   const int gps_total = NG / S;
   int GP = gps_total;
   if (GP > 8) {
@@ -206,11 +209,17 @@ hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const 
     if ((1 << i) == L->k) kshift = i;
   dim3 grid((unsigned)RB, (unsigned)max_slots);
   dim3 block((unsigned)(2 * S * 64));
-#define GU_LAUNCH(G)                                                                           \
-  hipLaunchKernelGGL((k_gemv_gateup_nvfp4<G, (G < 2 ? G : 2)>), grid, block, 0, s, x, L->H,   \
-                     L->I, L->k, kshift, S, gps_total, L->experts, lay.gate_q, lay.gate_s,     \
-                     lay.up_q, lay.up_s, b->counts, b->offsets, b->sorted_asg, b->active,      \
+#define GU_LAUNCH_W(G, W)                                                                       \
+  hipLaunchKernelGGL((k_gemv_gateup_nvfp4<G, (G < 2 ? G : 2), W>), grid, block, 0, s, x, L->H, \
+                     L->I, L->k, kshift, S, gps_total, L->experts, lay.gate_q, lay.gate_s,      \
+                     lay.up_q, lay.up_s, b->counts, b->offsets, b->sorted_asg, b->active,       \
                      b->n_active, h)
+#define GU_LAUNCH(G)          \
+  if (S == 8) {               \
+    GU_LAUNCH_W(G, 16);       \
+  } else {                    \
+    GU_LAUNCH_W(G, 8);        \
+  }
   switch (GP) {
     case 1: GU_LAUNCH(1); break;
     case 2: GU_LAUNCH(2); break;
@@ -222,6 +231,7 @@ hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const 
     default: GU_LAUNCH(8); break;
   }
 #undef GU_LAUNCH
+#undef GU_LAUNCH_W
   return hipGetLastError();
 }
 
