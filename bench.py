@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--tiered-steps", type=int, default=2048,
                    help="steps of the 48-layer tiered stack (0: skip)")
+    p.add_argument("--tiered-prepare", choices=("async", "sync"), default="async",
+                   help="tier prepare: on the device (moe_tier_prepare_async) or with a host "
+                        "round trip per layer (moe_tier_prepare)")
     p.add_argument("--tiered-sets", type=int, default=4,
                    help="distinct expert-weight sets shared round-robin by the 48 layers")
     p.add_argument("--cpu-sample-steps", type=int, default=12)
@@ -438,7 +441,9 @@ def measure_tiered(args, q, moegen, torch):
                                 W.zipf_alpha)
         return b
 
-    stack = LayerStack(sets, routers, bias, L=Lyr, k=W.k, tiered={"resident": R, "staging": S})
+    stack = LayerStack(sets, routers, bias, L=Lyr, k=W.k,
+                       tiered={"resident": R, "staging": S,
+                               "async": args.tiered_prepare == "async"})
     del sets
     # pinned host -> HBM copy ceiling on this machine (one expert-sized copy stream)
     hb = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
@@ -484,6 +489,7 @@ def measure_tiered(args, q, moegen, torch):
         "workload": "tiered decode: 48 layers x (256 experts, top-8, hidden 2048, intermediate "
                     "512, NVFP4 gate/up, Q6_K down), 96 resident per layer, 8 tokens/step, "
                     "Zipf(1.2) routing drifting every 256 steps",
+        "prepare": args.tiered_prepare,
         "steps": args.tiered_steps, "wall_s": round(wall, 3),
         "tok_per_s": round(T * args.tiered_steps / wall, 2),
         "ms_per_step": round(wall / args.tiered_steps * 1e3, 3),

@@ -298,9 +298,10 @@ moe_status moe_expert_hist(const moe_layer_desc* L, const moe_buckets* b, uint32
  *
  * Ownership: host blobs (pinned, e.g. hipHostMalloc), the HBM pool, the
  * device tables and both streams belong to the caller and must outlive the
- * tier.  The tier owns only host metadata, a few pinned bytes for the active
- * list, the table staging and the copy list, and two events.  A tier is not
- * thread-safe.
+ * tier.  The tier owns host metadata, a few pinned bytes for the active
+ * list, the table staging and the copy list, two events and the device state
+ * of moe_tier_prepare_async (allocated at create, freed by destroy).  A tier
+ * is not thread-safe.
  */
 typedef struct moe_tier_desc {
   int32_t L;                      /* layers */
@@ -336,6 +337,25 @@ moe_status moe_tier_create(const moe_tier_desc* desc, moe_tier** out);
  * MOE_ERR_BUDGET if the step has more misses than staging slots. */
 moe_status moe_tier_prepare(moe_tier* t, int32_t layer, const moe_buckets* b,
                             moe_expert_ref* table_dev, hipStream_t compute);
+
+/* The same on the device, with no host synchronization: two launches on
+ * `compute`, a planning kernel (reads the step's active list and the tier's
+ * device copy of the layer's resident slots, assigns the misses staging slots
+ * in active-list order, writes table_dev and the copy list) and the copy
+ * kernel, which reads the pinned host blobs directly.  So a caller can
+ * enqueue many layers ahead, or capture them in a graph (with
+ * moe_tier_rebalance, which synchronizes, outside it).  Results equal those
+ * of moe_tier_prepare bit for bit.  The tier's device state (base tables,
+ * blob addresses, copy list, counters: about 36 bytes per expert of every
+ * layer) is allocated once by moe_tier_create, when the host blobs are mapped
+ * for the device; otherwise this call returns MOE_ERR_UNSUPPORTED.  Staging
+ * must hold every possible miss: MOE_ERR_BUDGET, before any launch, if
+ * min(E, b->T_max * b->k) > S.  Hit and miss counts are kept on the device and
+ * added by moe_tier_stats_get (synchronize `compute` before reading them).
+ * This call and moe_tier_prepare share the staging slots: do not interleave
+ * them on different streams. */
+moe_status moe_tier_prepare_async(moe_tier* t, int32_t layer, const moe_buckets* b,
+                                  moe_expert_ref* table_dev, hipStream_t compute);
 
 /* Make the R most used experts of `layer` (hist_dev: device uint32 [E], as
  * updated by moe_expert_hist; ties to the lower index) resident, copying the

@@ -102,6 +102,7 @@ SIGNATURES = {
                                          _i32, _vp]),
     "moe_tier_create": (ctypes.c_int, [ctypes.POINTER(TierDesc), ctypes.POINTER(ctypes.c_void_p)]),
     "moe_tier_prepare": (ctypes.c_int, [_vp, _i32, _BP, _vp, _vp]),
+    "moe_tier_prepare_async": (ctypes.c_int, [_vp, _i32, _BP, _vp, _vp]),
     "moe_tier_rebalance": (ctypes.c_int, [_vp, _i32, _vp, _vp]),
     "moe_tier_stats_get": (ctypes.c_int, [_vp, ctypes.POINTER(TierStats), _i32, _vp]),
     "moe_tier_destroy": (None, [_vp]),
@@ -228,6 +229,11 @@ def moe_tier_create(desc: TierDesc) -> int:
 def moe_tier_prepare(tier, layer, buckets, table_dev, stream=None):
     _check(lib().moe_tier_prepare(tier, layer, ctypes.byref(buckets), _ptr(table_dev),
                                   _stream(stream)))
+
+
+def moe_tier_prepare_async(tier, layer, buckets, table_dev, stream=None):
+    _check(lib().moe_tier_prepare_async(tier, layer, ctypes.byref(buckets), _ptr(table_dev),
+                                        _stream(stream)))
 
 
 def moe_tier_rebalance(tier, layer, hist, stream=None):

@@ -9,6 +9,12 @@
 // 2 MB expert reaches about 44 GB/s.  If a host blob is not device-accessible
 // the runtime copies are used instead.  The side stream is ordered against
 // the compute stream with events.
+//
+// The asynchronous prepare does the same on the device, with no host round
+// trip: a planning kernel reads the step's active list and a device copy of
+// the layer's base table (resident experts -> their slots), assigns staging
+// slots to the misses and writes the table and the copy jobs; the copy kernel
+// then runs on the compute stream itself.
 #include <stdio.h>
 #include <string.h>
 
@@ -46,6 +52,16 @@ struct moe_tier {
   TierCopy* h_jobs = nullptr;
   const TierCopy* d_jobs = nullptr;
   const moe_expert_ref* d_h_table = nullptr;
+  // Asynchronous prepare (device memory, allocated at create when the blobs
+  // are mapped): base tables [L*E] (blob = resident slot or NULL), blob
+  // sources [L*E], job list [S] with its count, and hit/miss counters.
+  moe_expert_ref* d_base = nullptr;
+  const uint4** d_src = nullptr;
+  TierCopy* d_ajobs = nullptr;
+  int32_t* d_anjobs = nullptr;
+  unsigned long long* d_counts = nullptr;  // [0] hits, [1] misses
+  moe_expert_ref* h_row = nullptr;         // pinned [E]: base row staging for rebalance
+  uint64_t async_prepares = 0;
   moe_tier_stats st{};
 };
 
@@ -79,6 +95,69 @@ __global__ __launch_bounds__(256) void k_tier_copy(const TierCopy* __restrict__ 
   const size_t b = (size_t)blockIdx.x * per;
   const size_t e = b + per < n16 ? b + per : n16;
   for (size_t i = b + threadIdx.x; i < e; i += 256) j.dst[i] = j.src[i];
+}
+
+// Asynchronous prepare, one workgroup: table_dev = the layer's base row, then
+// each active expert without a resident slot (in active-list order) gets
+// staging slot j, a copy job and its table entry.  Counters: hits, misses.
+__global__ __launch_bounds__(1024) void k_tier_plan(
+    const moe_expert_ref* __restrict__ base, const uint4* const* __restrict__ src,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, int E,
+    uint8_t* __restrict__ staging, size_t eb, moe_expert_ref* __restrict__ table,
+    TierCopy* __restrict__ jobs, int32_t* __restrict__ n_jobs,
+    unsigned long long* __restrict__ counts) {
+  __shared__ int miss_rank[1024];
+  const int tid = threadIdx.x;
+  const int na = *n_active;
+  for (int x = tid; x < E; x += blockDim.x) table[x] = base[x];
+  // misses among the first na active entries, ranked by a block-wide scan
+  const int x = tid < na ? active[tid] : -1;
+  const int miss = (x >= 0 && base[x].blob == nullptr) ? 1 : 0;
+  miss_rank[tid] = miss;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = tid >= off ? miss_rank[tid - off] : 0;
+    __syncthreads();
+    miss_rank[tid] += v;
+    __syncthreads();
+  }
+  // (the scan's barriers also order the base-row writes before the patches)
+  if (miss) {
+    const int j = miss_rank[tid] - 1;
+    uint8_t* dst = staging + (size_t)j * eb;
+    table[x].blob = dst;
+    jobs[j] = TierCopy{src[x], (uint4*)dst};
+  }
+  if (tid == 0) {
+    const int n_miss = miss_rank[1023];
+    *n_jobs = n_miss;
+    counts[0] += (unsigned long long)(na - n_miss);
+    counts[1] += (unsigned long long)n_miss;
+  }
+}
+
+// Copy kernel of the asynchronous prepare: rows blockIdx.y >= *n_jobs exit.
+__global__ __launch_bounds__(256) void k_tier_copy_async(const TierCopy* __restrict__ jobs,
+                                                         const int32_t* __restrict__ n_jobs,
+                                                         size_t n16) {
+  if ((int)blockIdx.y >= *n_jobs) return;
+  const TierCopy j = jobs[blockIdx.y];
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b = (size_t)blockIdx.x * per;
+  const size_t e = b + per < n16 ? b + per : n16;
+  for (size_t i = b + threadIdx.x; i < e; i += 256) j.dst[i] = j.src[i];
+}
+
+// The layer's base row: resident experts -> their slot, the others NULL.
+void fill_base_row(moe_tier* t, int layer, moe_expert_ref* row) {
+  const size_t base = (size_t)layer * t->E;
+  for (int x = 0; x < t->E; ++x) {
+    moe_expert_ref r = t->scales[base + x];
+    const int sl = t->slot_of[base + x];
+    r.blob = sl >= 0 ? slot_ptr(t, layer, sl) : nullptr;
+    r.reserved = 0;
+    row[x] = r;
+  }
 }
 
 // The n jobs in h_jobs (and, with table_dev, the table) host -> HBM on the
@@ -172,6 +251,24 @@ moe_status moe_tier_create(const moe_tier_desc* d, moe_tier** out) {
   }
   t->d_jobs = (const TierCopy*)dj;
   t->d_h_table = (const moe_expert_ref*)dt;
+  if (mapped) {  // device state of the asynchronous prepare
+    const size_t nb = sizeof(moe_expert_ref) * n;
+    std::vector<moe_expert_ref> b0(n);
+    for (int l = 0; l < t->L; ++l) fill_base_row(t, l, b0.data() + (size_t)l * t->E);
+    if ((e = hipMalloc((void**)&t->d_base, nb)) != hipSuccess ||
+        (e = hipMalloc((void**)&t->d_src, sizeof(void*) * n)) != hipSuccess ||
+        (e = hipMalloc((void**)&t->d_ajobs, sizeof(TierCopy) * t->S)) != hipSuccess ||
+        (e = hipMalloc((void**)&t->d_anjobs, sizeof(int32_t))) != hipSuccess ||
+        (e = hipMalloc((void**)&t->d_counts, 2 * sizeof(unsigned long long))) != hipSuccess ||
+        (e = hipHostMalloc((void**)&t->h_row, sizeof(moe_expert_ref) * t->E, hipHostMallocDefault)) != hipSuccess ||
+        (e = hipMemcpy(t->d_base, b0.data(), nb, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(t->d_src, t->dev_blob.data(), sizeof(void*) * n, hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemset(t->d_counts, 0, 2 * sizeof(unsigned long long))) != hipSuccess ||
+        (e = hipDeviceSynchronize()) != hipSuccess) {
+      moe_tier_destroy(t);
+      return hip_err(W, e);
+    }
+  }
   *out = t;
   return MOE_OK;
 }
@@ -193,13 +290,7 @@ moe_status moe_tier_prepare(moe_tier* t, int32_t layer, const moe_buckets* b,
   if (na < 0 || na > t->E) return moe::tier_fail(MOE_ERR_INVALID_ARG, "%s: corrupt active count %d", W, na);
   // 2. table: resident experts point at their slot; misses get a staging slot
   const size_t base = (size_t)layer * t->E;
-  for (int x = 0; x < t->E; ++x) {
-    moe_expert_ref r = t->scales[base + x];
-    const int sl = t->slot_of[base + x];
-    r.blob = sl >= 0 ? slot_ptr(t, layer, sl) : nullptr;
-    r.reserved = 0;
-    t->h_table[x] = r;
-  }
+  fill_base_row(t, layer, t->h_table);
   int used = 0;
   for (int i = 0; i < na; ++i) {
     const int x = t->h_active[i];
@@ -224,6 +315,35 @@ moe_status moe_tier_prepare(moe_tier* t, int32_t layer, const moe_buckets* b,
   // after that call's event wait, which follows this layer's experts (and
   // hence these copies).
   t->st.prepares++;
+  return MOE_OK;
+}
+
+moe_status moe_tier_prepare_async(moe_tier* t, int32_t layer, const moe_buckets* b,
+                                  moe_expert_ref* table_dev, hipStream_t compute) {
+  const char* W = "moe_tier_prepare_async";
+  if (!t || !b || !table_dev) return moe::tier_fail(MOE_ERR_INVALID_ARG, "%s: NULL argument", W);
+  if (layer < 0 || layer >= t->L) return moe::tier_fail(MOE_ERR_INVALID_ARG, "%s: layer %d", W, layer);
+  if (b->E != t->E) return moe::tier_fail(MOE_ERR_INVALID_ARG, "%s: buckets carved for E=%d", W, b->E);
+  if (!t->d_base)
+    return moe::tier_fail(MOE_ERR_UNSUPPORTED, "%s: host blobs are not mapped for the device", W);
+  const int64_t max_active = std::min<int64_t>(t->E, b->T_max * b->k);
+  if (max_active > t->S)
+    return moe::tier_fail(MOE_ERR_BUDGET,
+                          "%s: %lld possible misses per step (T_max * k) exceed the %d staging slots",
+                          W, (long long)max_active, t->S);
+  if (max_active == 0) return MOE_OK;
+  const size_t base = (size_t)layer * t->E;
+  hipLaunchKernelGGL(k_tier_plan, dim3(1), dim3(1024), 0, compute, t->d_base + base,
+                     t->d_src + base, b->active, b->n_active, t->E, stage_ptr(t, 0), t->eb,
+                     table_dev, t->d_ajobs, t->d_anjobs, t->d_counts);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(k_tier_copy_async, dim3(kCopyWG, (unsigned)max_active), dim3(256), 0,
+                       compute, t->d_ajobs, t->d_anjobs, t->eb / 16);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return hip_err(W, e);
+  t->async_prepares++;
   return MOE_OK;
 }
 
@@ -267,6 +387,14 @@ moe_status moe_tier_rebalance(moe_tier* t, int32_t layer, const uint32_t* hist_d
       (e = hipEventRecord(t->ev_copies, t->copy)) != hipSuccess ||
       (e = hipStreamWaitEvent(compute, t->ev_copies, 0)) != hipSuccess)
     return hip_err(W, e);
+  if (t->d_base) {  // the asynchronous prepare's copy of this layer's base row
+    // h_row is free: the previous rebalance's copy of it finished before
+    // this call synchronized the compute stream.
+    fill_base_row(t, layer, t->h_row);
+    if ((e = hipMemcpyAsync(t->d_base + base, t->h_row, sizeof(moe_expert_ref) * t->E,
+                            hipMemcpyHostToDevice, compute)) != hipSuccess)
+      return hip_err(W, e);
+  }
   t->st.rebalances++;
   return MOE_OK;
 }
@@ -275,6 +403,15 @@ moe_status moe_tier_stats_get(const moe_tier* t, moe_tier_stats* out, int32_t la
                               int32_t* resident_out) {
   if (!t || !out) return moe::tier_fail(MOE_ERR_INVALID_ARG, "moe_tier_stats_get: NULL argument");
   *out = t->st;
+  if (t->d_counts && t->async_prepares) {  // counters of the asynchronous prepares
+    unsigned long long c[2];
+    hipError_t e = hipMemcpy(c, t->d_counts, sizeof(c), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_err("moe_tier_stats_get", e);
+    out->hits += c[0];
+    out->misses += c[1];
+    out->h2d_bytes += c[1] * t->eb;
+    out->prepares += t->async_prepares;
+  }
   if (resident_out) {
     if (layer < 0 || layer >= t->L)
       return moe::tier_fail(MOE_ERR_INVALID_ARG, "moe_tier_stats_get: layer %d", layer);
@@ -290,6 +427,12 @@ void moe_tier_destroy(moe_tier* t) {
   if (t->h_active) (void)hipHostFree(t->h_active);
   if (t->h_table) (void)hipHostFree(t->h_table);
   if (t->h_jobs) (void)hipHostFree(t->h_jobs);
+  if (t->h_row) (void)hipHostFree(t->h_row);
+  if (t->d_base) (void)hipFree(t->d_base);
+  if (t->d_src) (void)hipFree((void*)t->d_src);
+  if (t->d_ajobs) (void)hipFree(t->d_ajobs);
+  if (t->d_anjobs) (void)hipFree(t->d_anjobs);
+  if (t->d_counts) (void)hipFree(t->d_counts);
   delete t;
 }
 

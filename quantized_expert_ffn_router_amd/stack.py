@@ -10,10 +10,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (DeviceLayer, LayerDesc, MOE_FMT_NVFP4, StepBuffers, TierDesc, moe_bucket,
-               moe_combine, moe_expert_blob_bytes, moe_expert_ffn, moe_expert_hist,
-               moe_pack_experts, moe_route, moe_tier_create, moe_tier_destroy,
-               moe_tier_prepare, moe_tier_rebalance)
+from . import (DeviceLayer, LayerDesc, MOE_FMT_NVFP4, StepBuffers, TierDesc, moe_combine,
+               moe_expert_blob_bytes, moe_expert_ffn, moe_route_bucket, moe_tier_create,
+               moe_tier_destroy, moe_tier_prepare, moe_tier_prepare_async, moe_tier_rebalance)
 
 
 def _pin(nbytes, pinned=True):
@@ -116,13 +115,15 @@ class LayerStack:
             desc = self.descs[l]
             b = self.bias(l, epoch)
             desc.router_bias = None if b is None else b.data_ptr()
-            moe_route(desc, x, T, buf.logits, buf.idx, buf.w, stream)
-            moe_bucket(desc, buf.idx, T, buf.buckets, buf.ws, buf.ws_bytes, stream)
+            # route, top-k, bucketing and the usage histogram (one launch
+            # after the router when the step is small enough)
+            moe_route_bucket(desc, x, T, buf.logits, buf.idx, buf.w, buf.buckets, buf.ws,
+                             buf.ws_bytes, self.hists[l], hist_shifts[0], hist_shifts[1], stream)
             if self.tiered is not None:
-                moe_tier_prepare(self.tier, l, buf.buckets, self.tables[l], stream)
+                prepare = moe_tier_prepare_async if self.tiered.get("async") else moe_tier_prepare
+                prepare(self.tier, l, buf.buckets, self.tables[l], stream)
             moe_expert_ffn(desc, x, T, buf.buckets, buf.y, buf.y_dtype, buf.ws, buf.ws_bytes, stream)
             moe_combine(desc, buf.y, buf.y_dtype, buf.buckets, buf.w, T, x, x, stream)
-            moe_expert_hist(desc, buf.buckets, self.hists[l], hist_shifts[0], hist_shifts[1], stream)
         return x
 
     def rebalance(self, stream=None):

@@ -121,3 +121,55 @@ def test_tiered_layers_match_oracle_teacher_forced():
         ref = oracle.layer(ins[l], layer, residual=ins[l])
         check_out(ins[l + 1], ref["out"])
     st.close()
+
+
+def test_async_prepare_equals_sync_prepare_and_all_resident():
+    """moe_tier_prepare_async (planning and copies on the device, no host
+    round trip): the stack's outputs equal the all-resident stack's bit for
+    bit, and hits, misses and copied bytes equal those of the synchronous
+    prepare on the same steps."""
+    import quantized_expert_ffn_router_amd as q
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    w, sets, routers, bias = _stack_inputs()
+    ref = LayerStack(sets, routers, bias, L=3, k=w.k)
+    sync = LayerStack(sets, routers, bias, L=3, k=w.k, tiered={"resident": 16, "staging": 32})
+    asyn = LayerStack(sets, routers, bias, L=3, k=w.k,
+                      tiered={"resident": 16, "staging": 32, "async": True})
+    a = _run(ref, w, 6)
+    b = _run(sync, w, 6, rebalance_every=2)
+    c = _run(asyn, w, 6, rebalance_every=2)
+    for st, (u, v) in enumerate(zip(a, c)):
+        assert np.array_equal(u, v), f"step {st} differs"
+    s_sync, _ = q.moe_tier_stats_get(sync.tier)
+    s_async, _ = q.moe_tier_stats_get(asyn.tier)
+    print("sync", s_sync, "async", s_async)
+    for key in ("hits", "misses", "h2d_bytes", "promotions", "prepares", "rebalances"):
+        assert s_async[key] == s_sync[key], key
+    assert s_async["misses"] > 0 and s_async["hits"] > 0
+    sync.close()
+    asyn.close()
+
+
+def test_async_prepare_needs_staging_for_every_possible_miss():
+    """8 tokens x top-4 can miss 32 experts: 16 staging slots are refused
+    before any launch; pageable host blobs are refused too (the device cannot
+    read them)."""
+    import torch
+    import quantized_expert_ffn_router_amd as q
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    w, sets, routers, bias = _stack_inputs(L=1)
+    x = torch.from_numpy(moegen.make_tokens(w, 8).view(np.int16).copy()).cuda()
+    st = LayerStack(sets, routers, bias, L=1, k=w.k,
+                    tiered={"resident": 8, "staging": 16, "async": True})
+    with pytest.raises(q.MoeError) as ei:
+        st.step(x, 8)
+    assert ei.value.status == q.MOE_ERR_BUDGET
+    torch.cuda.synchronize()
+    st.close()
+    st = LayerStack(sets, routers, bias, L=1, k=w.k,
+                    tiered={"resident": 8, "staging": 32, "async": True, "pinned": False})
+    with pytest.raises(q.MoeError) as ei:
+        st.step(x, 8)
+    assert ei.value.status == q.MOE_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    st.close()
