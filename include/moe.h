@@ -244,7 +244,12 @@ moe_status moe_route_bucket(const moe_layer_desc* L, const uint16_t* x, int64_t 
  *   rows in sorted order.  Decode-sized batches run as dequant-fused GEMV;
  *   larger ones as an MFMA grouped GEMM over experts, which multiplies an
  *   fp16 copy of x scaled per token row by a power of two (exact for every
- *   value above 2^-29 of the row's largest magnitude).
+ *   value above 2^-29 of the row's largest magnitude).  h between the two
+ *   projections is rounded to 16 bits (bf16 in the GEMV; scaled fp16 in the
+ *   GEMM, redone in bf16 if it would overflow).  The GEMM rounds Q6_K and
+ *   Q8_0 down weights once to fp16; for Q8_0 the product q * d is formed as
+ *   q * (16 d) in fp16, so the GEMM needs |w| < 4096 there (the GEMV has no
+ *   such limit; with larger Q8_0 weights force MOE_FFN_GEMV).
  * ws: at least moe_workspace_bytes(L, T) bytes. */
 moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                           const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
