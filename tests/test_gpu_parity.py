@@ -248,3 +248,44 @@ def test_gemm_activation_magnitudes(x_std, w_std, fmt_down):
     got = moegen.bf16_to_f32(g["out"][toks])
     ref = moegen.bf16_to_f32(o_out[toks])
     assert rel_l2(got, ref) <= 5e-3, rel_l2(got, ref)
+
+
+def test_graph_replay_matches_eager():
+    """The bench times decode steps replayed from a HIP graph: each replay of
+    a captured step equals the eager step bit for bit (output, indices, gate
+    weights), with eager steps on other inputs and synchronizations between
+    the replays."""
+    import torch
+    import quantized_expert_ffn_router_amd as q
+    w, L = layer("decode")
+    dl = q.DeviceLayer(L)
+    B = 8
+    buf = q.StepBuffers(dl, B)
+    xa = torch.from_numpy(moegen.make_tokens(w, B, step=11).view(np.int16).copy()).cuda()
+    xb = torch.from_numpy(moegen.make_tokens(w, B, step=12).view(np.int16).copy()).cuda()
+    s = torch.cuda.Stream()
+
+    def snap():
+        return (buf.out[:B].clone(), buf.idx[:B].clone(), buf.w[:B].clone())
+
+    with torch.cuda.stream(s):
+        q.layer_forward(dl, buf, xa, B, stream=s, hist_shifts=None)
+    torch.cuda.synchronize()
+    ref = snap()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        q.layer_forward(dl, buf, xa, B, stream=s, hist_shifts=None)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        with torch.cuda.stream(s):
+            q.layer_forward(dl, buf, xb, B, stream=s, hist_shifts=None)
+        torch.cuda.synchronize()
+        other = snap()
+        assert not torch.equal(other[0], ref[0])  # the buffers now hold another step
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        got = snap()
+        for a, b, name in zip(got, ref, ("out", "idx", "w")):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs"
+    del g
