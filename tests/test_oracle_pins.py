@@ -140,6 +140,26 @@ def test_q8_0_generator_roundtrip_on_grid():
     np.testing.assert_array_equal(dec, W.astype(np.float64))
 
 
+def test_q8_0_generator_zero_block_and_code_range():
+    """An all-zero block gets d = 0 and zero codes (decodes to zeros); in
+    random blocks every code stays in [-127, 127] and each decoded weight is
+    within d/2 of the input, except where the clamp at 127 applies (the
+    block maximum, when fp16 rounds d below amax/127)."""
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((3, 96)) * 0.05).astype(np.float32)
+    W[1, 32:64] = 0.0
+    q = moegen.quant_q8_0(W).reshape(3, 3, 34)
+    codes = q[:, :, 2:].view(np.int8).astype(np.int64)
+    assert codes.min() >= -127 and codes.max() <= 127
+    assert (q[1, 1] == 0).all()
+    dec = oracle.decode_q8_0(moegen.quant_q8_0(W), 96)
+    assert (dec[1, 32:64] == 0).all()
+    d = q[:, :, :2].copy().view(np.float16).astype(np.float64)[:, :, 0]
+    err = np.abs(dec - W.astype(np.float64)).reshape(3, 3, 32)
+    clamped = (np.abs(codes) == 127)
+    assert (err[~clamped] <= (d[:, :, None] / 2 + 1e-12).repeat(32, 2)[~clamped]).all()
+
+
 def test_generator_quantizers_roundtrip_on_grid():
     """Values already on the NVFP4 / Q6_K grids survive quantize->decode."""
     e2m1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
