@@ -173,3 +173,53 @@ def test_async_prepare_needs_staging_for_every_possible_miss():
     assert ei.value.status == q.MOE_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     st.close()
+
+
+def test_tiered_full_size_equals_all_resident_bit_exact():
+    """The tiered configuration at full size, as the bench runs it: 48 layers
+    of 256 experts (hidden 2048, intermediate 512, Q6_K-style down), 96
+    resident per layer, 64 staging slots, the device-side prepare, a
+    rebalance every 4 steps and Zipf(1.2) routing whose ranking is redrawn
+    inside the run.  12 steps of 8 tokens equal the all-resident stack bit
+    for bit (two expert sets shared round-robin by the layers); the first and
+    last layers of the last step match the oracle (teacher-forced)."""
+    import torch
+    import quantized_expert_ffn_router_amd as q
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    W = moegen.WORKLOADS["tiered"]
+    L, R, S, T = W.extra["layers"], W.extra["resident"], 64, W.T
+    sets = [moegen.make_layer(W, layer=200 + i) for i in range(2)]
+    routers = [moegen.normal_f32(moegen.key(0, moegen.TAG_ROUTER, 300 + l), W.E * W.H, W.w_std)
+               .reshape(W.E, W.H) for l in range(L)]
+
+    def bias(l, epoch):
+        b, _ = moegen.zipf_bias(moegen.key(0, moegen.TAG_BIAS, 300 + l, epoch), W.E, W.zipf_s,
+                                W.zipf_alpha)
+        return b
+    ref = LayerStack(sets, routers, bias, L=L, k=W.k)
+    tiered = LayerStack(sets, routers, bias, L=L, k=W.k,
+                        tiered={"resident": R, "staging": S, "async": True})
+    steps, epoch_len = 12, 6
+    trace = []
+    for st in range(steps):
+        x0 = moegen.make_tokens(W, T, step=st, layer=999).view(np.int16)
+        xa = torch.from_numpy(x0.copy()).cuda()
+        xb = torch.from_numpy(x0.copy()).cuda()
+        ref.step(xa, T, epoch=st // epoch_len)
+        tiered.step(xb, T, epoch=st // epoch_len, trace=trace if st == steps - 1 else None)
+        if (st + 1) % 4 == 0:
+            tiered.rebalance()
+        torch.cuda.synchronize()
+        assert torch.equal(xa, xb), f"step {st} differs"
+    print("full-size tiered steps equal", flush=True)
+    stats, _ = q.moe_tier_stats_get(tiered.tier)
+    assert stats["hits"] > 0 and stats["misses"] > 0 and stats["promotions"] > 0
+    ins = [t.cpu().numpy().view(np.uint16) for t in trace] + [xb.cpu().numpy().view(np.uint16)]
+    ep = (steps - 1) // epoch_len
+    for l in (0, L - 1):
+        Lw = sets[l % 2]
+        layer = moegen.LayerWeights(**{**Lw.__dict__, "w_router": routers[l], "bias": bias(l, ep)})
+        out = oracle.layer(ins[l], layer, residual=ins[l])
+        check_out(ins[l + 1], out["out"])
+    tiered.close()
+    ref.close()
