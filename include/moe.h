@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -81,8 +81,8 @@ typedef enum moe_status {
 /* Library version of this header (MOE_ABI_VERSION). */
 int moe_abi_version(void);
 
-/* Expert-FFN kernel family used by moe_expert_ffn (process-wide setting, not
- * synchronized with calls in flight on other threads):
+/* Expert-FFN kernel family (moe_layer_desc.ffn_mode, read by each
+ * moe_expert_ffn call; there is no process-wide state):
  *   MOE_FFN_AUTO -- dequant-fused GEMV for decode-sized batches, MFMA grouped
  *                   GEMM once experts average >= 16 tokens (default);
  *   MOE_FFN_GEMV / MOE_FFN_GEMM -- force one family (any size; results agree
@@ -90,11 +90,11 @@ int moe_abi_version(void);
  *                   H % 256 == 0, T*H < 2^32 and T*k*I < 2^32; AUTO uses the
  *                   GEMV otherwise, and a forced GEMM call fails with
  *                   MOE_ERR_UNSUPPORTED.
- * Returns MOE_ERR_INVALID_ARG for any other value. */
+ * Any other value is rejected with MOE_ERR_INVALID_ARG by every call that
+ * takes the layer. */
 #define MOE_FFN_AUTO 0
 #define MOE_FFN_GEMV 1
 #define MOE_FFN_GEMM 2
-moe_status moe_set_ffn_mode(int32_t mode);
 
 /* Message of the last failing call on this thread ("" if none).  Host
  * string owned by the library, valid until the next failing call. */
@@ -124,7 +124,11 @@ const char* moe_last_error(void);
  * The GPU kernels read a packed "blob" per expert (a device-friendly
  * re-arrangement of the same bytes, 16-byte granules transposed so that one
  * wavefront load covers consecutive rows).  moe_expert_blob_bytes gives its
- * size; moe_pack_experts writes it.
+ * size; moe_pack_experts writes it.  With Q6_K or Q8_0 down weights the blob
+ * ends with a 256-byte section holding one int32 computed by the pack from
+ * the expert's block scales: the power of two by which the grouped GEMM
+ * scales that expert's fp16 down weights (so none can overflow fp16, for any
+ * scales; the product is scaled back in fp32).
  */
 
 /* One entry of the device-resident expert table (24 bytes). */
@@ -133,7 +137,7 @@ typedef struct moe_expert_ref {
   float ts_gate;      /* NVFP4 per-tensor scales */
   float ts_up;
   float ts_down;      /* ignored when the down projection is Q6_K or Q8_0 */
-  uint32_t reserved;  /* 0 */
+  uint32_t reserved;  /* 0 (not read by the library) */
 } moe_expert_ref;
 
 /* Bytes of one packed expert blob (a multiple of 256); 0 if unsupported. */
@@ -164,7 +168,7 @@ typedef struct moe_layer_desc {
   int32_t fmt_gate_up;  /* MOE_FMT_NVFP4 */
   int32_t fmt_down;     /* MOE_FMT_NVFP4, MOE_FMT_Q6K or MOE_FMT_Q8_0 */
   int32_t renormalize;  /* 1: softmax renormalised over the selected k; 0: full softmax */
-  int32_t reserved;     /* 0 */
+  int32_t ffn_mode;     /* MOE_FFN_AUTO (0), MOE_FFN_GEMV or MOE_FFN_GEMM */
   const moe_expert_ref* experts;  /* device [E] */
   const float* w_router;          /* device fp32 [E][H] */
   const float* router_bias;       /* device fp32 [E], or NULL (no bias) */
@@ -199,8 +203,11 @@ size_t moe_workspace_bytes(const moe_layer_desc* L, int64_t T_max);
 /* The layer's steps                                                         */
 /* ------------------------------------------------------------------------ */
 
-/* Router and top-k gating ("each token uses only a few experts":
- * basalt.jgulfo.com, "Expert tiers").
+/* Router and top-k gating.  The pages' model routes every token to a small
+ * subset of its many experts (basalt.jgulfo.com, "Expert tiers"; aiopssre.com,
+ * "Experts can move without becoming free"); how the subset is scored is not
+ * given, so this is the plainest reading: a linear router, top-k on its
+ * logits, softmax weights.
  *   logits[t][e] = fp32( sum_h x[t][h] * w_router[e][h] + bias[e] ), the sum
  *     taken in double precision in one fixed order -- 64 interleaved partial
  *     sums (partial j adds h = j, j+64, ... ascending), combined pairwise
@@ -217,7 +224,10 @@ moe_status moe_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, floa
                      int32_t* topk_idx, float* topk_w, hipStream_t stream);
 
 /* Token-to-expert bucketing: a stable counting sort of the T*k assignments by
- * expert (deterministic; no dependence on atomic ordering).  Fills every
+ * expert (deterministic; no dependence on atomic ordering), so that each
+ * selected expert runs once per step over all the tokens that chose it and
+ * experts nobody chose are not touched (the sparse selection of
+ * basalt.jgulfo.com, "Expert tiers").  Fills every
  * field of *b for this step.  b->T_max >= T, b->E == L->E, b->k == L->k.
  * ws: device workspace of at least moe_workspace_bytes(L, T) bytes. */
 moe_status moe_bucket(const moe_layer_desc* L, const int32_t* topk_idx, int64_t T,
@@ -235,7 +245,10 @@ moe_status moe_route_bucket(const moe_layer_desc* L, const uint16_t* x, int64_t 
                             void* ws, size_t ws_bytes, uint32_t* hist, int32_t decay_shift,
                             int32_t unit_shift, hipStream_t stream);
 
-/* Expert FFNs with fused dequantization (SwiGLU):
+/* Expert FFNs with fused dequantization (SwiGLU).  The routed experts are
+ * stored block-quantized -- NVFP4 in the pages' packs, with GGUF Q6_K tensors
+ * in the DQ6_K packs (basalt.jgulfo.com, "Models" and "Quick start"); the
+ * weights are decoded inside the matmuls, never materialised:
  *   for each assignment a of expert e (token t = a / k), at sorted position
  *   p = b->asg_pos[a]:
  *     g = x[t] . dq(Wg_e)^T,  u = x[t] . dq(Wu_e)^T,  h = silu(g) * u,
@@ -247,16 +260,18 @@ moe_status moe_route_bucket(const moe_layer_desc* L, const uint16_t* x, int64_t 
  *   value above 2^-29 of the row's largest magnitude).  h between the two
  *   projections is rounded to 16 bits (bf16 in the GEMV; scaled fp16 in the
  *   GEMM, redone in bf16 if it would overflow).  The GEMM rounds Q6_K and
- *   Q8_0 down weights once to fp16; for Q8_0 the product q * d is formed as
- *   q * (16 d) in fp16, so the GEMM needs |w| < 4096 there (the GEMV has no
- *   such limit; with larger Q8_0 weights force MOE_FFN_GEMV).
+ *   Q8_0 down weights once to fp16 after scaling each expert's weights by a
+ *   power of two fixed at pack time (see the blob), so any scales are in
+ *   range; the GEMV decodes them exactly.
  * ws: at least moe_workspace_bytes(L, T) bytes. */
 moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                           const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
                           size_t ws_bytes, hipStream_t stream);
 
-/* Gate-weighted combine (the scatter-add written as a gather, so the result
- * does not depend on scheduling):
+/* Gate-weighted combine: each token's output is its selected experts'
+ * outputs weighted by the gates (the mixture the pages' model computes from
+ * the few experts a token uses: basalt.jgulfo.com, "Expert tiers"), written
+ * as a gather so that the result does not depend on scheduling:
  *   out[t] = bf16_rne( residual[t] + sum_{j=0..k-1} topk_w[t][j] * y[asg_pos[t*k+j]] ),
  *   in fp32 with j ascending.  residual: bf16 [T][H] or NULL; out: bf16 [T][H]
  *   (may alias residual). */
@@ -264,9 +279,10 @@ moe_status moe_combine(const moe_layer_desc* L, const void* y, int32_t y_dtype,
                        const moe_buckets* b, const float* topk_w, int64_t T,
                        const uint16_t* residual, uint16_t* out, hipStream_t stream);
 
-/* Expert-usage histogram deciding residency ("keeps the busiest in VRAM",
- * "Tier 1 ... the most routed experts": basalt.jgulfo.com, "Expert tiers";
- * "an adaptive tier moves them": FAQ).  Exponentially decaying integer count,
+/* Expert-usage histogram deciding residency: the pages keep the most-routed
+ * experts in GPU memory and let the placement follow usage as the
+ * conversation changes (basalt.jgulfo.com, "Expert tiers" and the FAQ).  The
+ * running count is this reading: an exponentially decaying integer count,
  * unsigned 32-bit arithmetic:
  *   hist[e] = hist[e] - (hist[e] >> decay_shift) + (counts[e] << unit_shift).
  * hist: uint32 [E], read and written.  0 <= decay_shift, unit_shift < 32. */
@@ -277,13 +293,12 @@ moe_status moe_expert_hist(const moe_layer_desc* L, const moe_buckets* b, uint32
 /* Optional cold-expert tier: pinned host RAM -> HBM slots                   */
 /* ------------------------------------------------------------------------ */
 /*
- * Experts outside the GPU memory budget live in system RAM and are streamed in
- * when routed to ("experts outside its memory budget can live in system RAM
- * and be streamed as needed": aiopssre.com, "Experts can move without becoming
- * free"); the most-routed experts stay resident ("Tier 1 ... the most routed
- * experts", "Tier 3 System RAM": basalt.jgulfo.com, "Expert tiers"); the
- * resident set follows the usage histogram ("an adaptive tier moves them":
- * basalt.jgulfo.com, FAQ).  One GPU only: no peer-GPU tier.
+ * Experts that do not fit the GPU memory budget stay in system RAM and are
+ * copied in when a token routes to them (aiopssre.com, "Experts can move
+ * without becoming free"); the most-routed experts are the ones kept in GPU
+ * memory, with system RAM as the last tier (basalt.jgulfo.com, "Expert
+ * tiers"); the resident set follows the usage histogram, so it moves as usage
+ * changes (basalt.jgulfo.com, FAQ).  One GPU only: no peer-GPU tier.
  *
  * Per layer l: R resident slots (experts chosen by moe_tier_rebalance) in the
  * caller's HBM pool, plus S staging slots shared by all layers.  Before the

@@ -84,6 +84,9 @@ def lib():
         L.oracle_q8_0_weight.restype = ctypes.c_double
         L.oracle_q8_0_weight.argtypes = [vp, i64, i64, i64]
         L.oracle_decode_q8_0.argtypes = [vp, i64, i64, vp]
+        L.oracle_expert_rows.argtypes = [ctypes.POINTER(OracleExperts), i64, vp, i64, vp]
+        L.oracle_init.argtypes = []
+        L.oracle_init()
         _lib = L
     return _lib
 
@@ -199,6 +202,16 @@ def expert(L, e: int, x_row: np.ndarray) -> np.ndarray:
     s = experts_struct(L)
     y = np.empty(L.H, np.float64)
     lib().oracle_expert(ctypes.byref(s), e, _p(np.ascontiguousarray(x_row, np.uint16)), _p(y))
+    return y
+
+
+def expert_rows(L, e: int, x_rows: np.ndarray) -> np.ndarray:
+    """Expert e on each bf16 row of x_rows [n][H] -> float64 [n][H]; every row
+    equals expert(L, e, row) bit for bit (the weights are decoded once)."""
+    s = experts_struct(L)
+    x_rows = np.ascontiguousarray(x_rows, np.uint16).reshape(-1, L.H)
+    y = np.empty((x_rows.shape[0], L.H), np.float64)
+    lib().oracle_expert_rows(ctypes.byref(s), e, _p(x_rows), x_rows.shape[0], _p(y))
     return y
 
 

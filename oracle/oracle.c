@@ -5,11 +5,11 @@
  * code, header or table.
  *
  * What the layer computes is taken from the Basalt pages:
- *   - "Each token uses only a few experts" and the busiest experts are kept in
- *     VRAM (basalt.jgulfo.com, section "Expert tiers"); a mixture-of-experts
- *     model "selects a subset as it processes tokens" (aiopssre.com, "What
- *     Basalt changes in a Blackwell local inference stack", section "Experts
- *     can move without becoming free").
+ *   - A token is routed to a small subset of the experts and the most-used
+ *     experts are the ones kept in GPU memory (basalt.jgulfo.com, section
+ *     "Expert tiers"); the model picks a subset of experts per token
+ *     (aiopssre.com, "What Basalt changes in a Blackwell local inference
+ *     stack", section "Experts can move without becoming free").
  *   - Routed experts are stored as NVIDIA's NVFP4, and packs such as
  *     NVFP4-DQ6_K carry GGUF Q6_K tensors (basalt.jgulfo.com, sections
  *     "Models", "Quick start" and "All the numbers" / engine notes); the
@@ -303,6 +303,51 @@ void oracle_expert(const oracle_experts* X, int64_t e, const uint16_t* x, double
   }
   free(hv);
 }
+
+/* The same expert applied to n token rows x[n][H] (bf16), y[n][H] in double:
+ * the expert's three matrices are decoded once, then every row runs exactly
+ * the sums of oracle_expert, in the same order, so each y row equals
+ * oracle_expert's bit for bit (a speed-up for large parity checks only). */
+void oracle_expert_rows(const oracle_experts* X, int64_t e, const uint16_t* x, int64_t n,
+                        double* y) {
+  int64_t H = X->H, I = X->I;
+  double* wg = (double*)malloc(sizeof(double) * (size_t)(I * H));
+  double* wu = (double*)malloc(sizeof(double) * (size_t)(I * H));
+  double* wd = (double*)malloc(sizeof(double) * (size_t)(H * I));
+  double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+  double* hv = (double*)malloc(sizeof(double) * (size_t)I);
+  const uint8_t* gq = X->gate_q + e * I * (H / 2);
+  const uint8_t* gs = X->gate_s + e * I * (H / 16);
+  const uint8_t* uq = X->up_q + e * I * (H / 2);
+  const uint8_t* us = X->up_s + e * I * (H / 16);
+  for (int64_t i = 0; i < I; ++i)
+    for (int64_t h = 0; h < H; ++h) {
+      wg[i * H + h] = oracle_nvfp4_weight(gq, gs, X->gate_ts[e], H, i, h);
+      wu[i * H + h] = oracle_nvfp4_weight(uq, us, X->up_ts[e], H, i, h);
+    }
+  for (int64_t m = 0; m < H; ++m)
+    for (int64_t i = 0; i < I; ++i) wd[m * I + i] = down_weight(X, e, m, i);
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t h = 0; h < H; ++h) xv[h] = oracle_bf16(x[r * H + h]);
+    for (int64_t i = 0; i < I; ++i) {
+      double g = 0.0, u = 0.0;
+      for (int64_t h = 0; h < H; ++h) {
+        g += xv[h] * wg[i * H + h];
+        u += xv[h] * wu[i * H + h];
+      }
+      hv[i] = g / (1.0 + exp(-g)) * u;
+    }
+    for (int64_t m = 0; m < H; ++m) {
+      double s = 0.0;
+      for (int64_t i = 0; i < I; ++i) s += hv[i] * wd[m * I + i];
+      y[r * H + m] = s;
+    }
+  }
+  free(wg); free(wu); free(wd); free(xv); free(hv);
+}
+
+/* Builds the decode tables up front (before any concurrent calls). */
+void oracle_init(void) { tables_init(); }
 
 /* Layer output for the listed tokens (all T when tokens == NULL):
  *   out[t] = bf16( residual[t] + sum_{j<k} w[t][j] * y_{t,j} ),

@@ -50,7 +50,7 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("k", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("I", ctypes.c_int32), ("fmt_gate_up", ctypes.c_int32),
                 ("fmt_down", ctypes.c_int32), ("renormalize", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("experts", ctypes.c_void_p),
+                ("ffn_mode", ctypes.c_int32), ("experts", ctypes.c_void_p),
                 ("w_router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p)]
 
 
@@ -85,7 +85,6 @@ _LP = ctypes.POINTER(LayerDesc)
 _BP = ctypes.POINTER(Buckets)
 SIGNATURES = {
     "moe_abi_version": (ctypes.c_int, []),
-    "moe_set_ffn_mode": (ctypes.c_int, [_i32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_expert_blob_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_pack_experts": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
@@ -157,10 +156,6 @@ def _stream(stream) -> int | None:
 
 def moe_abi_version() -> int:
     return lib().moe_abi_version()
-
-
-def moe_set_ffn_mode(mode: int):
-    _check(lib().moe_set_ffn_mode(mode))
 
 
 def moe_expert_blob_bytes(H, I, fmt_gate_up, fmt_down) -> int:
@@ -256,9 +251,11 @@ def moe_tier_destroy(tier):
 
 class DeviceLayer:
     """One layer's weights resident in HBM: router weights/bias, packed expert
-    blobs (packed on the GPU by moe_pack_experts) and the expert table."""
+    blobs (packed on the GPU by moe_pack_experts) and the expert table.
+    ffn_mode: MOE_FFN_AUTO, _GEMV or _GEMM, carried in the layer descriptor
+    (desc.ffn_mode may be changed between calls)."""
 
-    def __init__(self, w, device="cuda", stream=None):
+    def __init__(self, w, device="cuda", stream=None, ffn_mode=MOE_FFN_AUTO):
         import torch
         self.E, self.k, self.H, self.I = w.E, w.k, w.H, w.I
         self.fmt_down = w.fmt_down
@@ -285,7 +282,7 @@ class DeviceLayer:
         torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
         del canon
         self.desc = LayerDesc(self.E, self.k, self.H, self.I, MOE_FMT_NVFP4, self.fmt_down,
-                              w.renormalize, 0, self.refs.data_ptr(), self.w_router.data_ptr(),
+                              w.renormalize, ffn_mode, self.refs.data_ptr(), self.w_router.data_ptr(),
                               None if self.bias is None else self.bias.data_ptr())
 
 

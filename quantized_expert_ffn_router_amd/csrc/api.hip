@@ -55,6 +55,8 @@ moe_status check_layer(const moe_layer_desc* L, const char* where) {
   if (st != MOE_OK) return st;
   if (L->renormalize != 0 && L->renormalize != 1)
     return fail(MOE_ERR_INVALID_ARG, "%s: renormalize=%d must be 0 or 1", where, L->renormalize);
+  if (L->ffn_mode != MOE_FFN_AUTO && L->ffn_mode != MOE_FFN_GEMV && L->ffn_mode != MOE_FFN_GEMM)
+    return fail(MOE_ERR_INVALID_ARG, "%s: ffn_mode=%d", where, L->ffn_mode);
   return MOE_OK;
 }
 
@@ -98,8 +100,6 @@ FfnWs ffn_ws_layout(const moe_layer_desc* L, int64_t T) {
 }
 size_t ffn_ws(const moe_layer_desc* L, int64_t T) { return ffn_ws_layout(L, T).total; }
 
-int g_ffn_mode = MOE_FFN_AUTO;
-
 // The grouped GEMM needs 256-column down tiles and 32-bit element offsets
 // of the token rows (x: T*H values) and of h (T*k*I values).
 bool gemm_fits(const moe_layer_desc* L, int64_t T) {
@@ -110,8 +110,8 @@ bool gemm_fits(const moe_layer_desc* L, int64_t T) {
 // Grouped GEMM once experts average >= 16 tokens (and the batch is not a
 // decode step); dequant-fused GEMV otherwise.
 bool use_gemm(const moe_layer_desc* L, int64_t T) {
-  if (g_ffn_mode == MOE_FFN_GEMV) return false;
-  if (g_ffn_mode == MOE_FFN_GEMM) return true;
+  if (L->ffn_mode == MOE_FFN_GEMV) return false;
+  if (L->ffn_mode == MOE_FFN_GEMM) return true;
   return T > 64 && T * L->k >= 16 * (int64_t)L->E && gemm_fits(L, T);
 }
 
@@ -130,13 +130,6 @@ moe_status tier_fail(moe_status st, const char* fmt, ...) {
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
-
-moe_status moe_set_ffn_mode(int32_t mode) {
-  if (mode != MOE_FFN_AUTO && mode != MOE_FFN_GEMV && mode != MOE_FFN_GEMM)
-    return fail(MOE_ERR_INVALID_ARG, "moe_set_ffn_mode: mode %d", mode);
-  g_ffn_mode = mode;
-  return MOE_OK;
-}
 
 const char* moe_last_error(void) { return g_err; }
 
@@ -179,12 +172,14 @@ moe_status moe_pack_experts(int32_t E, int32_t H, int32_t I, int32_t fmt_gate_up
     const size_t row = (size_t)(I / 32) * 34, ex = (size_t)H * row;
     e = moe::launch_pack_granules(down_q, E, ex, H, I / 16, 16, row, 2, 34, 2, d + lay.down_q, blob_stride, stream);
     if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 128, 2, row, 1, 34, 0, d + lay.down_s, blob_stride, stream, 4);
+    if (e == hipSuccess) e = moe::launch_down_exponent(down_q, E, H, I, fmt_down, d + lay.down_meta, blob_stride, stream);
   } else {
     const size_t row = (size_t)(I / 256) * 210, ex = (size_t)H * row;
     e = moe::launch_pack_granules(down_q, E, ex, H, I / 32, 16, row, 8, 210, 0, d + lay.down_ql, blob_stride, stream);
     if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 64, 16, row, 4, 210, 128, d + lay.down_qh, blob_stride, stream);
     if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 256, 16, row, 1, 210, 192, d + lay.down_sc, blob_stride, stream);
     if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 256, 2, row, 1, 210, 208, d + lay.down_d, blob_stride, stream);
+    if (e == hipSuccess) e = moe::launch_down_exponent(down_q, E, H, I, fmt_down, d + lay.down_meta, blob_stride, stream);
   }
   return hip_status(W, e);
 }

@@ -1,8 +1,9 @@
 // combine.hip -- gate-weighted combine of the expert outputs.
 //
 // The mixture's output for a token is the sum of its selected experts'
-// outputs weighted by the gate weights ("each token uses only a few experts":
-// basalt.jgulfo.com, section "Expert tiers").  It is written as a gather over
+// outputs weighted by the gate weights; a token goes through only a small
+// subset of the experts (basalt.jgulfo.com, section "Expert tiers").  It is
+// written as a gather over
 // the token's k assignments (position asg_pos[t*k+j] of the sorted expert
 // outputs), summed in fp32 with j ascending, plus the optional residual, then
 // rounded once to bf16 -- so the result never depends on scheduling.

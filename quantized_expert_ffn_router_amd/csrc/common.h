@@ -23,7 +23,12 @@
 //                         scales of blocks 4g..4g+3.
 //
 // Blob = gate, up (NVFP4, [I][H]) then down ([H][I], NVFP4, Q6_K or Q8_0); each
-// section starts on a 256-byte boundary.
+// section starts on a 256-byte boundary.  Q6_K and Q8_0 blobs end with a
+// 256-byte meta section whose first int32 is the expert's down-weight exponent
+// s (written by moe_pack_experts): the grouped GEMM forms its fp16 down
+// weights as w * 2^s, s chosen from the expert's largest block scale so that
+// no weight of the expert can overflow fp16, and takes 2^-s out in fp32.
+
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,6 +46,7 @@ struct BlobLayout {
   size_t gate_q, gate_s, up_q, up_s;
   size_t down_q, down_s;             // NVFP4 or Q8_0 down
   size_t down_ql, down_qh, down_sc, down_d;  // Q6_K down
+  size_t down_meta;                  // Q6_K / Q8_0: int32 fp16-path exponent (0 for NVFP4)
   size_t total;
 };
 
@@ -62,11 +68,13 @@ inline BlobLayout blob_layout(int64_t H, int64_t I, int fmt_down) {
   } else if (fmt_down == MOE_FMT_Q8_0) {
     b.down_q = take((size_t)H * I);
     b.down_s = take((size_t)H * I / 16);
+    b.down_meta = take(4);
   } else {
     b.down_ql = take((size_t)H * I / 2);
     b.down_qh = take((size_t)H * I / 4);
     b.down_sc = take((size_t)H * I / 16);
     b.down_d = take((size_t)H * I / 128);
+    b.down_meta = take(4);
   }
   b.total = off;
   return b;
@@ -111,6 +119,11 @@ __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 // Each returns hipSuccess or the launch error; arguments are pre-validated.
 
 namespace moe {
+
+// Per-expert exponent of the grouped GEMM's fp16 down weights (Q6_K, Q8_0)
+// from the canonical down bytes, into the blob's meta section.
+hipError_t launch_down_exponent(const uint8_t* down_q, int E, int64_t H, int64_t I, int fmt,
+                                uint8_t* meta, size_t dst_expert_stride, hipStream_t s);
 
 hipError_t launch_pack_granules(const uint8_t* src, int E, size_t src_expert_stride,
                                 int64_t N, int64_t G, int gsz, size_t row_stride,

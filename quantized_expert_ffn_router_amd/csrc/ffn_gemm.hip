@@ -19,12 +19,14 @@
 //     Q8_0) and dequantizes them in registers;
 //   - operands are fp16 (NVFP4 weights are exact in fp16; token rows carry
 //     an exact per-row power-of-two scale, see k_rows_to_f16; Q6_K and Q8_0
-//     weights are rounded once to fp16) except for the bf16 recompute path;
+//     weights are rounded once to fp16 after an exact per-expert power-of-two
+//     scale, see k_down_exponent) except for the bf16 recompute path;
 //   - 8 waves, each 128 rows x 32 columns = 8 x 2 v_mfma_f32_16x16x32 tiles
 //     with fp32 accumulation;
 //   - gate/up: each wave's two column tiles are the same 16 rows of gate and
 //     of up, so SwiGLU runs in registers; h is stored in 16 bits.  Down:
 //     y = acc * ts_d in bf16 or fp32.
+#include <mutex>
 #include <type_traits>
 
 #include "gemv_common.h"
@@ -120,12 +122,14 @@ static_assert(sizeof(TileRec) == 32, "TileRec layout");
 // Row tables of the row blocks, one workgroup of 128 threads per block:
 // record, token row offset of each row (row r -> token * H; rows past the
 // block's end repeat row 0, read but never stored) and that token's fp16 row
-// scale.
+// scale.  For Q6_K and Q8_0 down weights the record's ref.reserved carries
+// the expert's fp16-path exponent, read from the blob's meta section at
+// off_meta (0: none).
 __global__ __launch_bounds__(128) void k_tile_rows(
     const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const uint32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const moe_expert_ref* __restrict__ experts, const int32_t* __restrict__ sorted_asg, int ktop,
-    int H, const float* __restrict__ xscale, TileRec* __restrict__ recs,
+    int H, const float* __restrict__ xscale, size_t off_meta, TileRec* __restrict__ recs,
     uint32_t* __restrict__ toff, float* __restrict__ rsc) {
   const int mt = blockIdx.x;
   if (mt >= *n_tiles) return;
@@ -140,6 +144,8 @@ __global__ __launch_bounds__(128) void k_tile_rows(
   if (r == 0) {
     TileRec t;
     t.ref = experts[e];
+    t.ref.reserved =
+        off_meta ? *reinterpret_cast<const uint32_t*>((const uint8_t*)t.ref.blob + off_meta) : 0u;
     t.srow = srow;
     t.nrows = nrows;
     recs[mt] = t;
@@ -217,7 +223,8 @@ __device__ __forceinline__ void load_frag_pair(FragNvfp4 (&f)[2], const uint8_t*
   f[1].scale = 0;
 }
 
-// Sub-step s: 8 exact bf16 values (E2M1 x E4M3 has at most 6 significant bits).
+// Sub-step s: 8 exact bf16 values (an E2M1 value has at most 2 significant
+// bits and an E4M3 scale at most 4, so their product has at most 6).
 template <int S>
 __device__ __forceinline__ v8bf_t dequant_frag(const FragNvfp4& f) {
   const float s = e4m3x2<false>(f.scale)[S >> 1];  // block 0 for words 0, 1; block 1 for 2, 3
@@ -235,8 +242,9 @@ __device__ __forceinline__ v8bf_t dequant_frag(const FragNvfp4& f) {
 }
 
 // The same 8 values as fp16 -- also exact (E2M1 x E4M3 lies in [2^-10, 2688]
-// with at most 5 significant bits): the codes convert to fp16 pairs and one
-// packed fp16 multiply applies the block scale, 2 VALU per pair instead of 4.
+// with at most 6 significant bits, e.g. 1.5 x 1.875): the codes convert to fp16
+// pairs and one packed fp16 multiply applies the block scale, 2 VALU per pair
+// instead of 4.
 // The fp16 path keeps the scale bytes of both column tiles of a wave in one
 // register (tile j in 16-bit half j), so J selects the half.
 template <int S, int J>
@@ -286,17 +294,19 @@ __device__ __forceinline__ v8bf_t dequant_frag_q6k(const FragQ6k& f) {
   return r;
 }
 
-// The same 8 weights as fp16 for the fp16 path.  The six-bit codes are built
-// in byte lanes (even values of the sub-step in qe, odd in qo), then each pair
-// is placed by one byte permute as two fp16 subnormals q * 2^-24; one packed
-// fma gives (q - 32) * 2^-10 exactly and one packed multiply applies
-// d * sc * 2^10 (rounded once to fp16, then the product once: about 2^-11
-// relative, finer than the bf16 path's 2^-9).  Needs fp16 denormals, the
-// default mode.
+// The same 8 weights times 2^sx as fp16 for the fp16 path (sx: the expert's
+// exponent, k_down_exponent).  The six-bit codes are built in byte lanes (even
+// values of the sub-step in qe, odd in qo), then each pair is placed by one
+// byte permute as two fp16 subnormals q * 2^-24; one packed fma gives
+// (q - 32) * 2^-10 exactly and one packed multiply applies d * sc * 2^(10+sx)
+// (below 2^15 for every block of the expert; rounded once to fp16, then the
+// product once: about 2^-11 relative, finer than the bf16 path's 2^-9).
+// Needs fp16 denormals, the default mode.
 template <int S>
-__device__ __forceinline__ v8h_t dequant_frag_q6k_h(const FragQ6k& f) {
-  const float s32 = f16_to_f32((uint16_t)(f.sc >> 16)) * 1024.0f *
-                    (float)(int8_t)((f.sc >> (8 * (S >> 1))) & 0xffu);
+__device__ __forceinline__ v8h_t dequant_frag_q6k_h(const FragQ6k& f, int sx) {
+  const float s32 = __builtin_amdgcn_ldexpf(
+      f16_to_f32((uint16_t)(f.sc >> 16)) * (float)(int8_t)((f.sc >> (8 * (S >> 1))) & 0xffu),
+      10 + sx);
   const _Float16 sh = (_Float16)s32;
   const v2h_t ss = {sh, sh};
   const uint32_t lo = S == 0 ? f.lo.x : S == 1 ? f.lo.y : S == 2 ? f.lo.z : f.lo.w;
@@ -380,14 +390,15 @@ __device__ __forceinline__ v8bf_t dequant_frag_q8(const FragQ8& f) {
 
 // fp16 path: the codes, offset to unsigned bytes u = q + 128, are placed by
 // one byte permute under the fp16 exponent of 1024 (0x64: 1024 + u exactly),
-// one packed add leaves q and one packed multiply applies d * 2^4 (d is fp16,
-// so exact), rounding the product once.  The 2^4 keeps weights down to about
-// 2^-17 clear of fp16 subnormals; the epilogue takes it out.  Range: the
-// fp16 product needs |w| < 4096.
-constexpr float kQ8Pre = 16.0f;
+// one packed add leaves q and one packed multiply applies d * 2^sx (sx: the
+// expert's exponent, k_down_exponent; an exact ldexp of the fp16 d, below
+// 2^8 for every block of the expert), rounding the product once.  So the
+// weights times 2^sx stay below 2^15 whatever the scales; the epilogue takes
+// the 2^sx out in fp32.
 template <int S, int J>
-__device__ __forceinline__ v8h_t dequant_frag_q8_h(const FragQ8& f, uint32_t sc2) {
-  const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(sc2 >> (16 * J))) * (_Float16)kQ8Pre;
+__device__ __forceinline__ v8h_t dequant_frag_q8_h(const FragQ8& f, uint32_t sc2, int sx) {
+  const _Float16 dh =
+      __builtin_amdgcn_ldexph(__builtin_bit_cast(_Float16, (uint16_t)(sc2 >> (16 * J))), sx);
   const v2h_t ds = {dh, dh};
   const v2h_t off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   uint32_t w[2];
@@ -491,7 +502,7 @@ __device__ __forceinline__ void load_a_half(const uint16_t* base, const uint32_t
 // no wave stalls on a full memory queue right after the barrier.
 template <int FMT, int NC, bool F16, typename Issue>
 __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const uint16_t* Ab,
-                                          int lane, v4f_t (*acc)[NC], Issue issue) {
+                                          int lane, v4f_t (*acc)[NC], int sx, Issue issue) {
   const int r = lane & 15, cq = 4 * (lane >> 4);
   auto sub = [&](auto S_) {
     constexpr int S = decltype(S_)::value;
@@ -502,11 +513,11 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
         bf[0] = dequant_frag_h<S, 0>(bcur[0], bcur[0].scale);
         bf[1] = dequant_frag_h<S, 1>(bcur[1], bcur[0].scale);
       } else if constexpr (FMT == MOE_FMT_Q8_0) {
-        bf[0] = dequant_frag_q8_h<S, 0>(bcur[0], bcur[0].sc);
-        bf[1] = dequant_frag_q8_h<S, 1>(bcur[1], bcur[0].sc);
+        bf[0] = dequant_frag_q8_h<S, 0>(bcur[0], bcur[0].sc, sx);
+        bf[1] = dequant_frag_q8_h<S, 1>(bcur[1], bcur[0].sc, sx);
       } else {
-        bf[0] = dequant_frag_q6k_h<S>(bcur[0]);
-        bf[1] = dequant_frag_q6k_h<S>(bcur[1]);
+        bf[0] = dequant_frag_q6k_h<S>(bcur[0], sx);
+        bf[1] = dequant_frag_q6k_h<S>(bcur[1], sx);
       }
       __builtin_amdgcn_sched_barrier(0);
       issue(S_);
@@ -609,12 +620,12 @@ __device__ __forceinline__ TileRange tile_range(int n_logical) {
 // wave w takes gate rows n0 + 16w .. +16 (tile j = 0) and the same up rows
 // (tile j = 1), so each lane holds matching g and u values.
 //
-// h goes out as fp16 when the down projection is NVFP4 (its GEMM then runs on
-// fp16 operands, whose dequant is half the work) and as bf16 otherwise.  fp16
-// keeps 3 more mantissa bits than bf16 but tops out at 65504: a value beyond
-// that is saturated and raises the call's overflow flag, and then the
-// FALLBACK instance (launched right after, idle unless the flag is set)
-// recomputes all of h as bf16 for a bf16 down GEMM, so the range is bf16's.
+// h goes out as fp16 (every down format's GEMM runs on fp16 operands), scaled
+// per token (h_exp).  fp16 keeps 3 more mantissa bits than bf16 but tops out
+// at 65504: a value beyond that is saturated and raises the call's overflow
+// flag, and then the FALLBACK instance (launched right after, idle unless the
+// flag is set) recomputes all of h as bf16 for a bf16 down GEMM, so the range
+// is bf16's.
 
 template <bool HF16, bool FALLBACK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_gateup_nvfp4(
@@ -704,7 +715,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const int stn = more ? st + 1 : 0;
       uint16_t* Anext = As + (buf ^ 1) * GBM * ARB;
       // Next step: weights first (they come from farther away), rows after.
-      step_mfma<MOE_FMT_NVFP4, 2, true>(bcur, As + buf * GBM * ARB, lane, acc, [&](auto S_) {
+      step_mfma<MOE_FMT_NVFP4, 2, true>(bcur, As + buf * GBM * ARB, lane, acc, 0, [&](auto S_) {
         constexpr int S = decltype(S_)::value;
         if (!ld) return;
         if constexpr (S == 0) {
@@ -844,6 +855,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       nxt = recs[mtn];
       stage_rs(mtn, slotn);  // read in the tile's epilogue, after its steps' barriers
     }
+    const int sx = (int)cur.ref.reserved;  // fp16-path exponent of Q6_K / Q8_0 weights
     v4f_t acc[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -858,7 +870,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const bool ld = more || has_next;
       const int stn = more ? st + 1 : 0;
       uint16_t* Anext = As + (buf ^ 1) * GBM * ARB;
-      step_mfma<FMT, 2, AF16>(bcur, As + buf * GBM * ARB, lane, acc, [&](auto S_) {
+      step_mfma<FMT, 2, AF16>(bcur, As + buf * GBM * ARB, lane, acc, sx, [&](auto S_) {
         constexpr int S = decltype(S_)::value;
         if (!ld) return;
         if constexpr (AF16 && FMT == MOE_FMT_Q8_0) {
@@ -903,9 +915,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // Epilogue: lane holds row 16i + lane%16, columns cb + 16j + 4*(lane/16) .. +4.
     // bf16: the two column tiles are swapped between lane groups so that
     // group g stores columns cb + 8*(g/2) + 16*(g%2) .. +8 of its row.
-    const float ts = (FMT == MOE_FMT_NVFP4)  ? cur.ref.ts_down
-                     : (FMT == MOE_FMT_Q8_0) ? (AF16 ? 1.0f / kQ8Pre : 1.0f)
-                                             : 1.0f;
+    const float ts = (FMT == MOE_FMT_NVFP4) ? cur.ref.ts_down : (AF16 ? pow2f(-sx) : 1.0f);
     const int grp = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -931,7 +941,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-int g_gemm_slots = 0;  // workgroups of a persistent launch: 2 per CU
+// Workgroups of a persistent launch: 2 per CU of the device (rounded up to
+// a multiple of 8 XCDs), looked up once per device.
+constexpr int kMaxDevices = 64;
+std::once_flag g_slots_once[kMaxDevices];
+int g_gemm_slots[kMaxDevices];
+hipError_t g_slots_err[kMaxDevices];
 
 }  // namespace
 
@@ -960,13 +975,17 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
   uint32_t* toff = (uint32_t*)w;
   w += align_up(mtmax * GBM * sizeof(uint32_t));
   float* rsc = (float*)w;
-  if (g_gemm_slots == 0) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    g_gemm_slots = (2 * cus + 7) / 8 * 8;
-  }
+  int dev = 0;
+  hipError_t derr = hipGetDevice(&dev);
+  if (derr != hipSuccess) return derr;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_slots_once[dev], [dev] {
+    int cus = 0;
+    g_slots_err[dev] = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    g_gemm_slots[dev] = (2 * cus + 7) / 8 * 8;
+  });
+  if (g_slots_err[dev] != hipSuccess) return g_slots_err[dev];
+  const int slots = g_gemm_slots[dev];
   const int max_mtiles = (int)(A / BM) + L->E;
   hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, s, b->counts, L->E, BM, tiles, n_tiles);
   hipError_t err = hipGetLastError();
@@ -975,10 +994,10 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
                      xscale);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(k_tile_rows, dim3((unsigned)max_mtiles), dim3(GBM), 0, s, tiles, n_tiles,
-                     b->counts, b->offsets, L->experts, b->sorted_asg, L->k, L->H, xscale, recs,
-                     toff, rsc);
+                     b->counts, b->offsets, L->experts, b->sorted_asg, L->k, L->H, xscale,
+                     lay.down_meta, recs, toff, rsc);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const dim3 grid((unsigned)g_gemm_slots), block(kThreads);
+  const dim3 grid((unsigned)slots), block(kThreads);
   const bool bf = (y_dtype == MOE_DTYPE_BF16);
 #define GU_ARGS                                                                                   \
   xh, L->H, L->I, lay.gate_q, lay.gate_s, lay.up_q, lay.up_s, recs, toff, rsc, n_tiles, ovf, hbuf

@@ -2,7 +2,8 @@
 //
 // Routed experts are block-quantized (NVFP4; GGUF Q6_K in the DQ6_K packs:
 // basalt.jgulfo.com, sections "Models" and "Quick start"), and a token touches
-// only the experts it selected ("Expert tiers").  With 1..8 tokens per step
+// only the experts it selected (same page, "Expert tiers").  With 1..8 tokens
+// per step
 // (one per request slot) the expert FFN is bound by reading each active
 // expert's weight bytes once from HBM, so these kernels stream the packed
 // codes with 16-byte loads and dequantize in registers:

@@ -30,7 +30,62 @@ __global__ void k_pack_granules(const uint8_t* __restrict__ src, size_t src_expe
   }
 }
 
+// Exponent s of the grouped GEMM's fp16 down weights of one expert (one
+// workgroup per expert).  The fp16 path forms, per block, a scale times 2^s in
+// fp16 and the weights from it:
+//   Q8_0:  w * 2^s = q * (d * 2^s), |q| <= 128: with M = max |d| over the
+//          expert's blocks, M * 2^s < 2^8 keeps |w| * 2^s < 2^15;
+//   Q6_K:  w * 2^s = (q - 32) * 2^-10 * (d * sc * 2^(10+s)), |q - 32| <= 32:
+//          with M = max |d * sc|, M * 2^s < 2^5 keeps the fp16 factor below
+//          2^15 and |w| * 2^s below 2^10.
+// s = P - e for M = f * 2^e (f in [0.5, 1)) is the largest such s; all-zero
+// scales give s = 0.  Clamped to [-64, 64].
+__global__ __launch_bounds__(256) void k_down_exponent(const uint8_t* __restrict__ src,
+                                                       size_t src_expert_stride, int64_t nblocks,
+                                                       int fmt, uint8_t* __restrict__ meta,
+                                                       size_t dst_expert_stride) {
+  __shared__ float red[256];
+  const uint8_t* s = src + (size_t)blockIdx.x * src_expert_stride;
+  float m = 0.0f;
+  for (int64_t b = threadIdx.x; b < nblocks; b += blockDim.x) {
+    if (fmt == MOE_FMT_Q8_0) {
+      const uint8_t* blk = s + (size_t)b * 34;
+      m = fmaxf(m, fabsf(f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)))));
+    } else {
+      const uint8_t* blk = s + (size_t)b * 210;
+      int sc = 0;
+      for (int j = 0; j < 16; ++j) sc = max(sc, abs((int)(int8_t)blk[192 + j]));
+      m = fmaxf(m, fabsf(f16_to_f32((uint16_t)(blk[208] | (blk[209] << 8)))) * (float)sc);
+    }
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float M = red[0];
+    int e = 0;
+    (void)frexpf(M, &e);
+    const int P = (fmt == MOE_FMT_Q8_0) ? 8 : 5;
+    int sx = (M > 0.0f && M <= 3.0e38f) ? P - e : 0;
+    sx = sx < -64 ? -64 : (sx > 64 ? 64 : sx);
+    *reinterpret_cast<int32_t*>(meta + (size_t)blockIdx.x * dst_expert_stride) = sx;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_down_exponent(const uint8_t* down_q, int E, int64_t H, int64_t I, int fmt,
+                                uint8_t* meta, size_t dst_expert_stride, hipStream_t s) {
+  const int64_t per_row = (fmt == MOE_FMT_Q8_0) ? I / 32 : I / 256;
+  const size_t bsz = (fmt == MOE_FMT_Q8_0) ? 34 : 210;
+  const int64_t nblocks = H * per_row;
+  hipLaunchKernelGGL(k_down_exponent, dim3((unsigned)E), dim3(256), 0, s, down_q,
+                     (size_t)nblocks * bsz, nblocks, fmt, meta, dst_expert_stride);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_granules(const uint8_t* src, int E, size_t src_expert_stride, int64_t N,
                                 int64_t G, int gsz, size_t row_stride, int per_sb,

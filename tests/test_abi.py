@@ -36,24 +36,24 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_struct_sizes():
-    assert q.moe_abi_version() == 1
+    assert q.moe_abi_version() == 2
     src = open(HEADER).read()
-    assert "#define MOE_ABI_VERSION 1" in src
+    assert "#define MOE_ABI_VERSION 2" in src
     assert ctypes.sizeof(q.ExpertRef) == 24
 
 
 def test_blob_sizes():
     # codes + scales of gate, up, down: 3 * I*H*(1/2 + 1/16)
     assert q.moe_expert_blob_bytes(2048, 768, 1, 1) == 3 * (768 * 2048 // 2 + 768 * 2048 // 16)
-    # Q6_K down: 210 bytes per 256 weights
-    assert q.moe_expert_blob_bytes(2048, 512, 1, 2) == 2 * (512 * 2048 * 9 // 16) + 2048 * 2 * 210
+    # Q6_K down: 210 bytes per 256 weights, plus the 256-byte exponent section
+    assert q.moe_expert_blob_bytes(2048, 512, 1, 2) == 2 * (512 * 2048 * 9 // 16) + 2048 * 2 * 210 + 256
     assert q.moe_expert_blob_bytes(100, 768, 1, 1) == 0
     assert "multiple of 128" in q.last_error()
     assert q.moe_expert_blob_bytes(2048, 384, 1, 2) == 0  # Q6_K needs I % 256
 
 
-def _desc(E=8, k=2, H=256, I=128, fmt_down=1, renorm=1):
-    return q.LayerDesc(E, k, H, I, 1, fmt_down, renorm, 0, 0x1000, 0x2000, None)
+def _desc(E=8, k=2, H=256, I=128, fmt_down=1, renorm=1, ffn_mode=0):
+    return q.LayerDesc(E, k, H, I, 1, fmt_down, renorm, ffn_mode, 0x1000, 0x2000, None)
 
 
 def test_buckets_carve_layout_on_host_buffer():
@@ -84,6 +84,8 @@ def test_buckets_carve_layout_on_host_buffer():
     (dict(I=96, fmt_down=3), q.MOE_ERR_UNSUPPORTED, "I=96"),
     (dict(fmt_down=7), q.MOE_ERR_UNSUPPORTED, "down format"),
     (dict(renorm=2), q.MOE_ERR_INVALID_ARG, "renormalize"),
+    (dict(ffn_mode=3), q.MOE_ERR_INVALID_ARG, "ffn_mode=3"),
+    (dict(ffn_mode=-1), q.MOE_ERR_INVALID_ARG, "ffn_mode=-1"),
 ])
 def test_route_rejects_bad_layers_before_launch(kw, status, msg):
     d = _desc(**kw)
@@ -119,16 +121,17 @@ def test_zero_tokens_is_a_noop_and_null_checks():
 
 def test_blob_bytes_per_down_format():
     """Sections start on 256-byte boundaries: gate and up (NVFP4 codes and
-    scales), then the down projection's planes."""
+    scales), then the down projection's planes; Q6_K and Q8_0 blobs end with
+    a 256-byte section for the grouped GEMM's per-expert weight exponent."""
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
     H, I = 2048, 768
     gu = 2 * (al(I * H // 2) + al(I * H // 16))
     assert q.moe_expert_blob_bytes(H, I, 1, 1) == gu + al(H * I // 2) + al(H * I // 16)
-    assert q.moe_expert_blob_bytes(H, I, 1, 3) == gu + al(H * I) + al(H * I // 16)
+    assert q.moe_expert_blob_bytes(H, I, 1, 3) == gu + al(H * I) + al(H * I // 16) + 256
     I = 512
     gu = 2 * (al(I * H // 2) + al(I * H // 16))
     assert q.moe_expert_blob_bytes(H, I, 1, 2) == gu + al(H * I // 2) + al(H * I // 4) + \
-        al(H * I // 16) + al(H * I // 128)
+        al(H * I // 16) + al(H * I // 128) + 256
     assert q.moe_expert_blob_bytes(H, 96, 1, 3) == 0
 
 

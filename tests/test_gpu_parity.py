@@ -8,7 +8,8 @@ import pytest
 
 import moegen
 import oracle
-from parity_util import Y_REL, check_buckets, check_layer, check_route, rel_l2, run_gpu
+from parity_util import (Y_REL, check_block_edges, check_buckets, check_layer, check_route, rel_l2,
+                         run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +130,8 @@ def test_prefill_routing_full_size_and_sampled_outputs():
     x = moegen.make_tokens(w, w.T)
     sample = list(range(0, w.T, 512)) + [w.T - 1]
     g, _ = check_layer(L, x, tokens=sample, y_dtype=1, y_rel=GEMM_Y_REL)
+    (r, worst), n = check_block_edges(g, L, x)
+    print(f"prefill block edges: {n} rows, rel L2 {r:.2e}, worst row {worst:.2e}", flush=True)
     counts = g["buckets"]["counts"]
     assert counts.sum() == w.T * w.k and counts.min() > 0
     assert counts.max() > 4 * counts.min()   # biased load
@@ -186,7 +189,9 @@ def test_mixed_prefill_q6k_down_sampled():
     projection on the grouped GEMM path."""
     w, L = layer("mixed")
     x = moegen.make_tokens(w, 4096, step=1)
-    check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
+    g, _ = check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
+    (r, worst), n = check_block_edges(g, L, x)
+    print(f"mixed prefill block edges: {n} rows, rel L2 {r:.2e}, worst row {worst:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("B", [1, 8, 32])
@@ -215,7 +220,9 @@ def test_q8_0_prefill_sampled():
     w, L = layer("q8")
     x = moegen.make_tokens(w, 4096, step=2)
     print("q8 prefill", flush=True)
-    check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
+    g, _ = check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
+    (r, worst), n = check_block_edges(g, L, x)
+    print(f"q8 prefill block edges: {n} rows, rel L2 {r:.2e}, worst row {worst:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("x_std,w_std,fmt_down", [
@@ -289,3 +296,47 @@ def test_graph_replay_matches_eager():
         for a, b, name in zip(got, ref, ("out", "idx", "w")):
             assert torch.equal(a, b), f"replay {rep}: {name} differs"
     del g
+
+
+def _scale_down_block_scales(L, exp2):
+    """Copy of layer L whose Q6_K / Q8_0 down block scales d (fp16) are
+    multiplied by 2^exp2 (rounded to fp16 where the result is subnormal; the
+    oracle reads the same bytes)."""
+    import dataclasses
+    dq = L.down_q.copy()
+    flat = dq.reshape(-1)
+    bsz, off = (34, 0) if L.fmt_down == moegen.FMT_Q8_0 else (210, 208)
+    at = np.arange(flat.size // bsz) * bsz + off
+    d = (flat[at].astype(np.uint16) | (flat[at + 1].astype(np.uint16) << 8)).view(np.float16)
+    d2 = (d.astype(np.float64) * 2.0 ** exp2).astype(np.float16)
+    assert np.isfinite(d2).all()
+    bits = d2.view(np.uint16)
+    flat[at] = (bits & 0xff).astype(np.uint8)
+    flat[at + 1] = (bits >> 8).astype(np.uint8)
+    return dataclasses.replace(L, down_q=dq)
+
+
+@pytest.mark.parametrize("fmt_down,exp2", [(3, 18), (3, -10), (2, 16), (2, -8)])
+def test_gemm_down_weights_at_any_scale(fmt_down, exp2):
+    """The grouped GEMM's fp16 down weights carry a per-expert power of two
+    fixed at pack time from the expert's largest block scale: Q8_0 weights
+    up to 16K (beyond the plain fp16 product q * d * 16) and Q6_K d * sc up to
+    ~100 (beyond d * sc * 2^10 in fp16), and block scales pushed into fp16's
+    subnormal range, all match the oracle at the relative bars."""
+    I = 384 if fmt_down == 3 else 512
+    w, L0 = layer("gemm_scale", E=16, k=4, H=512, I=I, T=300, fmt_down=fmt_down)
+    L = _scale_down_block_scales(L0, exp2)
+    x = moegen.make_tokens(w, w.T, step=13)
+    print("down scale", fmt_down, exp2, flush=True)
+    g = run_gpu(L, x, ffn_mode=2)
+    logits, idx, wt = check_route(g, L, x)
+    ob = check_buckets(g["buckets"], idx, L.E)
+    toks = list(range(0, w.T, 3))
+    o_out, o_y = oracle.ffn_combine(L, x, idx, wt, None, toks, want_y=True)
+    rows = [t * L.k + j for t in toks for j in range(L.k)]
+    gy = g["y"][ob["asg_pos"][rows]]
+    assert np.isfinite(gy).all()
+    assert rel_l2(gy, o_y[rows]) <= GEMM_Y_REL, rel_l2(gy, o_y[rows])
+    got = moegen.bf16_to_f32(g["out"][toks])
+    ref = moegen.bf16_to_f32(o_out[toks])
+    assert rel_l2(got, ref) <= 5e-3, rel_l2(got, ref)

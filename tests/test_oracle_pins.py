@@ -391,3 +391,15 @@ def test_ffn_single_expert_identity():
     # y is double; rounding it through fp32 first may differ by one bf16 ulp at ties only
     _bf16_close(out, y, ulps=1)
     assert np.mean(out.view(np.int16) == ref) > 0.99
+
+
+def test_expert_rows_equals_expert():
+    """The batched evaluation runs the same sums in the same order as the
+    per-row oracle: equal bit for bit, for every down format."""
+    for fmt in (moegen.FMT_NVFP4, moegen.FMT_Q6K, moegen.FMT_Q8_0):
+        w = moegen.Workload(name="rows", E=3, k=2, H=256, I=256, T=5, fmt_down=fmt)
+        L = moegen.make_layer(w)
+        x = moegen.make_tokens(w, 5)
+        a = oracle.expert_rows(L, 2, x)
+        b = np.stack([oracle.expert(L, 2, x[i]) for i in range(5)])
+        assert np.array_equal(a, b)
