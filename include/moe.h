@@ -268,6 +268,29 @@ moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                           const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
                           size_t ws_bytes, hipStream_t stream);
 
+/* moe_expert_ffn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results (bit for bit) as moe_expert_ffn,
+ * with the workspace taken from a static buffer inside the library instead
+ * of a caller argument.  The caller still passes x, the buckets and y.
+ *   - The buffer is MOE_NOALLOC_WORKSPACE_BYTES (32 MiB) per GPU, part of the
+ *     library's code object: each GPU the library runs on holds it until the
+ *     process ends.  Its device address is looked up on the first call made
+ *     with that device current; the call itself allocates nothing (no
+ *     hipMalloc, no hipFree, no allocating library routine).
+ *   - A call whose workspace (moe_workspace_bytes covers it) would exceed the
+ *     buffer returns MOE_ERR_WORKSPACE before any launch.  At the decode
+ *     layer's shape (E 128, k 8, H 2048, I 768) that is above about 2,000
+ *     tokens.
+ *   - Every call on one GPU shares that GPU's buffer, which keeps the last
+ *     call's contents (nothing in it needs to start at zero): calls that
+ *     overlap on one GPU -- on different streams, or from different threads --
+ *     race and must not be issued.  Calls on different GPUs do not interact. */
+#define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+moe_status moe_expert_ffn_noalloc(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                                  const moe_buckets* b, void* y, int32_t y_dtype,
+                                  hipStream_t stream);
+
 /* Gate-weighted combine: each token's output is its selected experts'
  * outputs weighted by the gates (the mixture the pages' model computes from
  * the few experts a token uses: basalt.jgulfo.com, "Expert tiers"), written

@@ -29,6 +29,8 @@ MOE_FMT_Q8_0 = 3
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 
+MOE_NOALLOC_WORKSPACE_BYTES = 32 << 20
+
 MOE_FFN_AUTO = 0
 MOE_FFN_GEMV = 1
 MOE_FFN_GEMM = 2
@@ -95,6 +97,7 @@ SIGNATURES = {
     "moe_route": (ctypes.c_int, [_LP, _vp, _i64, _vp, _vp, _vp, _vp]),
     "moe_bucket": (ctypes.c_int, [_LP, _vp, _i64, _BP, _vp, _sz, _vp]),
     "moe_expert_ffn": (ctypes.c_int, [_LP, _vp, _i64, _BP, _vp, _i32, _vp, _sz, _vp]),
+    "moe_expert_ffn_noalloc": (ctypes.c_int, [_LP, _vp, _i64, _BP, _vp, _i32, _vp]),
     "moe_combine": (ctypes.c_int, [_LP, _vp, _i32, _BP, _vp, _i64, _vp, _vp, _vp]),
     "moe_expert_hist": (ctypes.c_int, [_LP, _BP, _vp, _i32, _i32, _vp]),
     "moe_route_bucket": (ctypes.c_int, [_LP, _vp, _i64, _vp, _vp, _vp, _BP, _vp, _sz, _vp, _i32,
@@ -196,6 +199,11 @@ def moe_bucket(desc, topk_idx, T, buckets, ws, ws_bytes, stream=None):
 def moe_expert_ffn(desc, x, T, buckets, y, y_dtype, ws, ws_bytes, stream=None):
     _check(lib().moe_expert_ffn(ctypes.byref(desc), _ptr(x), T, ctypes.byref(buckets), _ptr(y),
                                 y_dtype, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_expert_ffn_noalloc(desc, x, T, buckets, y, y_dtype, stream=None):
+    _check(lib().moe_expert_ffn_noalloc(ctypes.byref(desc), _ptr(x), T, ctypes.byref(buckets),
+                                        _ptr(y), y_dtype, _stream(stream)))
 
 
 def moe_combine(desc, y, y_dtype, buckets, topk_w, T, residual, out, stream=None):

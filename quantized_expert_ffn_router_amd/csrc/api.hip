@@ -4,7 +4,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gemv_common.h"
+
+// Workspace of moe_expert_ffn_noalloc: one copy per GPU, held until the
+// process ends.  Host code never passes this name to a kernel or a copy (on
+// the host it is only a stand-in for the symbol); it uses the device address
+// that hipGetSymbolAddress returns for the current device (scratch_ptr).
+constexpr size_t kScratchBytes = MOE_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -255,10 +264,13 @@ moe_status moe_bucket(const moe_layer_desc* L, const int32_t* topk_idx, int64_t 
   return hip_status(W, moe::launch_bucket(topk_idx, T * L->k, L->E, b, ws, stream));
 }
 
-moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
-                          const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
-                          size_t ws_bytes, hipStream_t stream) {
-  const char* W = "moe_expert_ffn";
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by moe_expert_ffn and moe_expert_ffn_noalloc.
+moe_status ffn_check(const char* W, const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                     const moe_buckets* b, const void* y, int32_t y_dtype) {
   moe_status st = check_layer(L, W);
   if (st != MOE_OK) return st;
   if ((st = check_T(T, L->k, W)) != MOE_OK) return st;
@@ -266,13 +278,18 @@ moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   if (y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "%s: y_dtype=%d", W, y_dtype);
   if (T == 0) return MOE_OK;
-  CHECK_PTR(x, W); CHECK_PTR(y, W); CHECK_PTR(ws, W); CHECK_PTR(L->experts, W);
-  size_t need = ffn_ws(L, T);
-  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
+  CHECK_PTR(x, W); CHECK_PTR(y, W); CHECK_PTR(L->experts, W);
+  if (use_gemm(L, T) && !gemm_fits(L, T))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: grouped GEMM needs H %% 256 == 0, T*H and T*k*I < 2^32",
+                W);
+  return MOE_OK;
+}
+
+// The FFN's launches (checks done, T > 0, ws holds ffn_ws(L, T) bytes).
+moe_status ffn_launch(const char* W, const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                      const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
+                      hipStream_t stream) {
   if (use_gemm(L, T)) {
-    if (!gemm_fits(L, T))
-      return fail(MOE_ERR_UNSUPPORTED, "%s: grouped GEMM needs H %% 256 == 0, T*H and T*k*I < 2^32",
-                  W);
     const FfnWs w = ffn_ws_layout(L, T);
     char* c = (char*)ws;
     return hip_status(W, moe::launch_gemm_ffn(L, x, T, b, (uint16_t*)(c + w.h),
@@ -285,6 +302,63 @@ moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   hipError_t e = moe::launch_gemv_gateup(L, x, b, max_slots, h, stream);
   if (e == hipSuccess) e = moe::launch_gemv_down(L, h, b, max_slots, y, y_dtype, stream);
   return hip_status(W, e);
+}
+
+// Device address of `scratch` on each device, looked up on the first
+// moe_expert_ffn_noalloc call made with that device current.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+moe_status scratch_ptr(const char* W, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(W, e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond %d", W, dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_status(W, g_scratch_err[dev]);
+  if (!g_scratch_ptr[dev]) return fail(MOE_ERR_HIP, "%s: no device address for the scratch", W);
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                          const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  const char* W = "moe_expert_ffn";
+  moe_status st = ffn_check(W, L, x, T, b, y, y_dtype);
+  if (st != MOE_OK || T == 0) return st;
+  CHECK_PTR(ws, W);
+  const size_t need = ffn_ws(L, T);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
+  return ffn_launch(W, L, x, T, b, y, y_dtype, ws, stream);
+}
+
+moe_status moe_expert_ffn_noalloc(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                                  const moe_buckets* b, void* y, int32_t y_dtype,
+                                  hipStream_t stream) {
+  const char* W = "moe_expert_ffn_noalloc";
+  moe_status st = ffn_check(W, L, x, T, b, y, y_dtype);
+  if (st != MOE_OK || T == 0) return st;
+  const size_t need = ffn_ws(L, T);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "%s: this call needs %zu bytes of workspace, above the library's static %zu "
+                "(use moe_expert_ffn with a caller workspace)",
+                W, need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_ptr(W, &ws)) != MOE_OK) return st;
+  return ffn_launch(W, L, x, T, b, y, y_dtype, ws, stream);
 }
 
 moe_status moe_combine(const moe_layer_desc* L, const void* y, int32_t y_dtype,
