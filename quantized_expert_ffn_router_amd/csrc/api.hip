@@ -299,7 +299,11 @@ moe_status ffn_launch(const char* W, const moe_layer_desc* L, const uint16_t* x,
   // Worst-case number of active experts; workgroups past n_active exit.
   const int max_slots = (int)((T * L->k < L->E) ? T * L->k : L->E);
   uint16_t* h = (uint16_t*)ws;  // bf16 [T*k][I], sorted order
-  hipError_t e = moe::launch_gemv_gateup(L, x, b, max_slots, h, stream);
+  // Gate/up in 32-row slices for up to 16 tokens (it redoes the weight decode
+  // per token, which costs more than it saves once experts hold many tokens).
+  hipError_t e = (T <= 16 && moe::gemv_gateup32_fits(L))
+                    ? moe::launch_gemv_gateup32(L, x, b, max_slots, h, stream)
+                    : moe::launch_gemv_gateup(L, x, b, max_slots, h, stream);
   if (e == hipSuccess) e = moe::launch_gemv_down(L, h, b, max_slots, y, y_dtype, stream);
   return hip_status(W, e);
 }

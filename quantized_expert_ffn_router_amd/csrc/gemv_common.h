@@ -210,6 +210,11 @@ hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const 
                               int max_slots, uint16_t* h, hipStream_t s);
 hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const moe_buckets* b,
                             int max_slots, void* y, int y_dtype, hipStream_t s);
+// Gate/up in 32-row slices (gemv_gateup32.hip), for the layers it fits; the
+// same h as launch_gemv_gateup.
+bool gemv_gateup32_fits(const moe_layer_desc* L);
+hipError_t launch_gemv_gateup32(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
+                                int max_slots, uint16_t* h, hipStream_t s);
 
 
 }  // namespace moe
