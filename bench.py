@@ -57,18 +57,37 @@ def parse():
                    help="tier prepare: on the device (moe_tier_prepare_async) or with a host "
                         "round trip per layer (moe_tier_prepare)")
     p.add_argument("--tiered-sets", type=int, default=4,
-                   help="distinct expert-weight sets shared round-robin by the 48 layers")
-    p.add_argument("--cpu-sample-steps", type=int, default=12)
+                   help="generated expert-weight sets used round-robin by the 48 layers")
+    p.add_argument("--tiered-shared-sets", action="store_true",
+                   help="layers share their set's pinned copy (default: one copy per layer, "
+                        "experts reordered per layer)")
+    p.add_argument("--tiered-graph-steps", type=int, default=512,
+                   help="steps of the graph-captured tiered run (0: skip)")
+    p.add_argument("--no-tiered-check", action="store_true",
+                   help="skip the all-resident run the tiered outputs are compared with")
+    p.add_argument("--cpu-sample-steps", type=int, default=12,
+                   help="decode steps of the oracle on all host cores (single-threaded: a quarter)")
+    p.add_argument("--cpu-prefill-tokens", type=int, default=1024,
+                   help="tokens of the prefill slice the oracle runs (extrapolated to 16384)")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many eager steps per batch (for profilers)")
     p.add_argument("--profile-prefill", type=int, default=0,
                    help="only run this many prefill steps (for profilers)")
+    p.add_argument("--profile-format", choices=("mixed", "q8"), default=None,
+                   help="with --profile-prefill: run that many 4096-token prefill FFN calls "
+                        "of this layer instead")
     p.add_argument("--copy-calibration", type=int, default=0,
                    help="only copy this many MiB device to device 8 times (counter calibration)")
     return p.parse_args()
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.md")
+_T0 = time.time()
+
+
+def progress(msg):
+    """A progress line on stderr (stdout carries only the result line)."""
+    print(f"[bench {time.time() - _T0:7.1f} s] {msg}", file=sys.stderr, flush=True)
 
 
 def sources_digest():
@@ -108,6 +127,29 @@ def measured_traffic(kind):
             r["write_kib_per_call"] * rec["write_factor"]) * 1024.0
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.md")
+
+
+def measured_mfma(kind):
+    """MFMA activity of one prefill FFN call from the committed counter
+    summary (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs, summed over
+    the call's kernels, and the flops the MFMA instructions issued); None when
+    the summary is missing or was taken on other kernel sources."""
+    try:
+        with open(MFMA_FILE) as f:
+            text = f.read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_digest() or kind not in rec:
+        return None
+    r = rec[kind]
+    return {"mfma_busy_frac": r["mfma_busy_frac"],
+            "mfma_flops_issued_per_call": r["mfma_flops_issued_per_call"],
+            "issued_over_useful": r["issued_over_useful"],
+            "source": "profiles/mfma_counters.md"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -133,6 +175,11 @@ def main():
             torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "copies": 8}))
+        return
+    if args.profile_prefill and args.profile_format:
+        print(json.dumps({"profile_run": True,
+                          args.profile_format: measure_format(args, q, moegen, torch, dev,
+                                                              args.profile_format)}))
         return
     if args.profile_prefill:
         args.prefill_steps = args.profile_prefill
@@ -162,6 +209,18 @@ def main():
 
         def step(i):
             return q.layer_forward(layers[i % N_LAYERS], buf, xs[i % X_POOL], B, stream=stream)
+
+        # cold: the first step of this batch size, before any warm-up (eager
+        # launches; the first batch's also pays the library's first launches)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            c0.record(stream)
+            step(0)
+            c1.record(stream)
+        torch.cuda.synchronize()
+        cold_us = c0.elapsed_time(c1) * 1e3
 
         with torch.cuda.stream(stream):
             for i in range(args.warmup):
@@ -202,50 +261,61 @@ def main():
         ffn_bytes = na * expert_bytes
         ffn_gbs = float(ffn_bytes.sum() / (ffn_ms.sum() * 1e-3) / 1e9)
 
-        # (2) whole-step throughput: the steps captured in a HIP graph
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(X_POOL):
-                step(i)
+        # (2) whole-step throughput: exactly args.steps steps, replayed from
+        # HIP graphs (one of X_POOL steps, replayed steps // X_POOL times, and
+        # one of the remaining steps % X_POOL)
+        full, rest = divmod(args.steps, X_POOL)
+        graphs = []
+        for n_in in ([X_POOL] if full else []) + ([rest] if rest else []):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n_in):
+                    step(i)
+            graphs.append((g, n_in))
         torch.cuda.synchronize()
-        reps = max(1, args.steps // X_POOL)
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):  # replay() launches on the current stream
-            g.replay()
+            for g, _ in graphs:
+                g.replay()
             torch.cuda.synchronize()
             t_start.record(stream)
-            for _ in range(reps):
-                g.replay()
+            for g, n_in in graphs:
+                for _ in range(full if n_in == X_POOL else 1):
+                    g.replay()
             t_end.record(stream)
         torch.cuda.synchronize()
         total_ms = t_start.elapsed_time(t_end)
-        steps_done = reps * X_POOL
+        steps_done = args.steps
         ms_step = total_ms / steps_done
+        progress(f"decode batch {B}: {ms_step * 1e3:.2f} us/step")
         results[B] = dict(
             batch=B, steps=steps_done, ms_per_step=ms_step, tok_per_s=B / (ms_step * 1e-3),
             ffn_us=float(ffn_ms.mean() * 1e3), active_experts=float(na.mean()),
             expert_bytes_per_step=float(ffn_bytes.mean()), ffn_GBps=ffn_gbs,
-            ffn_hbm_frac=ffn_gbs / HBM_PEAK_GBS)
-        del g
+            ffn_hbm_frac=ffn_gbs / HBM_PEAK_GBS, cold_first_step_us=cold_us)
+        del graphs
 
     if args.profile_steps:
         print(json.dumps({"profile_run": True, "batches": batches}))
         return
 
     prefill = None if args.no_prefill else measure_prefill(args, q, moegen, torch, dev)
+    progress("prefill done")
     del layers, buf
     torch.cuda.empty_cache()
     mixed = None if args.no_mixed else measure_format(args, q, moegen, torch, dev, "mixed")
     q8 = None if args.no_q8 else measure_format(args, q, moegen, torch, dev, "q8")
+    progress("format layers done")
     torch.cuda.empty_cache()
     tiered = None if args.tiered_steps <= 0 else measure_tiered(args, q, moegen, torch)
+    progress("tiered stack done")
 
     Bh = args.head_batch if args.head_batch in results else Bmax
     head = results[Bh]
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(W, host_layers[0], Bh, args.cpu_sample_steps)
+        cpu = cpu_baseline(W, host_layers[0], Bh, args.cpu_sample_steps, args.cpu_prefill_tokens)
 
     line = {
         "metric": "MoE-layer decode tok/s + expert-weight HBM GB/s (% peak); prefill TFLOP/s",
@@ -258,7 +328,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
+        "accumulate_dtype": "f32",
         "data": "synthetic",
         "config": {
             "workload": f"decode step, batch {Bh}: 128 experts, top-8, hidden 2048, "
@@ -267,7 +338,7 @@ def main():
             "weights": "nvfp4", "layers_cycled": N_LAYERS, "hip_graph": True,
         },
         "roofline": {
-            "kernel": "expert FFN (k_gemv_gateup_nvfp4<4, 2> + k_gemv_down<1, 2, 2, false>, NVFP4)",
+            "kernel": "expert FFN (k_gemv_gateup32_nvfp4<8> + k_gemv_down<1, 2, 2, false>, NVFP4)",
             "bound": "hbm",
             "achieved": round(head["ffn_GBps"], 1),
             "peak": HBM_PEAK_GBS,
@@ -335,9 +406,11 @@ def measure_prefill(args, q, moegen, torch, dev):
         "roofline": {"kernel": "grouped GEMM (k_gemm_gateup_nvfp4<true, false> + k_gemm_down<1, true, true, 1>, NVFP4)", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_ffn")},
+                     "traffic": measured_traffic("prefill_ffn"),
+                     "mfma_counters": measured_mfma("prefill_ffn")},
         "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
                         "mean": float(counts.mean())},
+        "padding": mfma_rows(counts),
     }
 
 
@@ -362,6 +435,9 @@ def measure_format(args, q, moegen, torch, dev, name):
     expert_bytes = layers[0].blob_bytes + 8
     stream = torch.cuda.Stream()
     out = {"workload": FORMAT_LAYERS[name]}
+    if args.profile_format:
+        return measure_format_prefill(args, q, moegen, torch, dev, W, layers[0], stream, out,
+                                      args.profile_prefill)
     # decode, batch 8
     B = 8
     buf = q.StepBuffers(layers[0], B)
@@ -395,12 +471,24 @@ def measure_format(args, q, moegen, torch, dev, name):
                         "active_experts": round(float(na.mean()), 2),
                         "ffn_GBps": round(gbs, 1), "ffn_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     del buf
-    # prefill, 4096 tokens
+    return measure_format_prefill(args, q, moegen, torch, dev, W, layers[0], stream, out, 10)
+
+
+def mfma_rows(counts, bm=128):
+    """Rows the grouped GEMM multiplies (each expert's rows rounded up to whole
+    128-row blocks) against the useful rows."""
+    c = np.asarray(counts, dtype=np.int64)
+    computed = int((-(-c // bm) * bm).sum())
+    return {"rows_computed": computed, "rows_useful": int(c.sum()),
+            "computed_over_useful": round(computed / max(1, int(c.sum())), 4)}
+
+
+def measure_format_prefill(args, q, moegen, torch, dev, W, L, stream, out, n):
+    """The 4096-token prefill FFN of a format layer: n timed calls after 2
+    untimed ones (HIP events on the launch stream)."""
     T = W.extra["prefill_T"]
-    L = layers[0]
     buf = q.StepBuffers(L, T, q.MOE_DTYPE_BF16)
     x = torch.from_numpy(moegen.make_tokens(W, T, step=1).view(np.int16).copy()).to(dev)
-    n = 10
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     with torch.cuda.stream(stream):
@@ -418,8 +506,57 @@ def measure_format(args, q, moegen, torch, dev, name):
     flops = 6.0 * T * W.k * W.H * W.I
     tf = flops / (ms * 1e-3) / 1e12
     out["prefill_4096"] = {"ffn_ms": round(ms, 4), "ffn_tflops": round(tf, 2),
-                           "frac_of_2500": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+                           "frac_of_2500": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "padding": mfma_rows(buf.bucket_view(W.E, T, W.k)["counts"]),
+                           "mfma_counters": measured_mfma(W.name + "_prefill")}
     return out
+
+
+PCIE_GEN5_X16_GBPS = 63.0  # 32 GT/s x 16 lanes, 128b/130b encoding, one direction
+
+
+def tier_copy_ceiling(q, moegen, torch, W, wset):
+    """Host-to-HBM rate of the tier's own copy path: one layer of the given
+    expert set in pinned host memory, no resident slots and staging for all
+    experts, 64 tokens routed (so about 220 of the 256 experts active, every
+    one a miss); moe_tier_prepare_async (planning kernel, then the copy kernel
+    reading the pinned blobs) repeated on the same buckets, timed with HIP
+    events on its stream.  Bytes: active experts x packed expert bytes."""
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    router = moegen.normal_f32(moegen.key(0, moegen.TAG_ROUTER, 777), W.E * W.H, W.w_std) \
+        .reshape(W.E, W.H)
+    stack = LayerStack([wset], [router], lambda l, e: None, L=1, k=W.k,
+                       tiered={"resident": 0, "staging": W.E, "async": True})
+    T = 64
+    x = torch.from_numpy(moegen.make_tokens(W, T, step=5, layer=777).view(np.int16).copy()).cuda()
+    stream = torch.cuda.current_stream()
+    stack.step(x, T)
+    torch.cuda.synchronize()
+    buf = stack.buf
+    bk = buf.bucket_view(W.E, T, W.k)
+    n_act = bk["n_active"]
+    reps = 8
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    q.moe_tier_prepare_async(stack.tier, 0, buf.buckets, stack.tables[0], stream)
+    a.record(stream)
+    for _ in range(reps):
+        q.moe_tier_prepare_async(stack.tier, 0, buf.buckets, stack.tables[0], stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    gbs = reps * n_act * stack.eb / (ms * 1e-3) / 1e9
+    stack.close()
+    del stack
+    torch.cuda.empty_cache()
+    return {"GBps": round(gbs, 2), "experts_per_copy": n_act,
+            "bytes_per_copy": n_act * stack_eb_bytes(W),
+            "method": "moe_tier_prepare_async with every active expert a miss, 8 repeats"}
+
+
+def stack_eb_bytes(W):
+    import quantized_expert_ffn_router_amd as q
+    return q.moe_expert_blob_bytes(W.H, W.I, q.MOE_FMT_NVFP4, W.fmt_down)
 
 
 def measure_tiered(args, q, moegen, torch):
@@ -427,41 +564,55 @@ def measure_tiered(args, q, moegen, torch):
     intermediate 512, NVFP4 gate/up, Q6_K down), 96 experts resident per layer
     in HBM, the rest in pinned host RAM copied on demand; 8 tokens per step;
     router bias Zipf(1.2) with the ranking redrawn every 256 steps (drift);
-    resident sets rebalanced from the usage histograms every 8 steps."""
+    resident sets rebalanced from the usage histograms every 8 steps.
+
+    Every layer holds its own pinned copy of its experts (4 generated weight
+    sets, experts reordered per layer), so the host footprint is that of 48
+    distinct layers.  The eager run's outputs of every step are compared bit
+    for bit with an all-resident stack's; then the whole 48-layer step is
+    captured as one HIP graph and replayed, also compared."""
+    import resource
     from quantized_expert_ffn_router_amd.stack import LayerStack
     W = moegen.WORKLOADS["tiered"]
     Lyr, R, S, T = W.extra["layers"], W.extra["resident"], 64, W.T
     drift, rb_every = W.extra["drift"], 8
+    n_steps, n_graph = args.tiered_steps, min(args.tiered_graph_steps, args.tiered_steps)
     sets = [moegen.make_layer(W, layer=200 + i) for i in range(args.tiered_sets)]
     routers = [moegen.normal_f32(moegen.key(0, moegen.TAG_ROUTER, 300 + l), W.E * W.H, W.w_std)
                .reshape(W.E, W.H) for l in range(Lyr)]
+    perms = None if args.tiered_shared_sets else \
+        [moegen.permutation(moegen.key(0, moegen.TAG_PERM, 300 + l), W.E) for l in range(Lyr)]
 
     def bias(l, epoch):
         b, _ = moegen.zipf_bias(moegen.key(0, moegen.TAG_BIAS, 300 + l, epoch), W.E, W.zipf_s,
                                 W.zipf_alpha)
         return b
 
-    stack = LayerStack(sets, routers, bias, L=Lyr, k=W.k,
-                       tiered={"resident": R, "staging": S,
-                               "async": args.tiered_prepare == "async"})
+    progress("tiered: weight sets generated")
+    h2d_ceiling = tier_copy_ceiling(q, moegen, torch, W, sets[0])
+    memlock = resource.getrlimit(resource.RLIMIT_MEMLOCK)
+    tiered_cfg = {"resident": R, "staging": S, "async": args.tiered_prepare == "async"}
+    footprint_note = None
+    try:
+        stack = LayerStack(sets, routers, bias, L=Lyr, k=W.k, tiered=tiered_cfg, layer_perms=perms)
+    except (RuntimeError, q.MoeError) as e:  # pinned host memory refused
+        if perms is None:
+            raise
+        footprint_note = f"per-layer pinned copies refused ({e}); expert sets shared by layers"
+        perms = None
+        torch.cuda.empty_cache()
+        stack = LayerStack(sets, routers, bias, L=Lyr, k=W.k, tiered=tiered_cfg)
+    ref = None if args.no_tiered_check else \
+        LayerStack(sets, routers, bias, L=Lyr, k=W.k, layer_perms=perms)
     del sets
-    # pinned host -> HBM copy ceiling on this box (one expert-sized copy stream)
-    hb = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
-    db = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-    db.copy_(hb, non_blocking=True)
-    torch.cuda.synchronize()
-    t = time.time()
-    for _ in range(4):
-        db.copy_(hb, non_blocking=True)
-    torch.cuda.synchronize()
-    h2d_ceiling = 4 * (256 << 20) / (time.time() - t) / 1e9
-    del hb, db
-    xs = [torch.from_numpy(moegen.make_tokens(W, T, step=s, layer=999).view(np.int16).copy()).cuda()
-          for s in range(16)]
+    progress("tiered: stacks built")
+    # fresh tokens for every step (a recycled pool would make the routing periodic)
+    xs = torch.from_numpy(np.stack([moegen.make_tokens(W, T, step=s, layer=999)
+                                    for s in range(n_steps)]).view(np.int16)).cuda()
     x = torch.empty_like(xs[0])
-    stream = torch.cuda.current_stream()
+    out_t = torch.empty((n_steps, T, W.H), dtype=torch.int16, device="cuda")
     for st in range(4):  # warm: first fill of the resident sets
-        x.copy_(xs[st % 16])
+        x.copy_(xs[st])
         stack.step(x, T, epoch=0)
     stack.rebalance()
     torch.cuda.synchronize()
@@ -469,9 +620,10 @@ def measure_tiered(args, q, moegen, torch):
     t = time.time()
     per_epoch = []
     prev = s0
-    for st in range(args.tiered_steps):
-        x.copy_(xs[st % 16])
+    for st in range(n_steps):
+        x.copy_(xs[st])
         stack.step(x, T, epoch=st // drift)
+        out_t[st].copy_(x)
         if (st + 1) % rb_every == 0:
             stack.rebalance()
         if (st + 1) % drift == 0:
@@ -482,39 +634,160 @@ def measure_tiered(args, q, moegen, torch):
     torch.cuda.synchronize()
     wall = time.time() - t
     s1, _ = q.moe_tier_stats_get(stack.tier)
-    stack.close()
     d = {k: s1[k] - s0[k] for k in s1}
     h2d_gbs = d["h2d_bytes"] / wall / 1e9
+
+    progress(f"tiered: {n_steps} eager steps in {wall:.1f} s")
+    # the same steps, captured: one graph of the 48-layer step, replayed on the
+    # step's input, biases refilled at epoch changes, rebalanced every 8 steps
+    graph = None
+    if n_graph > 0 and args.tiered_prepare == "async":
+        stack.use_bias_buffers(epoch=0)
+        out_g = torch.empty((n_graph, T, W.H), dtype=torch.int16, device="cuda")
+        g = stack.capture(x, T)
+        torch.cuda.synchronize()
+        g0, _ = q.moe_tier_stats_get(stack.tier)
+        t = time.time()
+        for st in range(n_graph):
+            if st % drift == 0:
+                stack.set_epoch(st // drift)
+            x.copy_(xs[st])
+            g.replay()
+            out_g[st].copy_(x)
+            if (st + 1) % rb_every == 0:
+                stack.rebalance()
+        torch.cuda.synchronize()
+        gwall = time.time() - t
+        g1, _ = q.moe_tier_stats_get(stack.tier)
+        gd = {k: g1[k] - g0[k] for k in ("hits", "misses", "h2d_bytes")}
+        graph = {"steps": n_graph, "wall_s": round(gwall, 3),
+                 "ms_per_step": round(gwall / n_graph * 1e3, 3),
+                 "tok_per_s": round(T * n_graph / gwall, 2),
+                 "miss_rate": round(gd["misses"] / max(1, gd["misses"] + gd["hits"]), 4),
+                 "h2d_GBps": round(gd["h2d_bytes"] / gwall / 1e9, 2)}
+        del g
+    host_gb = stack.host_bytes / 1e9
+    stack.close()
+    del stack
+    torch.cuda.empty_cache()
+
+    progress("tiered: graph-captured run done")
+    check, ideal_per_epoch = None, None
+    if ref is not None:
+        # The all-resident run routes exactly as the tiered one (its outputs
+        # are compared bit for bit), so it also counts, per layer, the steps
+        # in which each expert is active: at an epoch's end the best static
+        # resident set in hindsight (the R most often active experts of each
+        # layer) gives the miss rate no placement policy could beat.
+        out_r = torch.empty_like(out_t)
+        active = torch.zeros((Lyr, W.E), dtype=torch.int32, device="cuda")
+        ideal_per_epoch = []
+        for st in range(n_steps):
+            x.copy_(xs[st])
+            ref.step(x, T, epoch=st // drift, active_acc=active)
+            out_r[st].copy_(x)
+            if (st + 1) % drift == 0:
+                a = np.sort(active.cpu().numpy().astype(np.int64), axis=1)[:, ::-1]
+                ideal_per_epoch.append(round(1.0 - a[:, :R].sum() / max(1, a.sum()), 4))
+                active.zero_()
+        torch.cuda.synchronize()
+        same = (out_t == out_r).reshape(n_steps, -1).all(dim=1).cpu().numpy()
+        check = {"steps": n_steps, "equal": bool(same.all()),
+                 "first_differing_step": None if same.all() else int(np.argmin(same))}
+        if graph is not None:
+            gsame = (out_g == out_r[:n_graph]).reshape(n_graph, -1).all(dim=1).cpu().numpy()
+            graph["equal_all_resident"] = bool(gsame.all())
+        ref.close()
+        del ref, out_r
     return {
         "workload": "tiered decode: 48 layers x (256 experts, top-8, hidden 2048, intermediate "
                     "512, NVFP4 gate/up, Q6_K down), 96 resident per layer, 8 tokens/step, "
                     "Zipf(1.2) routing drifting every 256 steps",
         "prepare": args.tiered_prepare,
-        "steps": args.tiered_steps, "wall_s": round(wall, 3),
-        "tok_per_s": round(T * args.tiered_steps / wall, 2),
-        "ms_per_step": round(wall / args.tiered_steps * 1e3, 3),
+        "steps": n_steps, "wall_s": round(wall, 3),
+        "tok_per_s": round(T * n_steps / wall, 2),
+        "ms_per_step": round(wall / n_steps * 1e3, 3),
         "miss_rate": round(d["misses"] / max(1, d["misses"] + d["hits"]), 4),
         "miss_rate_per_epoch": per_epoch,
-        "h2d_GBps": round(h2d_gbs, 2), "pinned_h2d_ceiling_GBps": round(h2d_ceiling, 2),
-        "h2d_frac_of_ceiling": round(h2d_gbs / h2d_ceiling, 4),
+        "ideal_miss_rate_per_epoch": ideal_per_epoch,
+        "ideal_note": "best static resident set per epoch in hindsight: the 96 most often "
+                      "active experts of each layer over the epoch's steps",
+        "inputs": "fresh seeded tokens for every step",
+        "h2d_GBps": round(h2d_gbs, 2),
+        "copy_path_ceiling": h2d_ceiling,
+        "pcie_gen5_x16_spec_GBps": PCIE_GEN5_X16_GBPS,
+        "h2d_frac_of_ceiling": round(h2d_gbs / h2d_ceiling["GBps"], 4),
+        "h2d_frac_of_spec": round(h2d_gbs / PCIE_GEN5_X16_GBPS, 4),
+        "frac_above_1_flag": (h2d_gbs > h2d_ceiling["GBps"]) or (h2d_gbs > PCIE_GEN5_X16_GBPS),
+        "host_footprint_GB": round(host_gb, 2),
+        "per_layer_host_copies": perms is not None,
         "expert_sets": args.tiered_sets,
+        "footprint_note": footprint_note,
+        "rlimit_memlock": [int(v) for v in memlock],
+        "bit_exact_vs_all_resident": check,
+        "graph_captured": graph,
         "counters": d,
     }
 
 
-def cpu_baseline(W, L, B, n_steps):
-    """The oracle as it stands, single-threaded, on a bounded sample: n_steps
-    decode steps of batch B on one layer.  Reported in the same unit."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(W, L, B, n_steps, prefill_tokens):
+    """The oracle as it stands, on bounded samples of the same workloads:
+    decode steps of batch B on one layer, on all host cores (its OpenMP build:
+    the same loops, the listed assignments in parallel, same results) and
+    single-threaded; and a slice of the 16384-token prefill on all cores,
+    extrapolated per token.  Reported in the metric's units."""
+    import ctypes
     import moegen
     import oracle
+    threads = int(ctypes.CDLL(oracle._LIB_OMP).omp_get_max_threads()) \
+        if os.path.exists(oracle._LIB_OMP) else 1
+    oracle.lib(True)  # load before timing
     t = time.time()
     for s in range(n_steps):
-        x = moegen.make_tokens(W, B, step=10_000 + s)
-        oracle.layer(x, L)
-    dt = time.time() - t
-    return {"value": round(B * n_steps / dt, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_steps} decode steps of batch {B} on one layer, single-threaded "
-                      f"plain C in double precision ({dt:.1f} s)"}
+        oracle.layer(moegen.make_tokens(W, B, step=10_000 + s), L, parallel=True)
+    dt_all = time.time() - t
+    progress(f"cpu baseline: {n_steps} decode steps on all cores in {dt_all:.1f} s")
+    n_single = max(1, n_steps // 4)
+    t = time.time()
+    for s in range(n_single):
+        oracle.layer(moegen.make_tokens(W, B, step=20_000 + s), L)
+    dt_one = time.time() - t
+    progress(f"cpu baseline: {n_single} decode steps on one core in {dt_one:.1f} s")
+    WP = moegen.WORKLOADS["prefill"]
+    LP = moegen.make_layer(WP, layer=100)
+    xp = moegen.make_tokens(WP, prefill_tokens, step=0)
+    t = time.time()
+    oracle.layer(xp, LP, parallel=True)
+    dt_pre = time.time() - t
+    pre_tok_s = prefill_tokens / dt_pre
+    flops = 6.0 * WP.k * WP.H * WP.I  # per token, as the GPU figure counts them
+    return {
+        "value": round(B * n_steps / dt_all, 3), "unit": "tok/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n_steps} decode steps of batch {B} on one layer, plain C in double "
+                  f"precision, OpenMP build on {threads} threads ({dt_all:.1f} s)",
+        "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "single_thread": {"value": round(B * n_single / dt_one, 3), "unit": "tok/s", "cores": 1,
+                          "sample": f"{n_single} decode steps of batch {B} ({dt_one:.1f} s)"},
+        "prefill": {"value": round(pre_tok_s, 3), "unit": "tok/s", "cores": threads,
+                    "gflops_equiv": round(pre_tok_s * flops / 1e9, 3),
+                    "sample": f"{prefill_tokens}-token slice of the 16384-token prefill layer "
+                              f"(Zipf(1.1) router bias) on {threads} threads ({dt_pre:.1f} s); "
+                              f"16384 tokens extrapolated at this per-token rate: "
+                              f"{16384 / pre_tok_s:.0f} s"},
+    }
 
 
 if __name__ == "__main__":

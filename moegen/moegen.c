@@ -291,6 +291,100 @@ void moegen_q6k_normal(uint64_t key, int64_t N, int64_t K, double std,
   moegen_quant_q6k(scratch, N, K, out);
 }
 
+/* IQ3-style codebook blocks with our own grid: the 256 smallest vectors of
+ * four positive odd integers <= 15 by squared norm, then lexicographically
+ * (this generator's own copy, used to encode).  Superblock of 256 weights of a
+ * row, 102 bytes: d fp16 | 8 x 4-bit s_j (32 weights each) | 64 grid indices
+ * (4 weights each) | 32 sign bytes; w = d * (2 s_j + 1) * grid * sign. */
+static uint8_t g3_grid[256][4];
+static int16_t g3_index[8 * 8 * 8 * 8]; /* ((m-1)/2 digits, base 8) -> entry or -1 */
+
+static void g3_init(void) {
+  static int ready = 0;
+  if (ready) return;
+  for (int i = 0; i < 4096; ++i) g3_index[i] = -1;
+  int n = 0;
+  for (int norm = 4; n < 256; norm += 8)
+    for (int v = 0; v < 4096 && n < 256; ++v) {  /* v's base-8 digits in lexicographic order */
+      const int m0 = 2 * (v >> 9) + 1, m1 = 2 * ((v >> 6) & 7) + 1;
+      const int m2 = 2 * ((v >> 3) & 7) + 1, m3 = 2 * (v & 7) + 1;
+      if (m0 * m0 + m1 * m1 + m2 * m2 + m3 * m3 != norm) continue;
+      g3_grid[n][0] = (uint8_t)m0; g3_grid[n][1] = (uint8_t)m1;
+      g3_grid[n][2] = (uint8_t)m2; g3_grid[n][3] = (uint8_t)m3;
+      g3_index[v] = (int16_t)n++;
+    }
+  ready = 1;
+}
+
+/* Quantize fp32 W[N][K] (K % 256 == 0): per 32-weight sub-block the unit
+ * u_j = amax_j / 9 (9: the grid's largest magnitude), d = fp16(max_j u_j / 31),
+ * s_j = nearest (u_j / d - 1) / 2
+ * in [0, 15]; each group of 4 takes the nearest odd magnitudes when that
+ * vector is in the grid, else the grid entry nearest in L2. */
+void moegen_quant_iq3g(const float* W, int64_t N, int64_t K, uint8_t* out) {
+  g3_init();
+  const int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* w = W + n * K + b * 256;
+      uint8_t* blk = out + (n * nb + b) * 102;
+      memset(blk, 0, 102);
+      double u[8], umax = 0.0;
+      for (int j = 0; j < 8; ++j) {
+        double a = 0.0;
+        for (int i = 0; i < 32; ++i) a = fmax(a, fabs((double)w[32 * j + i]));
+        u[j] = a / 9.0;
+        umax = fmax(umax, u[j]);
+      }
+      const uint16_t dbits = f64_to_f16_rne(umax / 31.0);
+      const double d = f16_bits_to_f64(dbits);
+      blk[0] = (uint8_t)(dbits & 0xff);
+      blk[1] = (uint8_t)(dbits >> 8);
+      if (!(d > 0.0)) continue;
+      for (int j = 0; j < 8; ++j) {
+        double sj = nearbyint((u[j] / d - 1.0) / 2.0);
+        if (sj < 0) sj = 0;
+        if (sj > 15) sj = 15;
+        blk[2 + j / 2] |= (uint8_t)((int)sj << (4 * (j % 2)));
+        const double unit = d * (2.0 * sj + 1.0);
+        for (int g = 8 * j; g < 8 * j + 8; ++g) {
+          double t[4];
+          int code = 0;
+          for (int i = 0; i < 4; ++i) {
+            const float x = w[4 * g + i];
+            if (x < 0) blk[70 + (4 * g + i) / 8] |= (uint8_t)(1u << ((4 * g + i) % 8));
+            t[i] = fabs((double)x) / unit;
+            double m = 2.0 * nearbyint((t[i] - 1.0) / 2.0) + 1.0;
+            if (m < 1) m = 1;
+            if (m > 15) m = 15;
+            code = code * 8 + ((int)m - 1) / 2;
+          }
+          int e = g3_index[code];
+          if (e < 0) {
+            double best = 1e300;
+            for (int c = 0; c < 256; ++c) {
+              double err = 0.0;
+              for (int i = 0; i < 4; ++i) {
+                const double dd = t[i] - g3_grid[c][i];
+                err += dd * dd;
+              }
+              if (err < best) { best = err; e = c; }
+            }
+          }
+          blk[6 + g] = (uint8_t)e;
+        }
+      }
+    }
+  }
+}
+
+void moegen_iq3g_normal(uint64_t key, int64_t N, int64_t K, double std,
+                        float* scratch, uint8_t* out) {
+  moegen_normal_f32(key, N * K, std, scratch);
+  moegen_quant_iq3g(scratch, N, K, out);
+}
+
 void moegen_q8_0_normal(uint64_t key, int64_t N, int64_t K, double std,
                         float* scratch, uint8_t* out) {
   moegen_normal_f32(key, N * K, std, scratch);

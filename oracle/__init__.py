@@ -21,19 +21,24 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# the same source built with OpenMP: oracle_ffn_combine runs the listed
+# assignments on all host cores (timing of the CPU baseline only)
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
 
 FMT_NVFP4 = 1
 FMT_Q6K = 2
 FMT_Q8_0 = 3
+FMT_IQ3G = 4
 
 
 def build(force: bool = True) -> str:
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-fno-fast-math",
-               "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
-        subprocess.check_call(cmd)
-        os.replace(tmp, _LIB)
+    for lib_path, extra in ((_LIB, []), (_LIB_OMP, ["-fopenmp"])):
+        if force or not os.path.exists(lib_path):
+            tmp = lib_path + ".tmp"
+            cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-fno-fast-math",
+                   "-ffp-contract=off", *extra, _SRC, "-o", tmp, "-lm"]
+            subprocess.check_call(cmd)
+            os.replace(tmp, lib_path)
     return _LIB
 
 
@@ -49,46 +54,62 @@ class OracleExperts(ctypes.Structure):
 
 
 _lib = None
+_lib_omp = None
 
 
-def lib():
-    global _lib
+def lib(parallel: bool = False):
+    """The oracle library; parallel=True: the OpenMP timing build."""
+    global _lib, _lib_omp
+    if parallel:
+        if _lib_omp is None:
+            if not os.path.exists(_LIB_OMP):
+                build(force=False)
+            _lib_omp = _load(_LIB_OMP)
+        return _lib_omp
     if _lib is None:
         if not os.path.exists(_LIB):
             build(force=False)
-        L = ctypes.CDLL(_LIB)
-        vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
-        L.oracle_e2m1.restype = ctypes.c_double
-        L.oracle_e2m1.argtypes = [u32]
-        L.oracle_e4m3.restype = ctypes.c_double
-        L.oracle_e4m3.argtypes = [u32]
-        L.oracle_bf16.restype = ctypes.c_double
-        L.oracle_bf16.argtypes = [ctypes.c_uint16]
-        L.oracle_f16.restype = ctypes.c_double
-        L.oracle_f16.argtypes = [ctypes.c_uint16]
-        L.oracle_round_bf16.restype = ctypes.c_uint16
-        L.oracle_round_bf16.argtypes = [ctypes.c_double]
-        L.oracle_nvfp4_weight.restype = ctypes.c_double
-        L.oracle_nvfp4_weight.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64]
-        L.oracle_q6k_weight.restype = ctypes.c_double
-        L.oracle_q6k_weight.argtypes = [vp, i64, i64, i64]
-        L.oracle_router_logits.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp]
-        L.oracle_topk.argtypes = [vp, i64, i64, i64, i32, vp, vp]
-        L.oracle_bucket.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
-        L.oracle_hist.argtypes = [vp, i64, i32, i32, vp]
-        L.oracle_expert.argtypes = [ctypes.POINTER(OracleExperts), i64, vp, vp]
-        L.oracle_ffn_combine.argtypes = [ctypes.POINTER(OracleExperts), vp, i64, i64, vp, vp,
-                                         vp, vp, i64, vp, vp]
-        L.oracle_decode_nvfp4.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp]
-        L.oracle_decode_q6k.argtypes = [vp, i64, i64, vp]
-        L.oracle_q8_0_weight.restype = ctypes.c_double
-        L.oracle_q8_0_weight.argtypes = [vp, i64, i64, i64]
-        L.oracle_decode_q8_0.argtypes = [vp, i64, i64, vp]
-        L.oracle_expert_rows.argtypes = [ctypes.POINTER(OracleExperts), i64, vp, i64, vp]
-        L.oracle_init.argtypes = []
-        L.oracle_init()
-        _lib = L
+        _lib = _load(_LIB)
     return _lib
+
+
+def _load(path):
+    L = ctypes.CDLL(path)
+    vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+    L.oracle_e2m1.restype = ctypes.c_double
+    L.oracle_e2m1.argtypes = [u32]
+    L.oracle_e4m3.restype = ctypes.c_double
+    L.oracle_e4m3.argtypes = [u32]
+    L.oracle_bf16.restype = ctypes.c_double
+    L.oracle_bf16.argtypes = [ctypes.c_uint16]
+    L.oracle_f16.restype = ctypes.c_double
+    L.oracle_f16.argtypes = [ctypes.c_uint16]
+    L.oracle_round_bf16.restype = ctypes.c_uint16
+    L.oracle_round_bf16.argtypes = [ctypes.c_double]
+    L.oracle_nvfp4_weight.restype = ctypes.c_double
+    L.oracle_nvfp4_weight.argtypes = [vp, vp, ctypes.c_float, i64, i64, i64]
+    L.oracle_q6k_weight.restype = ctypes.c_double
+    L.oracle_q6k_weight.argtypes = [vp, i64, i64, i64]
+    L.oracle_router_logits.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp]
+    L.oracle_topk.argtypes = [vp, i64, i64, i64, i32, vp, vp]
+    L.oracle_bucket.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.oracle_hist.argtypes = [vp, i64, i32, i32, vp]
+    L.oracle_expert.argtypes = [ctypes.POINTER(OracleExperts), i64, vp, vp]
+    L.oracle_ffn_combine.argtypes = [ctypes.POINTER(OracleExperts), vp, i64, i64, vp, vp,
+                                     vp, vp, i64, vp, vp]
+    L.oracle_decode_nvfp4.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp]
+    L.oracle_decode_q6k.argtypes = [vp, i64, i64, vp]
+    L.oracle_q8_0_weight.restype = ctypes.c_double
+    L.oracle_q8_0_weight.argtypes = [vp, i64, i64, i64]
+    L.oracle_decode_q8_0.argtypes = [vp, i64, i64, vp]
+    L.oracle_iq3g_weight.restype = ctypes.c_double
+    L.oracle_iq3g_weight.argtypes = [vp, i64, i64, i64]
+    L.oracle_decode_iq3g.argtypes = [vp, i64, i64, vp]
+    L.oracle_iq3g_grid.argtypes = [vp]
+    L.oracle_expert_rows.argtypes = [ctypes.POINTER(OracleExperts), i64, vp, i64, vp]
+    L.oracle_init.argtypes = []
+    L.oracle_init()
+    return L
 
 
 def _p(a):
@@ -141,6 +162,21 @@ def decode_q8_0(blocks: np.ndarray, K: int) -> np.ndarray:
     N = blocks.shape[0]
     out = np.empty((N, K), np.float64)
     lib().oracle_decode_q8_0(_p(np.ascontiguousarray(blocks)), N, K, _p(out))
+    return out
+
+
+def decode_iq3g(blocks: np.ndarray, K: int) -> np.ndarray:
+    """IQ3-style grid rows [N][K/256*102] -> float64 [N][K]."""
+    N = blocks.shape[0]
+    out = np.empty((N, K), np.float64)
+    lib().oracle_decode_iq3g(_p(np.ascontiguousarray(blocks)), N, K, _p(out))
+    return out
+
+
+def iq3g_grid() -> np.ndarray:
+    """The oracle's 256-entry grid of the IQ3-style format, uint8 [256][4]."""
+    out = np.empty((256, 4), np.uint8)
+    lib().oracle_iq3g_grid(_p(out))
     return out
 
 
@@ -216,8 +252,9 @@ def expert_rows(L, e: int, x_rows: np.ndarray) -> np.ndarray:
 
 
 def ffn_combine(L, x: np.ndarray, idx: np.ndarray, w: np.ndarray, residual=None,
-                tokens=None, want_y: bool = False):
-    """Layer output bf16 bits [T][H] (rows of unlisted tokens are zero)."""
+                tokens=None, want_y: bool = False, parallel: bool = False):
+    """Layer output bf16 bits [T][H] (rows of unlisted tokens are zero).
+    parallel: the OpenMP build (same results, all host cores)."""
     s = experts_struct(L)
     x = np.ascontiguousarray(x, np.uint16)
     T = x.shape[0]
@@ -225,7 +262,7 @@ def ffn_combine(L, x: np.ndarray, idx: np.ndarray, w: np.ndarray, residual=None,
     out = np.zeros((T, L.H), np.uint16)
     y = np.zeros((T * k, L.H), np.float64) if want_y else None
     tok = None if tokens is None else np.ascontiguousarray(tokens, np.int32)
-    lib().oracle_ffn_combine(ctypes.byref(s), _p(x), T, k,
+    lib(parallel).oracle_ffn_combine(ctypes.byref(s), _p(x), T, k,
                              _p(np.ascontiguousarray(idx, np.int32)),
                              _p(np.ascontiguousarray(w, np.float32)),
                              _p(None if residual is None else np.ascontiguousarray(residual, np.uint16)),
@@ -239,9 +276,10 @@ def route(x, L, order: int = 0):
     return logits, idx, w
 
 
-def layer(x, L, residual=None, tokens=None):
-    """Full layer: route, bucket, experts and combine for the given tokens."""
+def layer(x, L, residual=None, tokens=None, parallel: bool = False):
+    """Full layer: route, bucket, experts and combine for the given tokens
+    (parallel: the experts on all host cores, same results)."""
     logits, idx, w = route(x, L)
     b = bucket(idx, L.E)
-    out = ffn_combine(L, x, idx, w, residual, tokens)
+    out = ffn_combine(L, x, idx, w, residual, tokens, parallel=parallel)
     return dict(logits=logits, idx=idx, w=w, buckets=b, out=out)

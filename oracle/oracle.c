@@ -246,11 +246,65 @@ double oracle_q8_0_weight(const uint8_t* blocks, int64_t K, int64_t n, int64_t k
   return oracle_f16(dbits) * (double)(int8_t)b[2 + k % 32];
 }
 
+/* IQ3-style codebook blocks with a grid of our own (the IQ3 formats of the
+ * pages' packs, basalt.jgulfo.com "Community", decode four weights at a time
+ * through a grid the pages do not give; this reading keeps the structure --
+ * an 8-bit index per 4 weights into a grid of odd magnitudes, one sign bit
+ * per weight, a small odd multiplier per 32 weights, an fp16 scale per 256 --
+ * and defines the grid itself):
+ *   grid = the 256 smallest vectors (m0, m1, m2, m3) of positive odd integers
+ *   up to 15, ordered by m0^2 + m1^2 + m2^2 + m3^2 and then lexicographically;
+ *   entry e is the e-th.
+ * Superblock b = k/256 of row n, 102 bytes:
+ *   d fp16 little-endian[2] | s[4]: 4-bit s_j of sub-block j = 32 weights
+ *   (byte j/2, low nibble for even j) | idx[64]: grid entry of weights 4g..4g+3
+ *   | sgn[32]: bit k%8 of byte k/8 set = negative;
+ *   value = d * (2 s_j + 1) * grid[idx[g]][k % 4] * (-1)^sign. */
+static uint8_t iq3g_grid[256][4];
+static int iq3g_ready = 0;
+
+/* Walk the squared norms upward (a sum of four odd squares is 4 mod 8) and,
+ * within a norm, the vectors in lexicographic order, until 256 are taken. */
+static void iq3g_build(void) {
+  int n = 0;
+  for (int norm = 4; n < 256; norm += 8)
+    for (int a = 1; a <= 15 && n < 256; a += 2)
+      for (int b = 1; b <= 15 && n < 256; b += 2)
+        for (int c = 1; c <= 15 && n < 256; c += 2)
+          for (int d = 1; d <= 15 && n < 256; d += 2)
+            if (a * a + b * b + c * c + d * d == norm) {
+              iq3g_grid[n][0] = (uint8_t)a;
+              iq3g_grid[n][1] = (uint8_t)b;
+              iq3g_grid[n][2] = (uint8_t)c;
+              iq3g_grid[n][3] = (uint8_t)d;
+              ++n;
+            }
+  iq3g_ready = 1;
+}
+
+/* The grid as 256 x 4 bytes (for the tests). */
+void oracle_iq3g_grid(uint8_t* out) {
+  if (!iq3g_ready) iq3g_build();
+  memcpy(out, iq3g_grid, sizeof(iq3g_grid));
+}
+
+double oracle_iq3g_weight(const uint8_t* blocks, int64_t K, int64_t n, int64_t k) {
+  if (!iq3g_ready) iq3g_build();
+  const uint8_t* b = blocks + (n * (K / 256) + k / 256) * 102;
+  const int r = (int)(k % 256), j = r / 32;
+  const uint16_t dbits = (uint16_t)(b[0] | (b[1] << 8));
+  const int s = (b[2 + j / 2] >> (4 * (j % 2))) & 15;
+  const int m = iq3g_grid[b[6 + r / 4]][r % 4];
+  const int neg = (b[70 + r / 8] >> (r % 8)) & 1;
+  const double v = oracle_f16(dbits) * (double)(2 * s + 1) * (double)m;
+  return neg ? -v : v;
+}
+
 /* ------------------------------------------------------------------ */
 /* Expert FFN and combine                                               */
 /* ------------------------------------------------------------------ */
 
-enum { ORACLE_FMT_NVFP4 = 1, ORACLE_FMT_Q6K = 2, ORACLE_FMT_Q8_0 = 3 };
+enum { ORACLE_FMT_NVFP4 = 1, ORACLE_FMT_Q6K = 2, ORACLE_FMT_Q8_0 = 3, ORACLE_FMT_IQ3G = 4 };
 
 /* Expert weights in the canonical layouts, stacked over experts. */
 typedef struct oracle_experts {
@@ -261,7 +315,8 @@ typedef struct oracle_experts {
   const uint8_t* up_q;
   const uint8_t* up_s;
   const float* up_ts;
-  const uint8_t* down_q;   /* NVFP4 [E][H][I/2], Q6_K [E][H][I/256*210] or Q8_0 [E][H][I/32*34] */
+  const uint8_t* down_q;   /* NVFP4 [E][H][I/2], Q6_K [E][H][I/256*210], Q8_0 [E][H][I/32*34]
+                              or IQ3G [E][H][I/256*102] */
   const uint8_t* down_s;   /* NVFP4 [E][H][I/16], NULL for Q6_K */
   const float* down_ts;    /* NVFP4 [E], NULL for Q6_K */
 } oracle_experts;
@@ -272,6 +327,8 @@ static double down_weight(const oracle_experts* X, int64_t e, int64_t n, int64_t
     return oracle_q6k_weight(X->down_q + e * H * (I / 256) * 210, I, n, i);
   if (X->fmt_down == ORACLE_FMT_Q8_0)
     return oracle_q8_0_weight(X->down_q + e * H * (I / 32) * 34, I, n, i);
+  if (X->fmt_down == ORACLE_FMT_IQ3G)
+    return oracle_iq3g_weight(X->down_q + e * H * (I / 256) * 102, I, n, i);
   return oracle_nvfp4_weight(X->down_q + e * H * (I / 2), X->down_s + e * H * (I / 16),
                              X->down_ts[e], I, n, i);
 }
@@ -347,7 +404,10 @@ void oracle_expert_rows(const oracle_experts* X, int64_t e, const uint16_t* x, i
 }
 
 /* Builds the decode tables up front (before any concurrent calls). */
-void oracle_init(void) { tables_init(); }
+void oracle_init(void) {
+  tables_init();
+  if (!iq3g_ready) iq3g_build();
+}
 
 /* Layer output for the listed tokens (all T when tokens == NULL):
  *   out[t] = bf16( residual[t] + sum_{j<k} w[t][j] * y_{t,j} ),
@@ -359,6 +419,36 @@ void oracle_ffn_combine(const oracle_experts* X, const uint16_t* x, int64_t T, i
                         const int32_t* tokens, int64_t n_tokens, uint16_t* out,
                         double* y_out) {
   int64_t H = X->H;
+#ifdef _OPENMP
+  /* The timing build (liboracle_omp.so, the CPU baseline on all host cores):
+   * every listed assignment's expert output first, in parallel, then the
+   * same per-token sums in the same order as the plain build below, so the
+   * results are identical. */
+  {
+    int64_t n_q = tokens ? n_tokens : T;
+    double* ys = (double*)malloc(sizeof(double) * (size_t)(n_q * k * H));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t qa = 0; qa < n_q * k; ++qa) {
+      int64_t q = qa / k, j = qa % k;
+      int64_t t = tokens ? tokens[q] : q;
+      oracle_expert(X, idx[t * k + j], x + t * H, ys + qa * H);
+    }
+    for (int64_t q = 0; q < n_q; ++q) {
+      int64_t t = tokens ? tokens[q] : q;
+      for (int64_t n = 0; n < H; ++n) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < k; ++j) acc += (double)w[t * k + j] * ys[(q * k + j) * H + n];
+        double r = residual ? oracle_bf16(residual[t * H + n]) : 0.0;
+        out[t * H + n] = oracle_round_bf16(r + acc);
+      }
+      if (y_out)
+        for (int64_t j = 0; j < k; ++j)
+          memcpy(y_out + (t * k + j) * H, ys + (q * k + j) * H, sizeof(double) * (size_t)H);
+    }
+    free(ys);
+    return;
+  }
+#endif
   double* y = (double*)malloc(sizeof(double) * (size_t)H);
   double* acc = (double*)malloc(sizeof(double) * (size_t)H);
   int64_t n_list = tokens ? n_tokens : T;
@@ -394,4 +484,9 @@ void oracle_decode_q6k(const uint8_t* blocks, int64_t N, int64_t K, double* out)
 void oracle_decode_q8_0(const uint8_t* blocks, int64_t N, int64_t K, double* out) {
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) out[n * K + k] = oracle_q8_0_weight(blocks, K, n, k);
+}
+
+void oracle_decode_iq3g(const uint8_t* blocks, int64_t N, int64_t K, double* out) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) out[n * K + k] = oracle_iq3g_weight(blocks, K, n, k);
 }

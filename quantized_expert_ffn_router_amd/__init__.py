@@ -26,6 +26,7 @@ MOE_ERR_HOST_ALLOC = -6
 MOE_FMT_NVFP4 = 1
 MOE_FMT_Q6K = 2
 MOE_FMT_Q8_0 = 3
+MOE_FMT_IQ3G = 4
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 
@@ -315,6 +316,13 @@ class StepBuffers:
         self.y = torch.empty((max(T_max * k, 1), H), dtype=ydt, device=dev)
         self.out = torch.empty((T_max, H), dtype=torch.int16, device=dev)
         self.hist = torch.zeros(E, dtype=torch.int32, device=dev)
+
+    def counts_view(self, E: int):
+        """The per-expert assignment counts of the last step as an int32
+        device tensor view [E] (no copy)."""
+        import torch
+        off = self.buckets.counts - self.bucket_buf.data_ptr()
+        return self.bucket_buf[off:off + 4 * E].view(torch.int32)
 
     def bucket_view(self, E: int, T: int, k: int) -> dict:
         """Host copies of the bucket outputs of the last step (synchronizes)."""

@@ -223,3 +223,86 @@ def test_tiered_full_size_equals_all_resident_bit_exact():
         check_out(ins[l + 1], out["out"])
     tiered.close()
     ref.close()
+
+
+def _permuted(w, perm):
+    """Layer weights whose expert e is expert perm[e] of w (host arrays)."""
+    d = dict(w.__dict__)
+    for name in ("gate_q", "gate_s", "gate_ts", "up_q", "up_s", "up_ts", "down_q", "down_s",
+                 "down_ts"):
+        if d[name] is not None:
+            d[name] = np.ascontiguousarray(d[name][perm])
+    return moegen.LayerWeights(**d)
+
+
+def test_per_layer_copies_with_permuted_experts():
+    """layer_perms gives every layer its own copy of its set's blobs with the
+    experts reordered: the tiered stack (per-layer pinned copies) equals the
+    all-resident stack (per-layer device copies) bit for bit, and a layer
+    matches the oracle run on the correspondingly permuted host weights."""
+    import torch
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    L = 4
+    w, sets, routers, bias = _stack_inputs(L=L)
+    perms = [np.random.default_rng(50 + l).permutation(w.E) for l in range(L)]
+    ref = LayerStack(sets, routers, bias, L=L, k=w.k, layer_perms=perms)
+    tiered = LayerStack(sets, routers, bias, L=L, k=w.k, layer_perms=perms,
+                        tiered={"resident": 16, "staging": 32, "async": True})
+    assert tiered.host_bytes == L * w.E * tiered.eb
+    trace = []
+    for st in range(6):
+        x0 = moegen.make_tokens(w, 8, step=st).view(np.int16)
+        xa = torch.from_numpy(x0.copy()).cuda()
+        xb = torch.from_numpy(x0.copy()).cuda()
+        ref.step(xa, 8, epoch=st // 2, trace=trace if st == 5 else None)
+        tiered.step(xb, 8, epoch=st // 2)
+        if (st + 1) % 2 == 0:
+            tiered.rebalance()
+        torch.cuda.synchronize()
+        assert torch.equal(xa, xb), f"step {st} differs"
+    ins = [t.cpu().numpy().view(np.uint16) for t in trace] + [xa.cpu().numpy().view(np.uint16)]
+    for l in (1, L - 1):
+        Lw = _permuted(sets[l % len(sets)], perms[l])
+        layer = moegen.LayerWeights(**{**Lw.__dict__, "w_router": routers[l], "bias": bias(l, 2)})
+        out = oracle.layer(ins[l], layer, residual=ins[l])
+        check_out(ins[l + 1], out["out"])
+    tiered.close()
+    ref.close()
+
+
+def test_captured_tiered_step_equals_eager_all_resident():
+    """The whole tiered step (route, bucket, device-side prepare, FFN and
+    combine of every layer) captured once as a HIP graph and replayed 10
+    times, with eager rebalances, epoch changes of the router bias and host
+    synchronizations between the replays: every replay's output equals the
+    eager all-resident step's bit for bit, and the tier's device counters
+    advance as in eager steps."""
+    import torch
+    import quantized_expert_ffn_router_amd as q
+    from quantized_expert_ffn_router_amd.stack import LayerStack
+    w, sets, routers, bias = _stack_inputs()
+    ref = LayerStack(sets, routers, bias, L=3, k=w.k)
+    tiered = LayerStack(sets, routers, bias, L=3, k=w.k,
+                        tiered={"resident": 16, "staging": 32, "async": True})
+    tiered.use_bias_buffers(epoch=0)
+    xg = torch.empty((8, w.H), dtype=torch.int16, device="cuda")
+    g = tiered.capture(xg, 8)
+    torch.cuda.synchronize()
+    s0, _ = q.moe_tier_stats_get(tiered.tier)
+    for st in range(10):
+        x0 = moegen.make_tokens(w, 8, step=st).view(np.int16)
+        xa = torch.from_numpy(x0.copy()).cuda()
+        ref.step(xa, 8, epoch=st // 3)
+        tiered.set_epoch(st // 3)
+        xg.copy_(torch.from_numpy(x0.copy()))
+        g.replay()
+        if (st + 1) % 2 == 0:
+            tiered.rebalance()
+        torch.cuda.synchronize()
+        assert torch.equal(xa, xg), f"replay {st} differs"
+    s1, _ = q.moe_tier_stats_get(tiered.tier)
+    assert s1["hits"] + s1["misses"] > s0["hits"] + s0["misses"]
+    assert s1["misses"] > s0["misses"] and s1["promotions"] > 0
+    del g
+    tiered.close()
+    ref.close()

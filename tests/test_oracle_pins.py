@@ -6,6 +6,7 @@ bfloat16 / numpy float16 decoders, exact rational arithmetic, brute-force
 sorting, numpy's stable argsort, scipy's softmax and expit, and a dense fp64
 reference of the whole layer on the tiny workload.
 """
+import itertools
 import math
 from fractions import Fraction
 
@@ -310,6 +311,8 @@ def _dense_reference(L, x, w_idx, w_val, residual=None):
             Wd = dq(L.down_q[e], L.down_s[e], L.down_ts[e])
         elif L.fmt_down == moegen.FMT_Q8_0:
             Wd = oracle.decode_q8_0(L.down_q[e], L.I)
+        elif L.fmt_down == moegen.FMT_IQ3G:
+            Wd = oracle.decode_iq3g(L.down_q[e], L.I)
         else:
             Wd = oracle.decode_q6k(L.down_q[e], L.I)
         g = xf @ Wg.T
@@ -369,6 +372,19 @@ def test_ffn_q8_0_down_dense_reference():
     _bf16_close(out, ref)
 
 
+def test_ffn_iq3g_down_dense_reference():
+    W = moegen.Workload("iq3", E=4, k=2, H=256, I=256, T=3, fmt_down=moegen.FMT_IQ3G)
+    L = moegen.make_layer(W)
+    x = moegen.make_tokens(W, W.T)
+    _, idx, w = oracle.route(x, L)
+    out, y = oracle.ffn_combine(L, x, idx, w, want_y=True)
+    ref, ys = _dense_reference(L, x, idx, w)
+    for t in range(W.T):
+        for j in range(W.k):
+            np.testing.assert_allclose(y[t * W.k + j], ys[idx[t, j]][t], rtol=1e-12, atol=1e-15)
+    _bf16_close(out, ref)
+
+
 def test_ffn_zero_gate_gives_residual():
     W = moegen.WORKLOADS["tiny"]
     L = moegen.make_layer(W)
@@ -403,3 +419,128 @@ def test_expert_rows_equals_expert():
         a = oracle.expert_rows(L, 2, x)
         b = np.stack([oracle.expert(L, 2, x[i]) for i in range(5)])
         assert np.array_equal(a, b)
+
+
+def test_openmp_timing_build_gives_the_same_results():
+    """The all-cores build of the oracle (CPU baseline timing only) computes
+    the same expert outputs and layer output bit for bit."""
+    w = moegen.Workload(name="omp", E=16, k=4, H=256, I=256, T=9)
+    L = moegen.make_layer(w)
+    x = moegen.make_tokens(w, 9)
+    res = moegen.make_residual(w, 9)
+    logits, idx, wt = oracle.route(x, L)
+    a, ya = oracle.ffn_combine(L, x, idx, wt, res, want_y=True)
+    b, yb = oracle.ffn_combine(L, x, idx, wt, res, want_y=True, parallel=True)
+    assert np.array_equal(a, b) and np.array_equal(ya, yb)
+    toks = [1, 4, 8]
+    c = oracle.ffn_combine(L, x, idx, wt, None, toks, parallel=True)
+    assert np.array_equal(c[toks], oracle.ffn_combine(L, x, idx, wt, None, toks)[toks])
+
+
+# ---------------------------------------------------------------- IQ3-style grid
+
+def _grid_by_sorting():
+    """The grid's definition by brute force: all 8^4 vectors of odd integers
+    1..15, sorted by (squared norm, lexicographic), the first 256."""
+    odd = range(1, 16, 2)
+    allv = sorted(itertools.product(odd, repeat=4), key=lambda v: (sum(c * c for c in v), v))
+    return np.array(allv[:256], np.uint8)
+
+
+def test_iq3g_grid_is_the_256_smallest_odd_vectors():
+    """The oracle's grid (built by walking norms upward) equals the sorted
+    brute-force enumeration; its shells are whole up to norm 108 (247
+    vectors), and the last 9 entries are the lexicographically first of norm
+    116, so the largest magnitude is 9."""
+    g = oracle.iq3g_grid()
+    np.testing.assert_array_equal(g, _grid_by_sorting())
+    norms = (g.astype(np.int64) ** 2).sum(1)
+    assert len({tuple(v) for v in g}) == 256
+    assert (np.diff(norms) >= 0).all() and (g % 2 == 1).all()
+    assert (norms <= 108).sum() == 247 and (norms == 116).sum() == 9
+    n108 = sum(1 for v in itertools.product(range(1, 16, 2), repeat=4)
+               if sum(c * c for c in v) <= 108)
+    assert n108 == 247
+    assert g.max() == 9 and tuple(g[0]) == (1, 1, 1, 1)
+
+
+def test_iq3g_decode_closed_form():
+    """Blocks packed by the documented byte layout from random integers:
+    decode equals d * (2 s + 1) * grid[idx][k % 4] * sign, with the grid from
+    the brute-force enumeration and d from numpy's float16."""
+    rng = np.random.default_rng(11)
+    G = _grid_by_sorting().astype(np.float64)
+    N, K = 3, 512
+    nb = K // 256
+    d = (rng.standard_normal((N, nb)) * 1e-3).astype(np.float16)
+    s = rng.integers(0, 16, size=(N, K // 32))
+    idx = rng.integers(0, 256, size=(N, K // 4))
+    neg = rng.integers(0, 2, size=(N, K))
+    blocks = np.zeros((N, nb, 102), np.uint8)
+    for n in range(N):
+        for b in range(nb):
+            blocks[n, b, 0:2] = np.frombuffer(d[n, b].tobytes(), np.uint8)
+            for j in range(8):
+                blocks[n, b, 2 + j // 2] |= s[n, 8 * b + j] << (4 * (j % 2))
+            blocks[n, b, 6:70] = idx[n, 64 * b:64 * b + 64]
+            for r in range(256):
+                blocks[n, b, 70 + r // 8] |= neg[n, 256 * b + r] << (r % 8)
+    got = oracle.decode_iq3g(blocks.reshape(N, -1), K)
+    for n in range(N):
+        for k in range(K):
+            exp = float(d[n, k // 256]) * (2 * s[n, k // 32] + 1) * G[idx[n, k // 4], k % 4]
+            assert got[n, k] == (-exp if neg[n, k] else exp)
+
+
+def test_iq3g_generator_roundtrip_on_grid():
+    """Weights that are exactly d * (2 s_j + 1) * (grid vector) * sign, with
+    d = 2^-10, one sub-block at s = 15 and a magnitude 9 in every sub-block
+    (so the quantizer's unit amax / 9 and scale max / 31 are exact), survive
+    quantize -> decode exactly; an all-zero superblock decodes to zeros."""
+    rng = np.random.default_rng(12)
+    G = _grid_by_sorting().astype(np.float64)
+    nine = np.flatnonzero((G == 9).any(1))
+    N, K = 2, 512
+    W = np.zeros((N, K))
+    for n in range(N):
+        for j in range(K // 32):
+            sj = 15 if j % 8 == 0 else int(rng.integers(0, 16))
+            unit = 2.0 ** -10 * (2 * sj + 1)
+            for g in range(8):
+                e = int(nine[rng.integers(len(nine))]) if g == 0 else int(rng.integers(256))
+                sign = np.where(rng.integers(0, 2, 4) > 0, -1.0, 1.0)
+                W[n, 32 * j + 4 * g:32 * j + 4 * g + 4] = unit * G[e] * sign
+    W[1, 256:] = 0.0
+    W = W.astype(np.float32)
+    assert (W.astype(np.float64) == W).all()
+    dec = oracle.decode_iq3g(moegen.quant_iq3g(W), K)
+    np.testing.assert_array_equal(dec, W.astype(np.float64))
+
+
+def test_iq3g_generator_signs_and_error_bound():
+    """On Gaussian weights every nonzero decoded weight keeps the input's
+    sign, and each group's decoded vector is the grid entry (times its unit)
+    nearest to the input whenever the input's nearest odd magnitudes form a
+    grid vector."""
+    rng = np.random.default_rng(13)
+    W = (rng.standard_normal((4, 256)) * 0.02).astype(np.float32)
+    q = moegen.quant_iq3g(W)
+    dec = oracle.decode_iq3g(q, 256)
+    nz = dec != 0
+    assert (np.sign(dec[nz]) == np.sign(W[nz])).all()
+    G = _grid_by_sorting()
+    gset = {tuple(v) for v in G}
+    blk = q.reshape(4, 102)
+    d = blk[:, :2].copy().view(np.float16).astype(np.float64)[:, 0]
+    checked = 0
+    for n in range(4):
+        for g in range(64):
+            j = g // 8
+            s = (blk[n, 2 + j // 2] >> (4 * (j % 2))) & 15
+            unit = d[n] * (2 * int(s) + 1)
+            t = np.abs(W[n, 4 * g:4 * g + 4].astype(np.float64)) / unit
+            m = np.clip(2 * np.rint((t - 1) / 2) + 1, 1, 15).astype(int)
+            if tuple(m) in gset:
+                np.testing.assert_array_equal(np.abs(dec[n, 4 * g:4 * g + 4]), unit * m)
+                checked += 1
+    assert checked > 200
