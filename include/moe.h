@@ -2,7 +2,7 @@
  * moe.h -- C ABI of libmoe, a single-GPU (MI355X / gfx950) implementation of
  * the mixture-of-experts layer of a Basalt-style local inference engine:
  * router logits, softmax top-k gating, token-to-expert bucketing, block-
- * quantized (NVFP4, Q6_K-style, Q8_0) SwiGLU expert FFNs with the dequantization
+ * quantized (NVFP4, Q6_K-style, Q8_0, IQ3-style) SwiGLU expert FFNs with the dequantization
  * fused into the matmuls, the gate-weighted combine, and the per-step expert
  * usage histogram that decides which experts stay resident.
  *
@@ -22,7 +22,11 @@
  *   - Q8_0 is the 8-bit GGUF format the pages measure quality against and
  *     keep for Basalt's dense projections -- basalt.jgulfo.com, "All the
  *     numbers" (the quality table and the engine notes); here it is offered
- *     as a down-projection format of the experts.
+ *     as a down-projection format of the experts;
+ *   - community packs run IQ3 GGUF files -- basalt.jgulfo.com, "Community";
+ *     their grids are not on the pages, so MOE_FMT_IQ3G keeps the IQ3
+ *     structure (grid indices per 4 weights, sign bits, small scales) with a
+ *     grid defined here (below), offered as a down-projection format.
  * The pages give no formula.  The arithmetic below is the plainest reading;
  * each entry point states it.
  *
@@ -42,7 +46,7 @@
  *   - bf16 values are passed as uint16_t bit patterns.
  *
  * Supported shapes: 1 <= k <= min(E, 64), E <= 1024, H % 128 == 0,
- * 128 <= H <= 8192, I % 128 == 0 (NVFP4, Q8_0) or I % 256 == 0 (Q6_K),
+ * 128 <= H <= 8192, I % 128 == 0 (NVFP4, Q8_0) or I % 256 == 0 (Q6_K, IQ3G),
  * I <= 8192.
  */
 #ifndef MOE_H
@@ -73,6 +77,8 @@ typedef enum moe_status {
 #define MOE_FMT_NVFP4 1  /* E2M1 codes, E4M3 scale per 16 along K, fp32 per-tensor scale */
 #define MOE_FMT_Q6K 2    /* 256-element superblocks: 16 x int8 sub-scales, fp16 scale, 6-bit codes */
 #define MOE_FMT_Q8_0 3   /* 32-element blocks: fp16 scale, 32 int8 codes (down projection only) */
+#define MOE_FMT_IQ3G 4   /* 256-element superblocks: fp16 scale, 4-bit odd multipliers per 32,
+                            8-bit grid index per 4, sign bits (down projection only) */
 
 /* Element types of the expert-output buffer y. */
 #define MOE_DTYPE_F32 0
@@ -119,12 +125,21 @@ const char* moe_last_error(void);
  *   Q8_0 matrix W[N][K]: row n is K/32 blocks of 34 bytes: d fp16
  *     little-endian[2], then the int8 codes q[32] of elements 32b..32b+31;
  *     w = d * q.
+ *   IQ3G matrix W[N][K] (3.19 bits per weight): row n is K/256 superblocks of
+ *     102 bytes: d fp16 little-endian[2]; s[4], the 4-bit multiplier s_j of
+ *     sub-block j (elements 32j..32j+31) in byte j/2 (low nibble for even j);
+ *     idx[64], the grid entry of elements 4g..4g+3; sgn[32], bit i%8 of byte
+ *     i/8 set when element i is negative;
+ *     w = d * (2 s_j + 1) * grid[idx[i/4]][i%4] * (sgn ? -1 : 1),
+ *     grid = the 256 smallest vectors of four positive odd integers <= 15,
+ *     ordered by squared norm, then lexicographically (entry 0 = (1,1,1,1);
+ *     every magnitude is at most 9).
  *   Gate and up are [I][H] (K = H); down is [H][I] (K = I).
  *
  * The GPU kernels read a packed "blob" per expert (a device-friendly
  * re-arrangement of the same bytes, 16-byte granules transposed so that one
  * wavefront load covers consecutive rows).  moe_expert_blob_bytes gives its
- * size; moe_pack_experts writes it.  With Q6_K or Q8_0 down weights the blob
+ * size; moe_pack_experts writes it.  With Q6_K, Q8_0 or IQ3G down weights the blob
  * ends with a 256-byte section holding one int32 computed by the pack from
  * the expert's block scales: the power of two by which the grouped GEMM
  * scales that expert's fp16 down weights (so none can overflow fp16, for any
@@ -136,7 +151,7 @@ typedef struct moe_expert_ref {
   const void* blob;   /* device pointer to the packed expert (256-byte aligned) */
   float ts_gate;      /* NVFP4 per-tensor scales */
   float ts_up;
-  float ts_down;      /* ignored when the down projection is Q6_K or Q8_0 */
+  float ts_down;      /* ignored when the down projection is Q6_K, Q8_0 or IQ3G */
   uint32_t reserved;  /* 0 (not read by the library) */
 } moe_expert_ref;
 
@@ -146,7 +161,8 @@ size_t moe_expert_blob_bytes(int32_t H, int32_t I, int32_t fmt_gate_up, int32_t 
 /* Pack E experts from the canonical layouts (device arrays stacked over
  * experts: gate_q [E][I][H/2], gate_s [E][I][H/16], up likewise, down_q
  * [E][H][I/2] and down_s [E][H][I/16] for NVFP4, down_q [E][H][I/256*210]
- * for Q6_K or down_q [E][H][I/32*34] for Q8_0, down_s == NULL for both) into
+ * for Q6_K, [E][H][I/32*34] for Q8_0 or [E][H][I/256*102] for IQ3G, down_s
+ * == NULL for those three) into
  * E blobs at blobs + e * blob_stride.
  * blob_stride >= moe_expert_blob_bytes(...) and a multiple of 256. */
 moe_status moe_pack_experts(int32_t E, int32_t H, int32_t I, int32_t fmt_gate_up,
@@ -166,7 +182,7 @@ typedef struct moe_layer_desc {
   int32_t H;            /* hidden size */
   int32_t I;            /* expert intermediate size */
   int32_t fmt_gate_up;  /* MOE_FMT_NVFP4 */
-  int32_t fmt_down;     /* MOE_FMT_NVFP4, MOE_FMT_Q6K or MOE_FMT_Q8_0 */
+  int32_t fmt_down;     /* MOE_FMT_NVFP4, MOE_FMT_Q6K, MOE_FMT_Q8_0 or MOE_FMT_IQ3G */
   int32_t renormalize;  /* 1: softmax renormalised over the selected k; 0: full softmax */
   int32_t ffn_mode;     /* MOE_FFN_AUTO (0), MOE_FFN_GEMV or MOE_FFN_GEMM */
   const moe_expert_ref* experts;  /* device [E] */

@@ -21,9 +21,16 @@
 //                         bytes 16*(c%2)..);
 //                         scales granule (g, n), g < K/128, 8 bytes = the fp16
 //                         scales of blocks 4g..4g+3.
+//   IQ3G matrix [N][K]:   idx  granule (c, n), c < K/64, 16 bytes = the grid
+//                         indices of elements 64c..64c+63 (superblock c/4);
+//                         sign granule (c, n), c < K/128, 16 bytes = the sign
+//                         bits of elements 128c..128c+127 (superblock c/2);
+//                         sc granule (s, n), s < K/256, 8 bytes = d (fp16) and
+//                         the 8 nibble multipliers of superblock s, 2 zero bytes.
 //
-// Blob = gate, up (NVFP4, [I][H]) then down ([H][I], NVFP4, Q6_K or Q8_0); each
-// section starts on a 256-byte boundary.  Q6_K and Q8_0 blobs end with a
+// Blob = gate, up (NVFP4, [I][H]) then down ([H][I], NVFP4, Q6_K, Q8_0 or
+// IQ3G); each section starts on a 256-byte boundary.  Q6_K, Q8_0 and IQ3G
+// blobs end with a
 // 256-byte meta section whose first int32 is the expert's down-weight exponent
 // s (written by moe_pack_experts): the grouped GEMM forms its fp16 down
 // weights as w * 2^s, s chosen from the expert's largest block scale so that
@@ -36,6 +43,7 @@
 #include <stdint.h>
 
 #include "../../include/moe.h"
+#include "iq3g.h"
 
 namespace moe {
 
@@ -44,9 +52,9 @@ inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a
 
 struct BlobLayout {
   size_t gate_q, gate_s, up_q, up_s;
-  size_t down_q, down_s;             // NVFP4 or Q8_0 down
-  size_t down_ql, down_qh, down_sc, down_d;  // Q6_K down
-  size_t down_meta;                  // Q6_K / Q8_0: int32 fp16-path exponent (0 for NVFP4)
+  size_t down_q, down_s;             // NVFP4 or Q8_0 down; IQ3G: grid indices, signs
+  size_t down_ql, down_qh, down_sc, down_d;  // Q6_K down; IQ3G: down_sc (d and multipliers)
+  size_t down_meta;                  // Q6_K / Q8_0 / IQ3G: int32 fp16-path exponent (0 for NVFP4)
   size_t total;
 };
 
@@ -68,6 +76,11 @@ inline BlobLayout blob_layout(int64_t H, int64_t I, int fmt_down) {
   } else if (fmt_down == MOE_FMT_Q8_0) {
     b.down_q = take((size_t)H * I);
     b.down_s = take((size_t)H * I / 16);
+    b.down_meta = take(4);
+  } else if (fmt_down == MOE_FMT_IQ3G) {
+    b.down_q = take((size_t)H * I / 4);
+    b.down_s = take((size_t)H * I / 8);
+    b.down_sc = take((size_t)H * I / 32);
     b.down_meta = take(4);
   } else {
     b.down_ql = take((size_t)H * I / 2);
@@ -120,15 +133,17 @@ __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
 namespace moe {
 
-// Per-expert exponent of the grouped GEMM's fp16 down weights (Q6_K, Q8_0)
+// Per-expert exponent of the grouped GEMM's fp16 down weights (Q6_K, Q8_0, IQ3G)
 // from the canonical down bytes, into the blob's meta section.
 hipError_t launch_down_exponent(const uint8_t* down_q, int E, int64_t H, int64_t I, int fmt,
                                 uint8_t* meta, size_t dst_expert_stride, hipStream_t s);
 
+// pad: zero bytes after each destination granule (granule size gsz * pieces + pad).
 hipError_t launch_pack_granules(const uint8_t* src, int E, size_t src_expert_stride,
                                 int64_t N, int64_t G, int gsz, size_t row_stride,
                                 int per_sb, size_t sb_stride, size_t inner, uint8_t* dst,
-                                size_t dst_expert_stride, hipStream_t s, int pieces = 1);
+                                size_t dst_expert_stride, hipStream_t s, int pieces = 1,
+                                int pad = 0);
 
 hipError_t launch_router(const uint16_t* x, int64_t T, int H, const float* Wr,
                          const float* bias, int E, float* logits, hipStream_t s);

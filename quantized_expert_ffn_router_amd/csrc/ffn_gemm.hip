@@ -16,7 +16,7 @@
 //     projection) is copied global -> LDS by the load unit; each wave loads
 //     its B fragments from the packed weight blob (one 16-byte granule per
 //     lane and column tile for NVFP4, see "B fragments"; more for Q6_K and
-//     Q8_0) and dequantizes them in registers;
+//     Q8_0 and IQ3G) and dequantizes them in registers;
 //   - operands are fp16 (NVFP4 weights are exact in fp16; token rows carry
 //     an exact per-row power-of-two scale, see k_rows_to_f16; Q6_K and Q8_0
 //     weights are rounded once to fp16 after an exact per-expert power-of-two
@@ -168,10 +168,13 @@ typedef __attribute__((address_space(1))) uint16_t g16_t;
 __device__ __forceinline__ uint4 gl16(const uint8_t* p) { return *(const g128_t*)(uintptr_t)p; }
 __device__ __forceinline__ uint2 gl8(const uint8_t* p) { return *(const g64_t*)(uintptr_t)p; }
 __device__ __forceinline__ uint32_t gl2(const uint8_t* p) { return *(const g16_t*)(uintptr_t)p; }
+typedef __attribute__((address_space(1))) uint32_t g32_t;
+__device__ __forceinline__ uint32_t gl4(const uint8_t* p) { return *(const g32_t*)(uintptr_t)p; }
 #else
 __device__ uint4 gl16(const uint8_t* p);
 __device__ uint2 gl8(const uint8_t* p);
 __device__ uint32_t gl2(const uint8_t* p);
+__device__ uint32_t gl4(const uint8_t* p);
 #endif
 
 struct FragNvfp4 {
@@ -417,6 +420,129 @@ __device__ __forceinline__ v8h_t dequant_frag_q8_h(const FragQ8& f, uint32_t sc2
   return r;
 }
 
+// IQ3G (iq3g.h): a lane group's 32 values of a K step are exactly one
+// sub-block (one odd multiplier 2 s + 1): 8 grid indices, 32 sign bits, and
+// the superblock's d with its multipliers.
+struct FragIq3g {
+  uint2 idx;  // grid indices of elements 32q .. 32q + 31 of the step (q = lane / 16)
+  uint32_t sg;  // their sign bits
+  uint2 sc;   // d fp16 (low 16 bits of x), then the superblock's 8 nibble multipliers
+};
+
+__device__ __forceinline__ void load_frag_iq3g(FragIq3g& f, const uint8_t* qi, const uint8_t* qs,
+                                               const uint8_t* qc, int N, int n, int step) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  f.idx = gl8(qi + ((size_t)(2 * step + (grp >> 1)) * N + n) * 16 + 8 * (grp & 1));
+  f.sg = gl4(qs + ((size_t)step * N + n) * 16 + 4 * grp);
+  f.sc = gl8(qc + ((size_t)(step >> 1) * N + n) * 8);
+}
+
+// Both column tiles cb.. and cb + 16.. (cb wave-uniform): the lane parts of
+// the three addresses are 32-bit offsets made opaque at each use (the
+// compiler then rebuilds them with one add instead of keeping 64-bit
+// addresses live across the K loop); tile 1 is tile 0 plus a constant.
+__device__ __forceinline__ void load_frag_iq3g_pair(FragIq3g (&f)[2], const uint8_t* qi,
+                                                    const uint8_t* qs, const uint8_t* qc, int N,
+                                                    int cb, int step) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4, n = lane & 15;
+  uint32_t oi = (uint32_t)(((grp >> 1) * N + n) * 16 + 8 * (grp & 1));
+  uint32_t os = (uint32_t)(n * 16 + 4 * grp), oc = (uint32_t)(n * 8);
+  __asm__ volatile("" : "+v"(oi), "+v"(os), "+v"(oc));
+  const uint8_t* pi = qi + ((size_t)(2 * step) * N + cb) * 16 + oi;
+  const uint8_t* ps = qs + ((size_t)step * N + cb) * 16 + os;
+  const uint8_t* pc = qc + ((size_t)(step >> 1) * N + cb) * 8 + oc;
+  f[0].idx = gl8(pi);
+  f[1].idx = gl8(pi + 16 * 16);
+  f[0].sg = gl4(ps);
+  f[1].sg = gl4(ps + 16 * 16);
+  f[0].sc = gl8(pc);
+  f[1].sc = gl8(pc + 16 * 8);
+}
+
+// Odd multiplier 2 s + 1 of the lane group's sub-block (4 * (step % 2) + q).
+__device__ __forceinline__ uint32_t iq3g_mult(const FragIq3g& f, int step) {
+  const int j = 4 * (step & 1) + ((threadIdx.x & 63) >> 4);
+  const uint32_t mul = (f.sc.x >> 16) | (f.sc.y << 16);
+  return 2u * ((mul >> (4 * j)) & 15u) + 1u;
+}
+
+// Sub-step S of the fp16 path: entries 2S, 2S + 1 of the lane's 8 as fp16
+// pairs from the LDS grid (tab: {(m0, m1), (m2, m3)} per entry), signs
+// applied, times 2 s + 1 (exact: at most 9 * 31 = 279) and then d * 2^sx (an
+// exact ldexp of the fp16 d; below 2^6 for every superblock of the expert,
+// see k_down_exponent), rounding each weight once.
+// The step's two fp16 factors of a column tile in one register: 2 s + 1 (low
+// half) and d * 2^sx (high half), formed once per step so that the
+// fragment's scale bytes are dead before the sub-steps.
+__device__ __forceinline__ uint32_t iq3g_factors(const FragIq3g& f, int step, int sx) {
+  const _Float16 m = (_Float16)(float)iq3g_mult(f, step);
+  const _Float16 dh = __builtin_amdgcn_ldexph(__builtin_bit_cast(_Float16, (uint16_t)(f.sc.x & 0xffffu)), sx);
+  return (uint32_t)__builtin_bit_cast(uint16_t, m) | ((uint32_t)__builtin_bit_cast(uint16_t, dh) << 16);
+}
+
+template <int S>
+__device__ __forceinline__ v8h_t dequant_frag_iq3g_h(const FragIq3g& f, const uint2* tab,
+                                                     uint32_t fac) {
+  const v2h_t f2 = __builtin_bit_cast(v2h_t, fac);
+  const v2h_t ms = {f2[0], f2[0]}, ds = {f2[1], f2[1]};
+  const uint32_t iw = (S < 2) ? f.idx.x : f.idx.y;
+  v8h_t r;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint2 v = tab[(iw >> (16 * (S & 1) + 8 * e)) & 255u];
+    const int p = 8 * S + 4 * e;  // sign bit of the entry's first value
+    const v2h_t lo = __builtin_bit_cast(v2h_t, v.x ^ pair_sign_at(f.sg, p)) * ms * ds;
+    const v2h_t hi = __builtin_bit_cast(v2h_t, v.y ^ pair_sign_at(f.sg, p + 2)) * ms * ds;
+    r[4 * e] = lo[0];
+    r[4 * e + 1] = lo[1];
+    r[4 * e + 2] = hi[0];
+    r[4 * e + 3] = hi[1];
+  }
+  return r;
+}
+
+// bf16 path (the fp16-h overflow fallback): w = +-m * (2 s + 1) * d in fp32,
+// rounded once to bf16.
+template <int S>
+__device__ __forceinline__ v8bf_t dequant_frag_iq3g(const FragIq3g& f, const uint2* tab,
+                                                    float mult) {
+  const float sc = f16_to_f32((uint16_t)(f.sc.x & 0xffffu)) * mult;
+  const uint32_t iw = (S < 2) ? f.idx.x : f.idx.y;
+  const uint32_t sb = f.sg >> (8 * S);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint2 t = tab[(iw >> (16 * (S & 1) + 8 * e)) & 255u];
+    const uint32_t w4[2] = {t.x, t.y};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const _Float16 m = __builtin_bit_cast(_Float16, (uint16_t)(w4[c >> 1] >> (16 * (c & 1))));
+      const float x = (float)m * sc;
+      v[4 * e + c] = ((sb >> (4 * e + c)) & 1u) ? -x : x;
+    }
+  }
+  v8bf_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const v2bf_t b = to_v2bf(v[2 * p], v[2 * p + 1]);
+    r[2 * p] = b[0];
+    r[2 * p + 1] = b[1];
+  }
+  return r;
+}
+
+// The grid as fp16 pairs in LDS (exact: odd integers up to 15).
+__device__ __forceinline__ void iq3g_table_f16(uint2* tab, int tid) {
+  if (tid < 256) {
+    const uint32_t m = kIq3gGridDev.m[tid];
+    auto h = [](uint32_t v) {
+      return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)v);
+    };
+    tab[tid] = make_uint2(h(m & 255u) | (h((m >> 8) & 255u) << 16),
+                          h((m >> 16) & 255u) | (h(m >> 24) << 16));
+  }
+}
+
 // ---------------------------------------------------------------- main loop
 // Persistent workgroups of 8 waves.  A tile is 128 token rows x 8*NC*16
 // columns; wave w owns all 128 rows and column tiles j < NC (NC = 2: 64
@@ -458,13 +584,16 @@ struct Planes {
 template <int FMT>
 using FragOf = typename std::conditional<
     FMT == MOE_FMT_NVFP4, FragNvfp4,
-    typename std::conditional<FMT == MOE_FMT_Q8_0, FragQ8, FragQ6k>::type>::type;
+    typename std::conditional<
+        FMT == MOE_FMT_Q8_0, FragQ8,
+        typename std::conditional<FMT == MOE_FMT_IQ3G, FragIq3g, FragQ6k>::type>::type>::type;
 
 template <int FMT>
 __device__ __forceinline__ void load_b_tile(FragOf<FMT>& f, const Planes& P, int N, int n,
                                             int step) {
   if constexpr (FMT == MOE_FMT_NVFP4) load_frag(f, P.p[0], P.p[1], N, n, step);
   else if constexpr (FMT == MOE_FMT_Q8_0) load_frag_q8(f, P.p[0], P.p[1], N, n, step);
+  else if constexpr (FMT == MOE_FMT_IQ3G) load_frag_iq3g(f, P.p[0], P.p[1], P.p[2], N, n, step);
   else load_frag_q6k(f, P.p[0], P.p[1], P.p[2], P.p[3], N, n, step);
 }
 
@@ -502,8 +631,17 @@ __device__ __forceinline__ void load_a_half(const uint16_t* base, const uint32_t
 // no wave stalls on a full memory queue right after the barrier.
 template <int FMT, int NC, bool F16, typename Issue>
 __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const uint16_t* Ab,
-                                          int lane, v4f_t (*acc)[NC], int sx, Issue issue) {
+                                          int lane, v4f_t (*acc)[NC], int sx, Issue issue,
+                                          const uint2* tab = nullptr, int st = 0) {
   const int r = lane & 15, cq = 4 * (lane >> 4);
+  // IQ3G: each column tile's factors for this step (fp16 path: 2 s + 1 and
+  // d * 2^sx in one register; bf16 path: the multiplier)
+  uint32_t imul[NC] = {};
+  if constexpr (FMT == MOE_FMT_IQ3G) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+      imul[j] = F16 ? iq3g_factors(bcur[j], st, sx) : iq3g_mult(bcur[j], st);
+  }
   auto sub = [&](auto S_) {
     constexpr int S = decltype(S_)::value;
     if constexpr (F16) {
@@ -515,6 +653,9 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
       } else if constexpr (FMT == MOE_FMT_Q8_0) {
         bf[0] = dequant_frag_q8_h<S, 0>(bcur[0], bcur[0].sc, sx);
         bf[1] = dequant_frag_q8_h<S, 1>(bcur[1], bcur[0].sc, sx);
+      } else if constexpr (FMT == MOE_FMT_IQ3G) {
+        bf[0] = dequant_frag_iq3g_h<S>(bcur[0], tab, imul[0]);
+        bf[1] = dequant_frag_iq3g_h<S>(bcur[1], tab, imul[1]);
       } else {
         bf[0] = dequant_frag_q6k_h<S>(bcur[0], sx);
         bf[1] = dequant_frag_q6k_h<S>(bcur[1], sx);
@@ -527,7 +668,7 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
       // 128-register budget of 4 waves per SIMD.
       // (Q8_0 and Q6_K fragments take 9 and 7 registers per column tile: no
       // A read-ahead, which would push more of the K loop into spills.)
-      constexpr bool kPre = FMT == MOE_FMT_NVFP4;
+      constexpr bool kPre = FMT == MOE_FMT_NVFP4;  // (also none for IQ3G)
       v8h_t an = *reinterpret_cast<const v8h_t*>(Ab + aswz(r, cq + S));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -547,6 +688,7 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
       for (int j = 0; j < NC; ++j) {
         if constexpr (FMT == MOE_FMT_NVFP4) bf[j] = dequant_frag<S>(bcur[j]);
         else if constexpr (FMT == MOE_FMT_Q8_0) bf[j] = dequant_frag_q8<S>(bcur[j]);
+        else if constexpr (FMT == MOE_FMT_IQ3G) bf[j] = dequant_frag_iq3g<S>(bcur[j], tab, (float)imul[j]);
         else bf[j] = dequant_frag_q6k<S>(bcur[j]);
       }
 #pragma unroll
@@ -793,13 +935,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   if (RUN == 2 && *ovf == 0) return;
   __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
   __shared__ float st_rs[AF16 ? 3 : 1][GBM];  // x row scales of up to 3 tiles (fp16 h)
+  __shared__ uint2 gtab[FMT == MOE_FMT_IQ3G ? 256 : 1];  // IQ3G grid, 16-bit pairs
   const int NT = H / 256;
   const TileRange tr = tile_range(*n_tiles * NT);
   if (tr.first >= tr.end) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nsteps = I / GBK;
-  constexpr int kB = (FMT == MOE_FMT_NVFP4) ? 2 : (FMT == MOE_FMT_Q8_0 ? 3 : 4);  // weight loads per column tile
+  constexpr int kB = (FMT == MOE_FMT_NVFP4) ? 2 : (FMT == MOE_FMT_Q6K ? 4 : 3);  // weight loads per column tile
 
   auto rows_of = [&](const TileRec& t, uint32_t (&off)[4]) {
 #pragma unroll
@@ -834,6 +977,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (AF16 && FMT == MOE_FMT_NVFP4) {
     load_frag_pair(bnext, P.p[0], P.p[1], H, cb, 0, bl);
+  } else if constexpr (FMT == MOE_FMT_IQ3G) {
+    load_frag_iq3g_pair(bnext, P.p[0], P.p[1], P.p[2], H, cb, 0);
   } else if constexpr (AF16 && FMT == MOE_FMT_Q8_0) {
     load_frag_q8_pair(bnext, P.p[0], P.p[1], H, cb + (lane & 15), 0);
   } else {
@@ -841,6 +986,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     load_b_tile<FMT>(bnext[1], P, H, cb + 16 + (lane & 15), 0);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (FMT == MOE_FMT_IQ3G) iq3g_table_f16(gtab, tid);  // visible after the barrier below
   wait_vmcnt<2 * kB>();
   __syncthreads();
 
@@ -881,6 +1027,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
           else if constexpr (S == 1)
             load_frag_q8_pair(bnext, P.p[0], P.p[1], H, cbl + (lane & 15), stn);
           else if constexpr (S == 2) load_a_half(h, off, stn * GBK, Anext, wave, lane, 1);
+        } else if constexpr (AF16 && FMT == MOE_FMT_IQ3G) {
+          // token rows first; the weights after sub-step 3's dequant, when
+          // this step's fragments are dead and the next step's can take their
+          // registers (issued at sub-step 1 or 2 they made the compiler spill
+          // 60 registers, with scratch traffic in every step)
+          if constexpr (S == 0) {
+            load_a_half(h, off, stn * GBK, Anext, wave, lane, 0);
+            load_a_half(h, off, stn * GBK, Anext, wave, lane, 1);
+          } else if constexpr (S == 3) {
+            load_frag_iq3g_pair(bnext, P.p[0], P.p[1], P.p[2], H, cbl, stn);
+          }
         } else if constexpr (AF16 && FMT == MOE_FMT_Q6K) {  // the same schedule
           if constexpr (S == 0) load_a_half(h, off, stn * GBK, Anext, wave, lane, 0);
           else if constexpr (S == 1) {
@@ -905,7 +1062,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
           load_b_tile<FMT>(bnext[1], P, H, cbl + 16 + (lane & 15), stn);
           load_a_tile(h, off, stn * GBK, Anext, wave, lane);
         }
-      });
+      }, gtab, st);
       __builtin_amdgcn_sched_barrier(0);
       if (ld) wait_vmcnt<0>();
       __syncthreads();
@@ -1026,6 +1183,17 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
     } else {
       DOWN(MOE_FMT_Q8_0, false, true, 1, q, sc, z, z);
       DOWN(MOE_FMT_Q8_0, false, false, 2, q, sc, z, z);
+    }
+  } else if (L->fmt_down == MOE_FMT_IQ3G) {
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<true, false>), grid, block, 0, s, GU_ARGS);
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<false, true>), grid, block, 0, s, GU_ARGS);
+    const size_t qi = lay.down_q, qs = lay.down_s, qc = lay.down_sc, z = 0;
+    if (bf) {
+      DOWN(MOE_FMT_IQ3G, true, true, 1, qi, qs, qc, z);
+      DOWN(MOE_FMT_IQ3G, true, false, 2, qi, qs, qc, z);
+    } else {
+      DOWN(MOE_FMT_IQ3G, false, true, 1, qi, qs, qc, z);
+      DOWN(MOE_FMT_IQ3G, false, false, 2, qi, qs, qc, z);
     }
   } else {
     hipLaunchKernelGGL((k_gemm_gateup_nvfp4<true, false>), grid, block, 0, s, GU_ARGS);

@@ -85,6 +85,15 @@ __device__ __forceinline__ void e2m1x8_bf16(uint32_t c, v2bf_t* o) {
 
 __device__ __forceinline__ v2bf_t as_v2bf(uint32_t u) { return __builtin_bit_cast(v2bf_t, u); }
 
+// Sign masks of a pair of 16-bit values from bits p and p + 1 of w: bit p to
+// bit 15 (low value), bit p + 1 to bit 31 (high value).  p is a constant once
+// the callers' loops are unrolled, so this is two shifts and a bit select.
+__device__ __forceinline__ uint32_t pair_sign_at(uint32_t w, int p) {
+  const uint32_t lo = p <= 15 ? (w << (15 - p)) : (w >> (p - 15));
+  const uint32_t hi = p <= 30 ? (w << (30 - p)) : (w >> (p - 30));
+  return (lo & 0x8000u) | (hi & 0x80000000u);
+}
+
 // Two floats -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 // silu(g) * u = g * u / (1 + e^-g) with the hardware exp2 and reciprocal
 // (about 1 ulp each; h is rounded to bf16 right after, 2^-9 relative).  Large

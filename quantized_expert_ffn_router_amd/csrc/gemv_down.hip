@@ -7,6 +7,9 @@
 //     w = d * sc * (q - 32).
 //   Q8_0 (the 8-bit GGUF blocks of basalt.jgulfo.com, "All the numbers"):
 //     32-element blocks, fp16 scale d, int8 codes q: w = d * q.
+//   IQ3G (IQ3-style codebook, own grid, iq3g.h): per 4 elements an 8-bit index
+//     into a grid of odd magnitudes m <= 9, a sign bit per element, an odd
+//     multiplier 2 s + 1 per 32 and fp16 d per 256: w = d * (2 s + 1) * +-m.
 // Weights are decoded exactly to bf16 (E2M1 has 2 significant bits, q - 32 is
 // a 6-bit integer, an int8 code has at most 8) and meet h (bf16, from the gate/up kernel) in
 // v_dot2_f32_bf16 with fp32 accumulation.  Each 16-element block sum is scaled
@@ -49,10 +52,17 @@ struct Group<MOE_FMT_Q8_0> {
   uint2 s;     // fp16 scales of the group's 4 blocks of 32
 };
 
+template <>
+struct Group<MOE_FMT_IQ3G> {
+  uint4 q[2];  // 32 grid indices
+  uint4 sg;    // 128 sign bits
+  uint2 sc;    // d fp16 and the superblock's 8 nibble multipliers
+};
+
 struct Planes {
-  const uint8_t* a;  // NVFP4 codes | Q6_K ql | Q8_0 codes
-  const uint8_t* b;  // NVFP4 scales | Q6_K qh | Q8_0 scales
-  const uint8_t* c;  // Q6_K sc
+  const uint8_t* a;  // NVFP4 codes | Q6_K ql | Q8_0 codes | IQ3G indices
+  const uint8_t* b;  // NVFP4 scales | Q6_K qh | Q8_0 scales | IQ3G signs
+  const uint8_t* c;  // Q6_K sc | IQ3G d and multipliers
   const uint8_t* d;  // Q6_K d
 };
 
@@ -79,6 +89,14 @@ __device__ __forceinline__ void load_group(Group<MOE_FMT_Q8_0>& r, const Planes&
 #pragma unroll
   for (int q = 0; q < 8; ++q) r.c[q] = ld16(P.a + (((size_t)(8 * g + q)) * H + nc) * 16);
   r.s = ld8(P.b + ((size_t)g * H + nc) * 8);
+}
+
+__device__ __forceinline__ void load_group(Group<MOE_FMT_IQ3G>& r, const Planes& P, int H,
+                                           size_t nc, int g) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) r.q[q] = ld16(P.a + (((size_t)(2 * g + q)) * H + nc) * 16);
+  r.sg = ld16(P.b + ((size_t)g * H + nc) * 16);
+  r.sc = ld8(P.c + ((size_t)(g >> 1) * H + nc) * 8);
 }
 
 // Exact bf16 pairs w[b][0..8) of the 8 blocks of 16 and their fp32 scales.
@@ -152,6 +170,40 @@ __device__ __forceinline__ void decode_half_q8(const Group<MOE_FMT_Q8_0>& r, v2b
   }
 }
 
+// The grid as bf16 pairs in LDS: entry e = {(m0, m1), (m2, m3)}, exact (odd
+// integers up to 15 need 4 significant bits).
+__device__ __forceinline__ void iq3g_table_bf16(uint2* tab, int tid, int nthreads) {
+  for (int e = tid; e < 256; e += nthreads) {
+    const uint32_t m = kIq3gGridDev.m[e];
+    auto bf = [](uint32_t v) { return __float_as_uint((float)v) >> 16; };
+    tab[e] = make_uint2(bf(m & 255u) | (bf((m >> 8) & 255u) << 16),
+                        bf((m >> 16) & 255u) | (bf(m >> 24) << 16));
+  }
+}
+
+
+// Exact bf16 pairs of a 128-element group (half h = g & 1 of its superblock)
+// and the fp32 scales d * (2 s + 1) of its 8 blocks of 16.
+__device__ __forceinline__ void decode_group_iq3g(const Group<MOE_FMT_IQ3G>& r, int h,
+                                                  const uint2* tab, v2bf_t (*w)[8], float* sc) {
+  const float d = f16_to_f32((uint16_t)(r.sc.x & 0xffffu));
+  const uint32_t mul = (r.sc.x >> 16) | (r.sc.y << 16);  // nibble j: multiplier of sub-block j
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int j = 4 * h + (b >> 1);
+    sc[b] = d * (float)(2u * ((mul >> (4 * j)) & 15u) + 1u);
+    const uint32_t idx = word_of(r.q[b >> 2], b & 3);  // entries 4b .. 4b + 3
+    const uint32_t sw = word_of(r.sg, b >> 1);         // sign bits of blocks 2(b/2), +1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 v = tab[(idx >> (8 * i)) & 255u];
+      const int p = 16 * (b & 1) + 4 * i;  // bit of the entry's first value
+      w[b][2 * i] = as_v2bf(v.x ^ pair_sign_at(sw, p));
+      w[b][2 * i + 1] = as_v2bf(v.y ^ pair_sign_at(sw, p + 2));
+    }
+  }
+}
+
 // Issue the loads of the first D groups of a pass.
 template <int FMT, int GP, int D>
 __device__ __forceinline__ void dn_issue(Group<FMT> (&r)[GP], const Planes& P, int H, size_t nc,
@@ -171,7 +223,8 @@ __device__ __forceinline__ void dn_issue(Group<FMT> (&r)[GP], const Planes& P, i
 template <int FMT, int GP, int D>
 __device__ __forceinline__ void dn_consume(Group<FMT> (&r)[GP], const uint16_t* __restrict__ h,
                                            int p0, int H, int I, size_t nc, const Planes& P,
-                                           float ts, int gb, int mt, float* acc) {
+                                           float ts, int gb, int mt, float* acc,
+                                           const uint2* tab) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int gi = 0; gi < GP; ++gi) {
@@ -210,7 +263,8 @@ __device__ __forceinline__ void dn_consume(Group<FMT> (&r)[GP], const uint16_t* 
     } else {
       v2bf_t w[8][8];
       float sc[8];
-      decode_group(r[gi], ts, w, sc);
+      if constexpr (FMT == MOE_FMT_IQ3G) decode_group_iq3g(r[gi], g & 1, tab, w, sc);
+      else decode_group(r[gi], ts, w, sc);
 #pragma unroll 1
       for (int t = 0; t < mt; ++t) {
         const uint32_t* hp = reinterpret_cast<const uint32_t*>(h + (size_t)(p0 + t) * I) + 64 * g;
@@ -237,6 +291,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const int32_t* __restrict__ n_active, void* __restrict__ y) {
   extern __shared__ __align__(16) float red[];  // [S][kDnMT][64]
+  __shared__ uint2 tab[FMT == MOE_FMT_IQ3G ? 256 : 1];  // IQ3G grid as bf16 pairs
 
   int e;
   moe_expert_ref ref;
@@ -270,6 +325,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
         }
         mt = min(kDnMT, cnt - c0);
         for (int t = 0; t < mt; ++t) acc[t * 64 + lane] = 0.0f;  // this wave's slice only
+        if constexpr (FMT == MOE_FMT_IQ3G) {
+          if (c0 == 0) {  // the grid, while the first weights are in flight
+            iq3g_table_bf16(tab, tid, nthreads);
+            __syncthreads();
+          }
+        }
       }
       {  // the pass's h values of the first 4 tokens (4 lines per group)
         uint32_t tch = 0;
@@ -281,7 +342,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
                                        64 * (gb + sg));
         keep_scalar(tch);
       }
-      dn_consume<FMT, GP, D>(r, h, base + c0, H, I, nc, P, ts, gb + sg, mt, acc);
+      dn_consume<FMT, GP, D>(r, h, base + c0, H, I, nc, P, ts, gb + sg, mt, acc, tab);
     }
     __syncthreads();
     for (int o = tid; o < mt * 64; o += nthreads) {
@@ -304,6 +365,9 @@ hipError_t down_t(const moe_layer_desc* L, const uint16_t* h, const moe_buckets*
   Planes P;
   if (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_Q8_0) {
     P = {(const uint8_t*)lay.down_q, (const uint8_t*)lay.down_s, nullptr, nullptr};
+  } else if (FMT == MOE_FMT_IQ3G) {
+    P = {(const uint8_t*)lay.down_q, (const uint8_t*)lay.down_s, (const uint8_t*)lay.down_sc,
+         nullptr};
   } else {
     P = {(const uint8_t*)lay.down_ql, (const uint8_t*)lay.down_qh, (const uint8_t*)lay.down_sc,
          (const uint8_t*)lay.down_d};
@@ -353,6 +417,7 @@ hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const mo
                             int max_slots, void* y, int y_dtype, hipStream_t s) {
   if (L->fmt_down == MOE_FMT_Q6K) return down_fmt<MOE_FMT_Q6K>(L, h, b, max_slots, y, y_dtype, s);
   if (L->fmt_down == MOE_FMT_Q8_0) return down_fmt<MOE_FMT_Q8_0>(L, h, b, max_slots, y, y_dtype, s);
+  if (L->fmt_down == MOE_FMT_IQ3G) return down_fmt<MOE_FMT_IQ3G>(L, h, b, max_slots, y, y_dtype, s);
   return down_fmt<MOE_FMT_NVFP4>(L, h, b, max_slots, y, y_dtype, s);
 }
 

@@ -82,6 +82,7 @@ def test_buckets_carve_layout_on_host_buffer():
     (dict(I=100), q.MOE_ERR_UNSUPPORTED, "I=100"),
     (dict(I=384, fmt_down=2), q.MOE_ERR_UNSUPPORTED, "Q6_K"),
     (dict(I=96, fmt_down=3), q.MOE_ERR_UNSUPPORTED, "I=96"),
+    (dict(I=384, fmt_down=4), q.MOE_ERR_UNSUPPORTED, "I=384"),
     (dict(fmt_down=7), q.MOE_ERR_UNSUPPORTED, "down format"),
     (dict(renorm=2), q.MOE_ERR_INVALID_ARG, "renormalize"),
     (dict(ffn_mode=3), q.MOE_ERR_INVALID_ARG, "ffn_mode=3"),
@@ -121,8 +122,9 @@ def test_zero_tokens_is_a_noop_and_null_checks():
 
 def test_blob_bytes_per_down_format():
     """Sections start on 256-byte boundaries: gate and up (NVFP4 codes and
-    scales), then the down projection's planes; Q6_K and Q8_0 blobs end with
-    a 256-byte section for the grouped GEMM's per-expert weight exponent."""
+    scales), then the down projection's planes; Q6_K, Q8_0 and IQ3G blobs end
+    with a 256-byte section for the grouped GEMM's per-expert weight
+    exponent."""
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
     H, I = 2048, 768
     gu = 2 * (al(I * H // 2) + al(I * H // 16))
@@ -133,6 +135,11 @@ def test_blob_bytes_per_down_format():
     assert q.moe_expert_blob_bytes(H, I, 1, 2) == gu + al(H * I // 2) + al(H * I // 4) + \
         al(H * I // 16) + al(H * I // 128) + 256
     assert q.moe_expert_blob_bytes(H, 96, 1, 3) == 0
+    # IQ3G: grid indices (I/4 per row), sign bits (I/8), d and multipliers
+    # (8 bytes per 256), exponent section
+    assert q.moe_expert_blob_bytes(H, I, 1, 4) == gu + al(H * I // 4) + al(H * I // 8) + \
+        al(H * I // 32) + 256
+    assert q.moe_expert_blob_bytes(H, 384, 1, 4) == 0
 
 
 def test_workspace_bytes_cover_hidden_buffers():
@@ -180,3 +187,28 @@ def test_route_bucket_checks_before_launch():
     assert "shifts" in q.last_error()
     assert f(ctypes.byref(d), 0x10, 5, 0x20, 0x30, 0x40, ctypes.byref(b), None, 0, None, 0, 0,
              None) == q.MOE_ERR_WORKSPACE
+
+
+def test_library_grid_equals_oracle_grid():
+    """The library builds the IQ3G grid at compile time (csrc/iq3g.h, a
+    counting sort on the squared norm); compiled on the host here, its 256
+    entries equal the oracle's (which walks the norms) and the brute-force
+    definition's."""
+    import os
+    import subprocess
+    import tempfile
+    import oracle
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hdr = os.path.join(root, "quantized_expert_ffn_router_amd", "csrc", "iq3g.h")
+    src = ('#include "%s"\n#include <cstdio>\nint main() {\n'
+           '  constexpr moe::Iq3gGrid g = moe::make_iq3g_grid();\n'
+           '  for (int e = 0; e < 256; ++e) printf("%%u\\n", g.m[e]);\n}\n') % hdr
+    with tempfile.TemporaryDirectory() as d:
+        with open(os.path.join(d, "g.cpp"), "w") as f:
+            f.write(src)
+        subprocess.check_call(["g++", "-std=c++17", "-O1", os.path.join(d, "g.cpp"), "-o",
+                               os.path.join(d, "g")])
+        out = subprocess.check_output([os.path.join(d, "g")], text=True).split()
+    m = np.array([int(v) for v in out], np.uint32)
+    lib_grid = np.stack([(m >> (8 * c)) & 255 for c in range(4)], axis=1).astype(np.uint8)
+    np.testing.assert_array_equal(lib_grid, oracle.iq3g_grid())

@@ -26,7 +26,8 @@ def _layer(fmt_down):
     return w, moegen.make_layer(w)
 
 
-@pytest.mark.parametrize("fmt_down", [moegen.FMT_NVFP4, moegen.FMT_Q6K, moegen.FMT_Q8_0])
+@pytest.mark.parametrize("fmt_down", [moegen.FMT_NVFP4, moegen.FMT_Q6K, moegen.FMT_Q8_0,
+                                      moegen.FMT_IQ3G])
 @pytest.mark.parametrize("y_dtype", [0, 1])
 def test_grouped_gemm_multi_tile_every_assignment(fmt_down, y_dtype):
     w, L = _layer(fmt_down)

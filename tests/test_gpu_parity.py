@@ -96,7 +96,8 @@ def test_more_than_eight_experts_per_token(T):
 GEMM_Y_REL = 5e-3
 
 
-@pytest.mark.parametrize("fmt_down,mode", [(1, 1), (1, 2), (2, 1), (2, 2), (3, 1), (3, 2)])
+@pytest.mark.parametrize("fmt_down,mode", [(1, 1), (1, 2), (2, 1), (2, 2), (3, 1), (3, 2), (4, 1),
+                                           (4, 2)])
 def test_largest_hidden_and_intermediate(fmt_down, mode):
     """H = I = 8192, the largest supported sizes, with each down format: the
     decode GEMVs split K over 4 (gate/up, 16 groups a wave) and 8 (down)
@@ -234,13 +235,16 @@ def test_q8_0_prefill_sampled():
     (3e5, 0.02, 3),   # the same with Q8_0
     (1e-3, 0.02, 3),
     (1.0, 4.0, 3),
+    (3e5, 0.02, 4),   # the same with IQ3G
+    (1e-3, 0.02, 4),
+    (1.0, 4.0, 4),
 ])
 def test_gemm_activation_magnitudes(x_std, w_std, fmt_down):
     """The grouped GEMM multiplies fp16 operands; the token rows and h carry
     per-row power-of-two scales and an h overflow redoes the FFN with bf16 h.
     Results stay within the relative bars at any activation magnitude (the
     absolute bar of the other tests is for unit-scale activations)."""
-    I = 384 if fmt_down == 1 else 512  # Q6_K needs I % 256 == 0
+    I = 384 if fmt_down in (1, 3) else 512  # Q6_K and IQ3G need I % 256 == 0
     w, L = layer("gemm_mag", E=16, k=4, H=512, I=I, T=300, x_std=x_std, w_std=w_std,
                  fmt_down=fmt_down)
     x = moegen.make_tokens(w, w.T)
@@ -299,13 +303,13 @@ def test_graph_replay_matches_eager():
 
 
 def _scale_down_block_scales(L, exp2):
-    """Copy of layer L whose Q6_K / Q8_0 down block scales d (fp16) are
-    multiplied by 2^exp2 (rounded to fp16 where the result is subnormal; the
-    oracle reads the same bytes)."""
+    """Copy of layer L whose Q6_K / Q8_0 / IQ3G down block scales d (fp16)
+    are multiplied by 2^exp2 (rounded to fp16 where the result is subnormal;
+    the oracle reads the same bytes)."""
     import dataclasses
     dq = L.down_q.copy()
     flat = dq.reshape(-1)
-    bsz, off = (34, 0) if L.fmt_down == moegen.FMT_Q8_0 else (210, 208)
+    bsz, off = {moegen.FMT_Q8_0: (34, 0), moegen.FMT_IQ3G: (102, 0)}.get(L.fmt_down, (210, 208))
     at = np.arange(flat.size // bsz) * bsz + off
     d = (flat[at].astype(np.uint16) | (flat[at + 1].astype(np.uint16) << 8)).view(np.float16)
     d2 = (d.astype(np.float64) * 2.0 ** exp2).astype(np.float16)
@@ -316,13 +320,14 @@ def _scale_down_block_scales(L, exp2):
     return dataclasses.replace(L, down_q=dq)
 
 
-@pytest.mark.parametrize("fmt_down,exp2", [(3, 18), (3, -10), (2, 16), (2, -8)])
+@pytest.mark.parametrize("fmt_down,exp2", [(3, 18), (3, -10), (2, 16), (2, -8), (4, 16), (4, -10)])
 def test_gemm_down_weights_at_any_scale(fmt_down, exp2):
     """The grouped GEMM's fp16 down weights carry a per-expert power of two
     fixed at pack time from the expert's largest block scale: Q8_0 weights
     up to 16K (beyond the plain fp16 product q * d * 16) and Q6_K d * sc up to
-    ~100 (beyond d * sc * 2^10 in fp16), and block scales pushed into fp16's
-    subnormal range, all match the oracle at the relative bars."""
+    ~100 (beyond d * sc * 2^10 in fp16), IQ3G superblock scales d near 20
+    (weights up to ~5K), and block scales pushed into fp16's subnormal range,
+    all match the oracle at the relative bars."""
     I = 384 if fmt_down == 3 else 512
     w, L0 = layer("gemm_scale", E=16, k=4, H=512, I=I, T=300, fmt_down=fmt_down)
     L = _scale_down_block_scales(L0, exp2)
@@ -340,3 +345,37 @@ def test_gemm_down_weights_at_any_scale(fmt_down, exp2):
     got = moegen.bf16_to_f32(g["out"][toks])
     ref = moegen.bf16_to_f32(o_out[toks])
     assert rel_l2(got, ref) <= 5e-3, rel_l2(got, ref)
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_iq3g_decode_parity(B):
+    """The decode layer with the IQ3-style grid down projection (own grid):
+    dequant-fused GEMV with the grid in LDS."""
+    w, L = layer("iq3")
+    x = moegen.make_tokens(w, B, step=B + 2)
+    print("iq3g decode B", B, flush=True)
+    check_layer(L, x)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_iq3g_both_ffn_families_ragged(mode):
+    # 600 tokens x top-8 over 64 experts, I = 512 (4 groups of 128, 2
+    # superblocks, 4 K steps of the GEMM): GEMV (mode 1) and grouped GEMM
+    # (mode 2) against the oracle.
+    w, L = layer("iq3_many", E=64, k=8, H=256, I=512, T=600, fmt_down=moegen.FMT_IQ3G)
+    x = moegen.make_tokens(w, w.T, step=7)
+    res = moegen.make_residual(w, w.T)
+    print("iq3g ragged mode", mode, flush=True)
+    check_layer(L, x, residual=res, tokens=list(range(0, 600, 5)), ffn_mode=mode,
+                y_rel=GEMM_Y_REL)
+
+
+def test_iq3g_prefill_sampled():
+    """4096-token prefill of the IQ3G layer on the grouped GEMM path, with
+    the first and last row of every 128-row block."""
+    w, L = layer("iq3")
+    x = moegen.make_tokens(w, 4096, step=3)
+    print("iq3g prefill", flush=True)
+    g, _ = check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
+    (r, worst), n = check_block_edges(g, L, x)
+    print(f"iq3g prefill block edges: {n} rows, rel L2 {r:.2e}, worst row {worst:.2e}", flush=True)
