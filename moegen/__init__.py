@@ -22,6 +22,7 @@ FMT_NVFP4 = 1
 FMT_Q6K = 2
 FMT_Q8_0 = 3
 FMT_IQ3G = 4
+FMT_IQ1G = 5
 
 # stream tags
 TAG_X = 1
@@ -69,6 +70,8 @@ def lib():
         L.moegen_q8_0_normal.argtypes = [u64, i64, i64, dbl, vp, vp]
         L.moegen_quant_iq3g.argtypes = [vp, i64, i64, vp]
         L.moegen_iq3g_normal.argtypes = [u64, i64, i64, dbl, vp, vp]
+        L.moegen_quant_iq1g.argtypes = [vp, i64, i64, vp]
+        L.moegen_iq1g_normal.argtypes = [u64, i64, i64, dbl, vp, vp]
         L.moegen_permutation.argtypes = [u64, i32, vp]
         L.moegen_zipf_bias.argtypes = [u64, i32, dbl, dbl, vp, vp]
         L.moegen_threads.restype = ctypes.c_int
@@ -146,6 +149,16 @@ def quant_iq3g(W: np.ndarray) -> np.ndarray:
     return out
 
 
+def quant_iq1g(W: np.ndarray) -> np.ndarray:
+    """fp32 [N][K] -> IQ1-style ternary-grid rows [N][K/256*46] (see moegen.c)."""
+    W = np.ascontiguousarray(W, np.float32)
+    N, K = W.shape
+    assert K % 256 == 0
+    out = np.empty((N, K // 256 * 46), np.uint8)
+    lib().moegen_quant_iq1g(_p(W), N, K, _p(out))
+    return out
+
+
 def permutation(k: int, n: int) -> np.ndarray:
     out = np.empty(n, np.int32)
     lib().moegen_permutation(k, n, _p(out))
@@ -205,6 +218,9 @@ WORKLOADS = {
     # the decode layer with its down projection in the IQ3-style grid format
     "iq3": Workload("iq3", E=128, k=8, H=2048, I=768, T=8, fmt_down=FMT_IQ3G,
                     extra={"prefill_T": 4096}),
+    # the decode layer with its down projection in the IQ1-style ternary grid
+    "iq1": Workload("iq1", E=128, k=8, H=2048, I=768, T=8, fmt_down=FMT_IQ1G,
+                    extra={"prefill_T": 4096}),
     # 48 stacked mixed layers with 96 of 256 experts resident per layer
     "tiered": Workload("tiered", E=256, k=8, H=2048, I=512, T=8, fmt_down=FMT_Q6K,
                        zipf_s=1.2, zipf_alpha=ZIPF_ALPHA["tiered"],
@@ -228,7 +244,7 @@ class LayerWeights:
     up_s: np.ndarray
     up_ts: np.ndarray
     down_q: np.ndarray              # NVFP4 u8 [E][H][I/2], Q6K u8 [E][H][I/256*210], Q8_0 u8 [E][H][I/32*34],
-                                    # IQ3G u8 [E][H][I/256*102]
+                                    # IQ3G u8 [E][H][I/256*102], IQ1G u8 [E][H][I/256*46]
     down_s: np.ndarray | None       # NVFP4 u8 [E][H][I/16]
     down_ts: np.ndarray | None      # NVFP4 f32 [E]
     renormalize: int = 1
@@ -262,6 +278,10 @@ def make_layer(w: Workload, layer: int = 0, seed: int | None = None) -> LayerWei
         dq = np.empty((E, H, I // 256 * 102), np.uint8)
         ds = None
         dts = None
+    elif w.fmt_down == FMT_IQ1G:
+        dq = np.empty((E, H, I // 256 * 46), np.uint8)
+        ds = None
+        dts = None
     else:
         dq = np.empty((E, H, I // 256 * 210), np.uint8)
         ds = None
@@ -283,6 +303,9 @@ def make_layer(w: Workload, layer: int = 0, seed: int | None = None) -> LayerWei
                                  _p(scratch), _p(dq[e]))
         elif w.fmt_down == FMT_IQ3G:
             L.moegen_iq3g_normal(key(seed, (TAG_DOWN << 20) | e, layer), H, I, w.w_std,
+                                 _p(scratch), _p(dq[e]))
+        elif w.fmt_down == FMT_IQ1G:
+            L.moegen_iq1g_normal(key(seed, (TAG_DOWN << 20) | e, layer), H, I, w.w_std,
                                  _p(scratch), _p(dq[e]))
         else:
             L.moegen_q6k_normal(key(seed, (TAG_DOWN << 20) | e, layer), H, I, w.w_std,

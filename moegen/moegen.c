@@ -385,6 +385,92 @@ void moegen_iq3g_normal(uint64_t key, int64_t N, int64_t K, double std,
   moegen_quant_iq3g(scratch, N, K, out);
 }
 
+/* IQ1-style ternary-grid superblocks (the oracle's reading): grid = the 1024
+ * vectors of eight values in {-1, 0, +1} with the fewest nonzero values, by
+ * nonzero count, then lexicographically (-1 < 0 < +1; this generator's own
+ * copy, used to encode).  Superblock of 256 weights of a row, 46 bytes:
+ * d fp16 | 8 x 4-bit s_j (32 weights each) | 32 low index bytes (8 weights
+ * each) | 8 bytes of 2-bit high index parts; w = d * (2 s_j + 1) * grid. */
+static int16_t g1_index[6561]; /* base-3 code (digit = value + 1, value 0 first) -> entry or -1 */
+
+static void g1_init(void) {
+  static int ready = 0;
+  if (ready) return;
+  for (int i = 0; i < 6561; ++i) g1_index[i] = -1;
+  int n = 0;
+  for (int nz = 0; nz <= 8 && n < 1024; ++nz)
+    for (int u = 0; u < 6561 && n < 1024; ++u) {
+      int c = 0;
+      for (int r = u, i = 0; i < 8; ++i, r /= 3) c += (r % 3) != 1;
+      if (c == nz) g1_index[u] = (int16_t)n++;
+    }
+  ready = 1;
+}
+
+/* Quantize fp32 W[N][K] (K % 256 == 0): per 32-weight sub-block the unit
+ * u_j = amax_j, d = fp16(max_j u_j / 31), s_j = nearest (u_j / d - 1) / 2 in
+ * [0, 15]; each weight rounds to the nearest of -1, 0, +1 units (|w| >= unit/2
+ * is nonzero) and while a group's vector is not in the grid its nonzero
+ * value of least magnitude becomes 0. */
+void moegen_quant_iq1g(const float* W, int64_t N, int64_t K, uint8_t* out) {
+  g1_init();
+  const int64_t nb = K / 256;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* w = W + n * K + b * 256;
+      uint8_t* blk = out + (n * nb + b) * 46;
+      memset(blk, 0, 46);
+      double u[8], umax = 0.0;
+      for (int j = 0; j < 8; ++j) {
+        double a = 0.0;
+        for (int i = 0; i < 32; ++i) a = fmax(a, fabs((double)w[32 * j + i]));
+        u[j] = a;
+        umax = fmax(umax, u[j]);
+      }
+      const uint16_t dbits = f64_to_f16_rne(umax / 31.0);
+      const double d = f16_bits_to_f64(dbits);
+      blk[0] = (uint8_t)(dbits & 0xff);
+      blk[1] = (uint8_t)(dbits >> 8);
+      int sj[8] = {0};
+      if (d > 0.0)
+        for (int j = 0; j < 8; ++j) {
+          double v = nearbyint((u[j] / d - 1.0) / 2.0);
+          sj[j] = v < 0 ? 0 : (v > 15 ? 15 : (int)v);
+          blk[2 + j / 2] |= (uint8_t)(sj[j] << (4 * (j % 2)));
+        }
+      for (int g = 0; g < 32; ++g) {
+        const double unit = d * (2.0 * sj[g / 4] + 1.0);
+        double t[8];
+        int v[8];
+        for (int i = 0; i < 8; ++i) {
+          t[i] = d > 0.0 ? (double)w[8 * g + i] / unit : 0.0;
+          v[i] = fabs(t[i]) >= 0.5 ? (t[i] < 0 ? -1 : 1) : 0;
+        }
+        int e;
+        for (;;) {
+          int code = 0;
+          for (int i = 0; i < 8; ++i) code = code * 3 + (v[i] + 1);
+          e = g1_index[code];
+          if (e >= 0) break;
+          int m = -1;
+          for (int i = 0; i < 8; ++i)
+            if (v[i] != 0 && (m < 0 || fabs(t[i]) < fabs(t[m]))) m = i;
+          v[m] = 0;
+        }
+        blk[6 + g] = (uint8_t)(e & 255);
+        blk[38 + g / 4] |= (uint8_t)((e >> 8) << (2 * (g % 4)));
+      }
+    }
+  }
+}
+
+void moegen_iq1g_normal(uint64_t key, int64_t N, int64_t K, double std,
+                        float* scratch, uint8_t* out) {
+  moegen_normal_f32(key, N * K, std, scratch);
+  moegen_quant_iq1g(scratch, N, K, out);
+}
+
 void moegen_q8_0_normal(uint64_t key, int64_t N, int64_t K, double std,
                         float* scratch, uint8_t* out) {
   moegen_normal_f32(key, N * K, std, scratch);

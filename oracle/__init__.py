@@ -29,6 +29,7 @@ FMT_NVFP4 = 1
 FMT_Q6K = 2
 FMT_Q8_0 = 3
 FMT_IQ3G = 4
+FMT_IQ1G = 5
 
 
 def build(force: bool = True) -> str:
@@ -106,6 +107,10 @@ def _load(path):
     L.oracle_iq3g_weight.argtypes = [vp, i64, i64, i64]
     L.oracle_decode_iq3g.argtypes = [vp, i64, i64, vp]
     L.oracle_iq3g_grid.argtypes = [vp]
+    L.oracle_iq1g_weight.restype = ctypes.c_double
+    L.oracle_iq1g_weight.argtypes = [vp, i64, i64, i64]
+    L.oracle_decode_iq1g.argtypes = [vp, i64, i64, vp]
+    L.oracle_iq1g_grid.argtypes = [vp]
     L.oracle_expert_rows.argtypes = [ctypes.POINTER(OracleExperts), i64, vp, i64, vp]
     L.oracle_init.argtypes = []
     L.oracle_init()
@@ -177,6 +182,21 @@ def iq3g_grid() -> np.ndarray:
     """The oracle's 256-entry grid of the IQ3-style format, uint8 [256][4]."""
     out = np.empty((256, 4), np.uint8)
     lib().oracle_iq3g_grid(_p(out))
+    return out
+
+
+def decode_iq1g(blocks: np.ndarray, K: int) -> np.ndarray:
+    """IQ1-style ternary-grid rows [N][K/256*46] -> float64 [N][K]."""
+    N = blocks.shape[0]
+    out = np.empty((N, K), np.float64)
+    lib().oracle_decode_iq1g(_p(np.ascontiguousarray(blocks)), N, K, _p(out))
+    return out
+
+
+def iq1g_grid() -> np.ndarray:
+    """The oracle's 1024-entry ternary grid of the IQ1-style format, int8 [1024][8]."""
+    out = np.empty((1024, 8), np.int8)
+    lib().oracle_iq1g_grid(_p(out))
     return out
 
 

@@ -300,11 +300,72 @@ double oracle_iq3g_weight(const uint8_t* blocks, int64_t K, int64_t n, int64_t k
   return neg ? -v : v;
 }
 
+/* IQ1-style codebook blocks with a grid of our own (the pages' packs carry
+ * IQ1_M tensors, basalt.jgulfo.com "Models", at under two bits per weight;
+ * the pages give no bytes or grid.  This reading keeps the structure of a
+ * 1-bit-class codebook -- a ternary vector per 8 weights picked from a fixed
+ * grid, a small odd multiplier per 32 weights, an fp16 scale per 256 -- and
+ * defines the grid itself):
+ *   grid = the 1024 vectors v of eight values in {-1, 0, +1} with the fewest
+ *   nonzero values, ordered by the number of nonzero values and then
+ *   lexicographically (-1 < 0 < +1, value 0 most significant); entry e is
+ *   the e-th.
+ * Superblock b = k/256 of row n, 46 bytes:
+ *   d fp16 little-endian[2] | s[4]: 4-bit s_j of sub-block j = 32 weights
+ *   (byte j/2, low nibble for even j) | qs[32]: low 8 bits of the grid index
+ *   of group g = weights 8g..8g+7 | qh[8]: its high 2 bits at bits
+ *   2(g%4), 2(g%4)+1 of byte g/4;
+ *   value = d * (2 s_j + 1) * grid[idx_g][k % 8]. */
+static int8_t iq1g_grid[1024][8];
+static int iq1g_ready = 0;
+
+/* Walk the nonzero counts upward and, within a count, the vectors in
+ * lexicographic order (the base-3 numbers 0..6560, digit i = value i + 1,
+ * value 0 the most significant digit), until 1024 are taken. */
+static void iq1g_build(void) {
+  int n = 0;
+  for (int nz = 0; nz <= 8 && n < 1024; ++nz)
+    for (int u = 0; u < 6561 && n < 1024; ++u) {
+      int v[8], c = 0, r = u;
+      for (int i = 7; i >= 0; --i) {
+        v[i] = r % 3 - 1;
+        r /= 3;
+      }
+      for (int i = 0; i < 8; ++i) c += v[i] != 0;
+      if (c != nz) continue;
+      for (int i = 0; i < 8; ++i) iq1g_grid[n][i] = (int8_t)v[i];
+      ++n;
+    }
+  iq1g_ready = 1;
+}
+
+/* The grid as 1024 x 8 signed bytes (for the tests). */
+void oracle_iq1g_grid(int8_t* out) {
+  if (!iq1g_ready) iq1g_build();
+  memcpy(out, iq1g_grid, sizeof(iq1g_grid));
+}
+
+double oracle_iq1g_weight(const uint8_t* blocks, int64_t K, int64_t n, int64_t k) {
+  if (!iq1g_ready) iq1g_build();
+  const uint8_t* b = blocks + (n * (K / 256) + k / 256) * 46;
+  const int r = (int)(k % 256), j = r / 32, g = r / 8;
+  const uint16_t dbits = (uint16_t)(b[0] | (b[1] << 8));
+  const int s = (b[2 + j / 2] >> (4 * (j % 2))) & 15;
+  const int idx = b[6 + g] | (((b[38 + g / 4] >> (2 * (g % 4))) & 3) << 8);
+  return oracle_f16(dbits) * (double)(2 * s + 1) * (double)iq1g_grid[idx][r % 8];
+}
+
 /* ------------------------------------------------------------------ */
 /* Expert FFN and combine                                               */
 /* ------------------------------------------------------------------ */
 
-enum { ORACLE_FMT_NVFP4 = 1, ORACLE_FMT_Q6K = 2, ORACLE_FMT_Q8_0 = 3, ORACLE_FMT_IQ3G = 4 };
+enum {
+  ORACLE_FMT_NVFP4 = 1,
+  ORACLE_FMT_Q6K = 2,
+  ORACLE_FMT_Q8_0 = 3,
+  ORACLE_FMT_IQ3G = 4,
+  ORACLE_FMT_IQ1G = 5
+};
 
 /* Expert weights in the canonical layouts, stacked over experts. */
 typedef struct oracle_experts {
@@ -316,7 +377,7 @@ typedef struct oracle_experts {
   const uint8_t* up_s;
   const float* up_ts;
   const uint8_t* down_q;   /* NVFP4 [E][H][I/2], Q6_K [E][H][I/256*210], Q8_0 [E][H][I/32*34]
-                              or IQ3G [E][H][I/256*102] */
+                              IQ3G [E][H][I/256*102] or IQ1G [E][H][I/256*46] */
   const uint8_t* down_s;   /* NVFP4 [E][H][I/16], NULL for Q6_K */
   const float* down_ts;    /* NVFP4 [E], NULL for Q6_K */
 } oracle_experts;
@@ -329,6 +390,8 @@ static double down_weight(const oracle_experts* X, int64_t e, int64_t n, int64_t
     return oracle_q8_0_weight(X->down_q + e * H * (I / 32) * 34, I, n, i);
   if (X->fmt_down == ORACLE_FMT_IQ3G)
     return oracle_iq3g_weight(X->down_q + e * H * (I / 256) * 102, I, n, i);
+  if (X->fmt_down == ORACLE_FMT_IQ1G)
+    return oracle_iq1g_weight(X->down_q + e * H * (I / 256) * 46, I, n, i);
   return oracle_nvfp4_weight(X->down_q + e * H * (I / 2), X->down_s + e * H * (I / 16),
                              X->down_ts[e], I, n, i);
 }
@@ -407,6 +470,7 @@ void oracle_expert_rows(const oracle_experts* X, int64_t e, const uint16_t* x, i
 void oracle_init(void) {
   tables_init();
   if (!iq3g_ready) iq3g_build();
+  if (!iq1g_ready) iq1g_build();
 }
 
 /* Layer output for the listed tokens (all T when tokens == NULL):
@@ -489,4 +553,9 @@ void oracle_decode_q8_0(const uint8_t* blocks, int64_t N, int64_t K, double* out
 void oracle_decode_iq3g(const uint8_t* blocks, int64_t N, int64_t K, double* out) {
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) out[n * K + k] = oracle_iq3g_weight(blocks, K, n, k);
+}
+
+void oracle_decode_iq1g(const uint8_t* blocks, int64_t N, int64_t K, double* out) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) out[n * K + k] = oracle_iq1g_weight(blocks, K, n, k);
 }

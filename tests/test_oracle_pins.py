@@ -313,6 +313,8 @@ def _dense_reference(L, x, w_idx, w_val, residual=None):
             Wd = oracle.decode_q8_0(L.down_q[e], L.I)
         elif L.fmt_down == moegen.FMT_IQ3G:
             Wd = oracle.decode_iq3g(L.down_q[e], L.I)
+        elif L.fmt_down == moegen.FMT_IQ1G:
+            Wd = oracle.decode_iq1g(L.down_q[e], L.I)
         else:
             Wd = oracle.decode_q6k(L.down_q[e], L.I)
         g = xf @ Wg.T
@@ -383,6 +385,20 @@ def test_ffn_iq3g_down_dense_reference():
         for j in range(W.k):
             np.testing.assert_allclose(y[t * W.k + j], ys[idx[t, j]][t], rtol=1e-12, atol=1e-15)
     _bf16_close(out, ref)
+
+
+def test_ffn_iq1g_down_dense_reference():
+    W = moegen.Workload("iq1", E=4, k=2, H=256, I=256, T=3, fmt_down=moegen.FMT_IQ1G)
+    L = moegen.make_layer(W)
+    x = moegen.make_tokens(W, W.T)
+    _, idx, w = oracle.route(x, L)
+    out, y = oracle.ffn_combine(L, x, idx, w, want_y=True)
+    ref, ys = _dense_reference(L, x, idx, w)
+    for t in range(W.T):
+        for j in range(W.k):
+            np.testing.assert_allclose(y[t * W.k + j], ys[idx[t, j]][t], rtol=1e-12, atol=1e-15)
+    _bf16_close(out, ref)
+    assert np.abs(np.concatenate(list(ys.values()))).max() > 0
 
 
 def test_ffn_zero_gate_gives_residual():
@@ -544,3 +560,105 @@ def test_iq3g_generator_signs_and_error_bound():
                 np.testing.assert_array_equal(np.abs(dec[n, 4 * g:4 * g + 4]), unit * m)
                 checked += 1
     assert checked > 200
+
+
+def _ternary_grid_by_sorting():
+    allv = sorted(itertools.product((-1, 0, 1), repeat=8),
+                  key=lambda v: (sum(c != 0 for c in v), v))
+    return np.array(allv[:1024], np.int8)
+
+
+def test_iq1g_grid_is_the_1024_sparsest_ternary_vectors():
+    """The oracle's grid (built by walking nonzero counts upward) equals the
+    sorted brute-force enumeration of {-1, 0, +1}^8: every vector with at
+    most 3 nonzero values (1 + 16 + 112 + 448 = 577), then the first 447 with
+    4 in lexicographic order."""
+    g = oracle.iq1g_grid()
+    np.testing.assert_array_equal(g, _ternary_grid_by_sorting())
+    nz = (g != 0).sum(1)
+    assert [int((nz == c).sum()) for c in range(5)] == [1, 16, 112, 448, 447]
+    assert (np.diff(nz) >= 0).all() and len({tuple(v) for v in g}) == 1024
+    assert tuple(g[0]) == (0,) * 8 and tuple(g[1]) == (-1,) + (0,) * 7
+    assert tuple(g[9]) == (0,) * 7 + (1,) and tuple(g[16]) == (1,) + (0,) * 7
+    assert tuple(g[577]) == (-1, -1, -1, -1, 0, 0, 0, 0)
+    assert int(np.abs(g).max()) == 1
+
+
+def test_iq1g_decode_closed_form():
+    """Blocks packed by the documented byte layout from random integers:
+    decode equals d * (2 s + 1) * grid[idx][k % 8], with the grid from the
+    brute-force enumeration, the 10-bit index split into its low byte and
+    2-bit high part, and d from numpy's float16."""
+    rng = np.random.default_rng(21)
+    G = _ternary_grid_by_sorting().astype(np.float64)
+    N, K = 3, 512
+    nb = K // 256
+    d = (rng.standard_normal((N, nb)) * 1e-3).astype(np.float16)
+    s = rng.integers(0, 16, size=(N, K // 32))
+    idx = rng.integers(0, 1024, size=(N, K // 8))
+    blocks = np.zeros((N, nb, 46), np.uint8)
+    for n in range(N):
+        for b in range(nb):
+            blocks[n, b, 0:2] = np.frombuffer(d[n, b].tobytes(), np.uint8)
+            for j in range(8):
+                blocks[n, b, 2 + j // 2] |= s[n, 8 * b + j] << (4 * (j % 2))
+            for g in range(32):
+                i = idx[n, 32 * b + g]
+                blocks[n, b, 6 + g] = i & 255
+                blocks[n, b, 38 + g // 4] |= (i >> 8) << (2 * (g % 4))
+    got = oracle.decode_iq1g(blocks.reshape(N, -1), K)
+    for n in range(N):
+        for k in range(K):
+            exp = float(d[n, k // 256]) * (2 * s[n, k // 32] + 1) * G[idx[n, k // 8], k % 8]
+            assert got[n, k] == exp
+
+
+def test_iq1g_generator_roundtrip_on_grid():
+    """Weights that are exactly d * (2 s_j + 1) * (grid vector), d = 2^-10,
+    one sub-block at s = 15 and a nonzero value in every sub-block (so the
+    quantizer's unit amax and scale max / 31 are exact), survive quantize ->
+    decode exactly; an all-zero superblock decodes to zeros."""
+    rng = np.random.default_rng(22)
+    G = _ternary_grid_by_sorting().astype(np.float64)
+    N, K = 2, 512
+    W = np.zeros((N, K))
+    for n in range(N):
+        for j in range(K // 32):
+            sj = 15 if j % 8 == 0 else int(rng.integers(0, 16))
+            unit = 2.0 ** -10 * (2 * sj + 1)
+            for g in range(4):
+                e = int(rng.integers(1, 1024)) if g == 0 else int(rng.integers(1024))
+                W[n, 32 * j + 8 * g:32 * j + 8 * g + 8] = unit * G[e]
+    W[1, 256:] = 0.0
+    W = W.astype(np.float32)
+    assert (W.astype(np.float64) == W).all()
+    q = moegen.quant_iq1g(W)
+    np.testing.assert_array_equal(oracle.decode_iq1g(q, K), W.astype(np.float64))
+
+
+def test_iq1g_generator_keeps_signs_and_rounds_in_grid():
+    """On Gaussian weights every nonzero decoded weight keeps the input's
+    sign and is one unit in magnitude, and a group whose rounded vector has at
+    most 3 nonzero values (always in the grid) decodes to exactly that
+    rounding."""
+    rng = np.random.default_rng(23)
+    W = (rng.standard_normal((4, 256)) * 0.02).astype(np.float32)
+    q = moegen.quant_iq1g(W)
+    dec = oracle.decode_iq1g(q, 256)
+    nz = dec != 0
+    assert nz.any() and (np.sign(dec[nz]) == np.sign(W[nz])).all()
+    blk = q.reshape(4, 46)
+    d = blk[:, :2].copy().view(np.float16).astype(np.float64)[:, 0]
+    checked = 0
+    for n in range(4):
+        for g in range(32):
+            j = g // 4
+            sj = (int(blk[n, 2 + j // 2]) >> (4 * (j % 2))) & 15
+            unit = d[n] * (2 * sj + 1)
+            t = W[n, 8 * g:8 * g + 8].astype(np.float64) / unit
+            r = np.where(np.abs(t) >= 0.5, np.sign(t), 0.0)
+            np.testing.assert_array_equal(np.abs(dec[n, 8 * g:8 * g + 8]) <= unit, True)
+            if (r != 0).sum() <= 3:
+                np.testing.assert_array_equal(dec[n, 8 * g:8 * g + 8], r * unit)
+                checked += 1
+    assert checked > 64
