@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--no-mixed", action="store_true")
     p.add_argument("--no-q8", action="store_true")
     p.add_argument("--no-iq3", action="store_true")
+    p.add_argument("--no-iq1", action="store_true")
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--tiered-steps", type=int, default=2048,
                    help="steps of the 48-layer tiered stack (0: skip)")
@@ -74,7 +75,7 @@ def parse():
                    help="only run this many eager steps per batch (for profilers)")
     p.add_argument("--profile-prefill", type=int, default=0,
                    help="only run this many prefill steps (for profilers)")
-    p.add_argument("--profile-format", choices=("mixed", "q8", "iq3"), default=None,
+    p.add_argument("--profile-format", choices=("mixed", "q8", "iq3", "iq1"), default=None,
                    help="with --profile-prefill: run that many 4096-token prefill FFN calls "
                         "of this layer instead")
     p.add_argument("--copy-calibration", type=int, default=0,
@@ -308,6 +309,7 @@ def main():
     mixed = None if args.no_mixed else measure_format(args, q, moegen, torch, dev, "mixed")
     q8 = None if args.no_q8 else measure_format(args, q, moegen, torch, dev, "q8")
     iq3 = None if args.no_iq3 else measure_format(args, q, moegen, torch, dev, "iq3")
+    iq1 = None if args.no_iq1 else measure_format(args, q, moegen, torch, dev, "iq1")
     progress("format layers done")
     torch.cuda.empty_cache()
     tiered = None if args.tiered_steps <= 0 else measure_tiered(args, q, moegen, torch)
@@ -356,6 +358,7 @@ def main():
         "mixed": mixed,
         "q8_0": q8,
         "iq3g": iq3,
+        "iq1g": iq1,
         "tiered": tiered,
         "cpu_baseline": cpu,
         "setup_s": round(gen_s, 1),
@@ -424,13 +427,15 @@ FORMAT_LAYERS = {
           "NVFP4 gate/up, Q8_0 down",
     "iq3": "IQ3G-down layer: 128 experts, top-8, hidden 2048, intermediate 768, "
            "NVFP4 gate/up, IQ3-style grid down (own grid, 3.19 bits per weight)",
+    "iq1": "IQ1G-down layer: 128 experts, top-8, hidden 2048, intermediate 768, "
+           "NVFP4 gate/up, IQ1-style ternary grid down (own grid, 1.44 bits per weight)",
 }
 
 
 def measure_format(args, q, moegen, torch, dev, name):
     """A layer with another down-projection format (the mixed layer: 256
-    experts, top-8, hidden 2048, intermediate 512, Q6_K-style down; the Q8_0
-    and IQ3G layers: the decode layer's shape with Q8_0 or IQ3G down): decode
+    experts, top-8, hidden 2048, intermediate 512, Q6_K-style down; the Q8_0,
+    IQ3G and IQ1G layers: the decode layer's shape with that down format): decode
     batch 8 expert FFN
     (GB/s over the active experts' bytes, four layer copies cycled so the
     Infinity Cache cannot hold them) and the 4096-token prefill FFN (TFLOP/s),

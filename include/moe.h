@@ -26,7 +26,12 @@
  *   - community packs run IQ3 GGUF files -- basalt.jgulfo.com, "Community";
  *     their grids are not on the pages, so MOE_FMT_IQ3G keeps the IQ3
  *     structure (grid indices per 4 weights, sign bits, small scales) with a
- *     grid defined here (below), offered as a down-projection format.
+ *     grid defined here (below), offered as a down-projection format;
+ *   - the pages' packs also carry IQ1_M tensors (basalt.jgulfo.com,
+ *     "Models"), a codebook format of under two bits per weight whose grid
+ *     the pages do not give either, so MOE_FMT_IQ1G keeps that structure
+ *     (a ternary grid vector per 8 weights, small scales) with a grid
+ *     defined here (below), offered as a down-projection format.
  * The pages give no formula.  The arithmetic below is the plainest reading;
  * each entry point states it.
  *
@@ -46,7 +51,7 @@
  *   - bf16 values are passed as uint16_t bit patterns.
  *
  * Supported shapes: 1 <= k <= min(E, 64), E <= 1024, H % 128 == 0,
- * 128 <= H <= 8192, I % 128 == 0 (NVFP4, Q8_0) or I % 256 == 0 (Q6_K, IQ3G),
+ * 128 <= H <= 8192, I % 128 == 0 (NVFP4, Q8_0) or I % 256 == 0 (Q6_K, IQ3G, IQ1G),
  * I <= 8192.
  */
 #ifndef MOE_H
@@ -79,6 +84,8 @@ typedef enum moe_status {
 #define MOE_FMT_Q8_0 3   /* 32-element blocks: fp16 scale, 32 int8 codes (down projection only) */
 #define MOE_FMT_IQ3G 4   /* 256-element superblocks: fp16 scale, 4-bit odd multipliers per 32,
                             8-bit grid index per 4, sign bits (down projection only) */
+#define MOE_FMT_IQ1G 5   /* 256-element superblocks: fp16 scale, 4-bit odd multipliers per 32,
+                            10-bit ternary grid index per 8 (down projection only) */
 
 /* Element types of the expert-output buffer y. */
 #define MOE_DTYPE_F32 0
@@ -134,12 +141,21 @@ const char* moe_last_error(void);
  *     grid = the 256 smallest vectors of four positive odd integers <= 15,
  *     ordered by squared norm, then lexicographically (entry 0 = (1,1,1,1);
  *     every magnitude is at most 9).
+ *   IQ1G matrix W[N][K] (1.44 bits per weight): row n is K/256 superblocks of
+ *     46 bytes: d fp16 little-endian[2]; s[4], the 4-bit multiplier s_j of
+ *     sub-block j (elements 32j..32j+31) in byte j/2 (low nibble for even j);
+ *     qs[32], the low 8 bits of the grid entry of elements 8g..8g+7; qh[8],
+ *     its high 2 bits at bits 2(g%4), 2(g%4)+1 of byte g/4;
+ *     w = d * (2 s_j + 1) * grid[idx[i/8]][i%8],
+ *     grid = the 1024 vectors of eight values in {-1, 0, +1} with the fewest
+ *     nonzero values, ordered by that count, then lexicographically
+ *     (-1 < 0 < +1, value 0 the most significant; entry 0 = all zero).
  *   Gate and up are [I][H] (K = H); down is [H][I] (K = I).
  *
  * The GPU kernels read a packed "blob" per expert (a device-friendly
  * re-arrangement of the same bytes, 16-byte granules transposed so that one
  * wavefront load covers consecutive rows).  moe_expert_blob_bytes gives its
- * size; moe_pack_experts writes it.  With Q6_K, Q8_0 or IQ3G down weights the blob
+ * size; moe_pack_experts writes it.  With Q6_K, Q8_0, IQ3G or IQ1G down weights the blob
  * ends with a 256-byte section holding one int32 computed by the pack from
  * the expert's block scales: the power of two by which the grouped GEMM
  * scales that expert's fp16 down weights (so none can overflow fp16, for any
@@ -151,7 +167,7 @@ typedef struct moe_expert_ref {
   const void* blob;   /* device pointer to the packed expert (256-byte aligned) */
   float ts_gate;      /* NVFP4 per-tensor scales */
   float ts_up;
-  float ts_down;      /* ignored when the down projection is Q6_K, Q8_0 or IQ3G */
+  float ts_down;      /* ignored when the down projection is Q6_K, Q8_0, IQ3G or IQ1G */
   uint32_t reserved;  /* 0 (not read by the library) */
 } moe_expert_ref;
 
@@ -161,8 +177,8 @@ size_t moe_expert_blob_bytes(int32_t H, int32_t I, int32_t fmt_gate_up, int32_t 
 /* Pack E experts from the canonical layouts (device arrays stacked over
  * experts: gate_q [E][I][H/2], gate_s [E][I][H/16], up likewise, down_q
  * [E][H][I/2] and down_s [E][H][I/16] for NVFP4, down_q [E][H][I/256*210]
- * for Q6_K, [E][H][I/32*34] for Q8_0 or [E][H][I/256*102] for IQ3G, down_s
- * == NULL for those three) into
+ * for Q6_K, [E][H][I/32*34] for Q8_0, [E][H][I/256*102] for IQ3G or
+ * [E][H][I/256*46] for IQ1G, down_s == NULL for those four) into
  * E blobs at blobs + e * blob_stride.
  * blob_stride >= moe_expert_blob_bytes(...) and a multiple of 256. */
 moe_status moe_pack_experts(int32_t E, int32_t H, int32_t I, int32_t fmt_gate_up,
@@ -182,7 +198,7 @@ typedef struct moe_layer_desc {
   int32_t H;            /* hidden size */
   int32_t I;            /* expert intermediate size */
   int32_t fmt_gate_up;  /* MOE_FMT_NVFP4 */
-  int32_t fmt_down;     /* MOE_FMT_NVFP4, MOE_FMT_Q6K, MOE_FMT_Q8_0 or MOE_FMT_IQ3G */
+  int32_t fmt_down;     /* MOE_FMT_NVFP4, MOE_FMT_Q6K, MOE_FMT_Q8_0, MOE_FMT_IQ3G or MOE_FMT_IQ1G */
   int32_t renormalize;  /* 1: softmax renormalised over the selected k; 0: full softmax */
   int32_t ffn_mode;     /* MOE_FFN_AUTO (0), MOE_FFN_GEMV or MOE_FFN_GEMM */
   const moe_expert_ref* experts;  /* device [E] */

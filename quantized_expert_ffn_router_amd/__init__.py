@@ -27,6 +27,7 @@ MOE_FMT_NVFP4 = 1
 MOE_FMT_Q6K = 2
 MOE_FMT_Q8_0 = 3
 MOE_FMT_IQ3G = 4
+MOE_FMT_IQ1G = 5
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 

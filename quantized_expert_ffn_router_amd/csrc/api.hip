@@ -48,11 +48,11 @@ moe_status check_shape(int E, int k, int H, int I, int fmt_gu, int fmt_down, con
   if (fmt_down == MOE_FMT_NVFP4 || fmt_down == MOE_FMT_Q8_0) {
     if (I % 128 != 0 || I > 8192)
       return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d must be a multiple of 128 and <= 8192", where, I);
-  } else if (fmt_down == MOE_FMT_Q6K || fmt_down == MOE_FMT_IQ3G) {
+  } else if (fmt_down == MOE_FMT_Q6K || fmt_down == MOE_FMT_IQ3G || fmt_down == MOE_FMT_IQ1G) {
     if (I % 256 != 0 || I > 8192)
       return fail(MOE_ERR_UNSUPPORTED,
                   "%s: I=%d must be a multiple of 256 and <= 8192 for %s", where, I,
-                  fmt_down == MOE_FMT_Q6K ? "Q6_K" : "IQ3G");
+                  fmt_down == MOE_FMT_Q6K ? "Q6_K" : (fmt_down == MOE_FMT_IQ3G ? "IQ3G" : "IQ1G"));
   } else {
     return fail(MOE_ERR_UNSUPPORTED, "%s: down format %d", where, fmt_down);
   }
@@ -191,6 +191,16 @@ moe_status moe_pack_experts(int32_t E, int32_t H, int32_t I, int32_t fmt_gate_up
     e = moe::launch_pack_granules(down_q, E, ex, H, I / 64, 16, row, 4, moe::kIq3gBlockBytes, 6, d + lay.down_q, blob_stride, stream);
     if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 128, 16, row, 2, moe::kIq3gBlockBytes, 70, d + lay.down_s, blob_stride, stream);
     if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 256, 6, row, 1, moe::kIq3gBlockBytes, 0, d + lay.down_sc, blob_stride, stream, 1, 2);
+    if (e == hipSuccess) e = moe::launch_down_exponent(down_q, E, H, I, fmt_down, d + lay.down_meta, blob_stride, stream);
+  } else if (fmt_down == MOE_FMT_IQ1G) {
+    // 46-byte superblocks: index low bytes in 16-byte granules of 128
+    // elements, their 2-bit high parts in 4-byte granules of 128 elements,
+    // and d with the 4-bit multipliers (6 bytes) in an 8-byte granule per
+    // superblock
+    const size_t row = (size_t)(I / 256) * moe::kIq1gBlockBytes, ex = (size_t)H * row;
+    e = moe::launch_pack_granules(down_q, E, ex, H, I / 128, 16, row, 2, moe::kIq1gBlockBytes, 6, d + lay.down_q, blob_stride, stream);
+    if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 128, 4, row, 2, moe::kIq1gBlockBytes, 38, d + lay.down_s, blob_stride, stream);
+    if (e == hipSuccess) e = moe::launch_pack_granules(down_q, E, ex, H, I / 256, 6, row, 1, moe::kIq1gBlockBytes, 0, d + lay.down_sc, blob_stride, stream, 1, 2);
     if (e == hipSuccess) e = moe::launch_down_exponent(down_q, E, H, I, fmt_down, d + lay.down_meta, blob_stride, stream);
   } else {
     const size_t row = (size_t)(I / 256) * 210, ex = (size_t)H * row;

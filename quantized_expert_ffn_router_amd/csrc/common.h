@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include "../../include/moe.h"
+#include "iq1g.h"
 #include "iq3g.h"
 
 namespace moe {
@@ -52,9 +53,10 @@ inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a
 
 struct BlobLayout {
   size_t gate_q, gate_s, up_q, up_s;
-  size_t down_q, down_s;             // NVFP4 or Q8_0 down; IQ3G: grid indices, signs
-  size_t down_ql, down_qh, down_sc, down_d;  // Q6_K down; IQ3G: down_sc (d and multipliers)
-  size_t down_meta;                  // Q6_K / Q8_0 / IQ3G: int32 fp16-path exponent (0 for NVFP4)
+  size_t down_q, down_s;  // NVFP4 or Q8_0 down; IQ3G: grid indices, signs; IQ1G: index
+                          // low bytes, 2-bit high parts
+  size_t down_ql, down_qh, down_sc, down_d;  // Q6_K down; IQ3G / IQ1G: down_sc (d and multipliers)
+  size_t down_meta;  // Q6_K / Q8_0 / IQ3G / IQ1G: int32 fp16-path exponent (0 for NVFP4)
   size_t total;
 };
 
@@ -81,6 +83,11 @@ inline BlobLayout blob_layout(int64_t H, int64_t I, int fmt_down) {
     b.down_q = take((size_t)H * I / 4);
     b.down_s = take((size_t)H * I / 8);
     b.down_sc = take((size_t)H * I / 32);
+    b.down_meta = take(4);
+  } else if (fmt_down == MOE_FMT_IQ1G) {
+    b.down_q = take((size_t)H * I / 8);   // [I/128][H][16]: index low bytes of 16 groups of 8
+    b.down_s = take((size_t)H * I / 32);  // [I/128][H][4]: their 2-bit high parts
+    b.down_sc = take((size_t)H * I / 32); // [I/256][H][8]: d, 8 nibble multipliers, 2 zero bytes
     b.down_meta = take(4);
   } else {
     b.down_ql = take((size_t)H * I / 2);

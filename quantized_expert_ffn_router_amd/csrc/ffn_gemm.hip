@@ -543,6 +543,125 @@ __device__ __forceinline__ void iq3g_table_f16(uint2* tab, int tid) {
   }
 }
 
+// IQ1G (iq1g.h): a lane group's 32 values of a K step are one sub-block (one
+// odd multiplier 2 s + 1) made of 4 groups of 8, one grid entry each: 4 index
+// low bytes, their 2-bit high parts (one byte of the step's 4-byte record) and
+// the superblock's d with its multipliers.
+struct FragIq1g {
+  uint32_t lo;  // index low bytes of groups 4q .. 4q + 3 of the step (q = lane / 16)
+  uint32_t hi;  // the step's 16 two-bit high parts (group g at bits 2g, 2g + 1)
+  uint2 sc;     // d fp16 (low 16 bits of x), then the superblock's 8 nibble multipliers
+};
+
+__device__ __forceinline__ void load_frag_iq1g(FragIq1g& f, const uint8_t* qi, const uint8_t* qh,
+                                               const uint8_t* qc, int N, int n, int step) {
+  const int grp = (threadIdx.x & 63) >> 4;
+  f.lo = gl4(qi + ((size_t)step * N + n) * 16 + 4 * grp);
+  f.hi = gl4(qh + ((size_t)step * N + n) * 4);
+  f.sc = gl8(qc + ((size_t)(step >> 1) * N + n) * 8);
+}
+
+// Both column tiles cb.. and cb + 16.. (cb wave-uniform), lane offsets made
+// opaque as in load_frag_iq3g_pair.
+__device__ __forceinline__ void load_frag_iq1g_pair(FragIq1g (&f)[2], const uint8_t* qi,
+                                                    const uint8_t* qh, const uint8_t* qc, int N,
+                                                    int cb, int step) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4, n = lane & 15;
+  uint32_t oi = (uint32_t)(n * 16 + 4 * grp), oh = (uint32_t)(n * 4), oc = (uint32_t)(n * 8);
+  __asm__ volatile("" : "+v"(oi), "+v"(oh), "+v"(oc));
+  const uint8_t* pi = qi + ((size_t)step * N + cb) * 16 + oi;
+  const uint8_t* ph = qh + ((size_t)step * N + cb) * 4 + oh;
+  const uint8_t* pc = qc + ((size_t)(step >> 1) * N + cb) * 8 + oc;
+  f[0].lo = gl4(pi);
+  f[1].lo = gl4(pi + 16 * 16);
+  f[0].hi = gl4(ph);
+  f[1].hi = gl4(ph + 16 * 4);
+  f[0].sc = gl8(pc);
+  f[1].sc = gl8(pc + 16 * 8);
+}
+
+// Odd multiplier 2 s + 1 of the lane group's sub-block (4 * (step % 2) + q).
+__device__ __forceinline__ uint32_t iq1g_mult(const FragIq1g& f, int step) {
+  const int j = 4 * (step & 1) + ((threadIdx.x & 63) >> 4);
+  const uint32_t mul = (f.sc.x >> 16) | (f.sc.y << 16);
+  return 2u * ((mul >> (4 * j)) & 15u) + 1u;
+}
+
+// The step's two fp16 factors of a column tile (2 s + 1, d * 2^sx), as for
+// IQ3G.
+__device__ __forceinline__ uint32_t iq1g_factors(const FragIq1g& f, int step, int sx) {
+  const _Float16 m = (_Float16)(float)iq1g_mult(f, step);
+  const _Float16 dh = __builtin_amdgcn_ldexph(__builtin_bit_cast(_Float16, (uint16_t)(f.sc.x & 0xffffu)), sx);
+  return (uint32_t)__builtin_bit_cast(uint16_t, m) | ((uint32_t)__builtin_bit_cast(uint16_t, dh) << 16);
+}
+
+// Grid entry of sub-step S's group (4q + S of the step).
+template <int S>
+__device__ __forceinline__ uint32_t iq1g_entry(const FragIq1g& f) {
+  const int q = (threadIdx.x & 63) >> 4;
+  return ((f.lo >> (8 * S)) & 255u) | (((f.hi >> (8 * q + 2 * S)) & 3u) << 8);
+}
+
+// Sub-step S of the fp16 path: the group's 8 values -1, 0, +1 as fp16 pairs
+// (LDS entry: byte i = the high byte of value i's fp16; one byte permute per
+// pair), times 2 s + 1 and then d * 2^sx (exact up to the last product,
+// rounded once; |2 s + 1| <= 31 and d * 2^sx < 2^9, see k_down_exponent).
+template <int S>
+__device__ __forceinline__ v8h_t dequant_frag_iq1g_h(const FragIq1g& f, const uint2* tab,
+                                                     uint32_t fac) {
+  const v2h_t f2 = __builtin_bit_cast(v2h_t, fac);
+  const v2h_t ms = {f2[0], f2[0]}, ds = {f2[1], f2[1]};
+  const uint2 t = tab[iq1g_entry<S>(f)];
+  v8h_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t src = p < 2 ? t.x : t.y, b0 = 2 * (p & 1);
+    // result bytes [0, src.b0, 0, src.b0+1] (selector 0x0c: zero)
+    const uint32_t raw = __builtin_amdgcn_perm(0u, src, 0x000c000cu | (b0 << 8) | ((b0 + 1) << 24));
+    const v2h_t v = __builtin_bit_cast(v2h_t, raw) * ms * ds;
+    r[2 * p] = v[0];
+    r[2 * p + 1] = v[1];
+  }
+  return r;
+}
+
+// bf16 path (the fp16-h overflow fallback): w = v * (2 s + 1) * d in fp32,
+// rounded once to bf16.
+template <int S>
+__device__ __forceinline__ v8bf_t dequant_frag_iq1g(const FragIq1g& f, const uint2* tab,
+                                                    float mult) {
+  const float sc = f16_to_f32((uint16_t)(f.sc.x & 0xffffu)) * mult;
+  const uint2 t = tab[iq1g_entry<S>(f)];
+  v8bf_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w = p < 2 ? t.x : t.y;
+    float v[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t hb = (w >> (8 * (2 * (p & 1) + c))) & 255u;  // 0x00, 0x3c or 0xbc
+      v[c] = hb == 0u ? 0.0f : ((hb & 0x80u) ? -sc : sc);
+    }
+    const v2bf_t b = to_v2bf(v[0], v[1]);
+    r[2 * p] = b[0];
+    r[2 * p + 1] = b[1];
+  }
+  return r;
+}
+
+// The IQ1G grid in LDS, 8 bytes per entry: byte i = the high byte of value
+// i's fp16 (0x00, 0x3c = +1, 0xbc = -1; the low bytes are zero).
+__device__ __forceinline__ void iq1g_table_f16(uint2* tab, int tid, int nthreads) {
+  for (int e = tid; e < 1024; e += nthreads) {
+    const uint32_t c = kIq1gGridDev.c[e];
+    auto byte = [c](int i) {
+      return ((c >> (2 * i)) & 1u) ? (((c >> (2 * i + 1)) & 1u) ? 0xbcu : 0x3cu) : 0u;
+    };
+    tab[e] = make_uint2(byte(0) | (byte(1) << 8) | (byte(2) << 16) | (byte(3) << 24),
+                        byte(4) | (byte(5) << 8) | (byte(6) << 16) | (byte(7) << 24));
+  }
+}
+
 // ---------------------------------------------------------------- main loop
 // Persistent workgroups of 8 waves.  A tile is 128 token rows x 8*NC*16
 // columns; wave w owns all 128 rows and column tiles j < NC (NC = 2: 64
@@ -586,7 +705,9 @@ using FragOf = typename std::conditional<
     FMT == MOE_FMT_NVFP4, FragNvfp4,
     typename std::conditional<
         FMT == MOE_FMT_Q8_0, FragQ8,
-        typename std::conditional<FMT == MOE_FMT_IQ3G, FragIq3g, FragQ6k>::type>::type>::type;
+        typename std::conditional<
+            FMT == MOE_FMT_IQ3G, FragIq3g,
+            typename std::conditional<FMT == MOE_FMT_IQ1G, FragIq1g, FragQ6k>::type>::type>::type>::type;
 
 template <int FMT>
 __device__ __forceinline__ void load_b_tile(FragOf<FMT>& f, const Planes& P, int N, int n,
@@ -594,6 +715,7 @@ __device__ __forceinline__ void load_b_tile(FragOf<FMT>& f, const Planes& P, int
   if constexpr (FMT == MOE_FMT_NVFP4) load_frag(f, P.p[0], P.p[1], N, n, step);
   else if constexpr (FMT == MOE_FMT_Q8_0) load_frag_q8(f, P.p[0], P.p[1], N, n, step);
   else if constexpr (FMT == MOE_FMT_IQ3G) load_frag_iq3g(f, P.p[0], P.p[1], P.p[2], N, n, step);
+  else if constexpr (FMT == MOE_FMT_IQ1G) load_frag_iq1g(f, P.p[0], P.p[1], P.p[2], N, n, step);
   else load_frag_q6k(f, P.p[0], P.p[1], P.p[2], P.p[3], N, n, step);
 }
 
@@ -641,6 +763,10 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
 #pragma unroll
     for (int j = 0; j < NC; ++j)
       imul[j] = F16 ? iq3g_factors(bcur[j], st, sx) : iq3g_mult(bcur[j], st);
+  } else if constexpr (FMT == MOE_FMT_IQ1G) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+      imul[j] = F16 ? iq1g_factors(bcur[j], st, sx) : iq1g_mult(bcur[j], st);
   }
   auto sub = [&](auto S_) {
     constexpr int S = decltype(S_)::value;
@@ -656,6 +782,9 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
       } else if constexpr (FMT == MOE_FMT_IQ3G) {
         bf[0] = dequant_frag_iq3g_h<S>(bcur[0], tab, imul[0]);
         bf[1] = dequant_frag_iq3g_h<S>(bcur[1], tab, imul[1]);
+      } else if constexpr (FMT == MOE_FMT_IQ1G) {
+        bf[0] = dequant_frag_iq1g_h<S>(bcur[0], tab, imul[0]);
+        bf[1] = dequant_frag_iq1g_h<S>(bcur[1], tab, imul[1]);
       } else {
         bf[0] = dequant_frag_q6k_h<S>(bcur[0], sx);
         bf[1] = dequant_frag_q6k_h<S>(bcur[1], sx);
@@ -689,6 +818,7 @@ __device__ __forceinline__ void step_mfma(const FragOf<FMT> (&bcur)[NC], const u
         if constexpr (FMT == MOE_FMT_NVFP4) bf[j] = dequant_frag<S>(bcur[j]);
         else if constexpr (FMT == MOE_FMT_Q8_0) bf[j] = dequant_frag_q8<S>(bcur[j]);
         else if constexpr (FMT == MOE_FMT_IQ3G) bf[j] = dequant_frag_iq3g<S>(bcur[j], tab, (float)imul[j]);
+        else if constexpr (FMT == MOE_FMT_IQ1G) bf[j] = dequant_frag_iq1g<S>(bcur[j], tab, (float)imul[j]);
         else bf[j] = dequant_frag_q6k<S>(bcur[j]);
       }
 #pragma unroll
@@ -935,7 +1065,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   if (RUN == 2 && *ovf == 0) return;
   __shared__ __align__(16) uint16_t As[2 * GBM * ARB];
   __shared__ float st_rs[AF16 ? 3 : 1][GBM];  // x row scales of up to 3 tiles (fp16 h)
-  __shared__ uint2 gtab[FMT == MOE_FMT_IQ3G ? 256 : 1];  // IQ3G grid, 16-bit pairs
+  // IQ3G grid (16-bit pairs) or IQ1G grid (fp16 high bytes)
+  __shared__ uint2 gtab[FMT == MOE_FMT_IQ3G ? 256 : (FMT == MOE_FMT_IQ1G ? 1024 : 1)];
   const int NT = H / 256;
   const TileRange tr = tile_range(*n_tiles * NT);
   if (tr.first >= tr.end) return;
@@ -979,6 +1110,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     load_frag_pair(bnext, P.p[0], P.p[1], H, cb, 0, bl);
   } else if constexpr (FMT == MOE_FMT_IQ3G) {
     load_frag_iq3g_pair(bnext, P.p[0], P.p[1], P.p[2], H, cb, 0);
+  } else if constexpr (FMT == MOE_FMT_IQ1G) {
+    load_frag_iq1g_pair(bnext, P.p[0], P.p[1], P.p[2], H, cb, 0);
   } else if constexpr (AF16 && FMT == MOE_FMT_Q8_0) {
     load_frag_q8_pair(bnext, P.p[0], P.p[1], H, cb + (lane & 15), 0);
   } else {
@@ -987,6 +1120,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (FMT == MOE_FMT_IQ3G) iq3g_table_f16(gtab, tid);  // visible after the barrier below
+  if constexpr (FMT == MOE_FMT_IQ1G) iq1g_table_f16(gtab, tid, kThreads);
   wait_vmcnt<2 * kB>();
   __syncthreads();
 
@@ -1027,6 +1161,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
           else if constexpr (S == 1)
             load_frag_q8_pair(bnext, P.p[0], P.p[1], H, cbl + (lane & 15), stn);
           else if constexpr (S == 2) load_a_half(h, off, stn * GBK, Anext, wave, lane, 1);
+        } else if constexpr (AF16 && FMT == MOE_FMT_IQ1G) {
+          // token rows first, the weights (4 registers per tile) after
+          // sub-step 1 (issued at sub-step 3 as for IQ3G, the compiler
+          // spilled 75 registers; here 8, as in the NVFP4 kernel)
+          if constexpr (S == 0) {
+            load_a_half(h, off, stn * GBK, Anext, wave, lane, 0);
+            load_a_half(h, off, stn * GBK, Anext, wave, lane, 1);
+          } else if constexpr (S == 1) {
+            load_frag_iq1g_pair(bnext, P.p[0], P.p[1], P.p[2], H, cbl, stn);
+          }
         } else if constexpr (AF16 && FMT == MOE_FMT_IQ3G) {
           // token rows first; the weights after sub-step 3's dequant, when
           // this step's fragments are dead and the next step's can take their
@@ -1194,6 +1338,17 @@ hipError_t launch_gemm_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T
     } else {
       DOWN(MOE_FMT_IQ3G, false, true, 1, qi, qs, qc, z);
       DOWN(MOE_FMT_IQ3G, false, false, 2, qi, qs, qc, z);
+    }
+  } else if (L->fmt_down == MOE_FMT_IQ1G) {
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<true, false>), grid, block, 0, s, GU_ARGS);
+    hipLaunchKernelGGL((k_gemm_gateup_nvfp4<false, true>), grid, block, 0, s, GU_ARGS);
+    const size_t qi = lay.down_q, qh = lay.down_s, qc = lay.down_sc, z = 0;
+    if (bf) {
+      DOWN(MOE_FMT_IQ1G, true, true, 1, qi, qh, qc, z);
+      DOWN(MOE_FMT_IQ1G, true, false, 2, qi, qh, qc, z);
+    } else {
+      DOWN(MOE_FMT_IQ1G, false, true, 1, qi, qh, qc, z);
+      DOWN(MOE_FMT_IQ1G, false, false, 2, qi, qh, qc, z);
     }
   } else {
     hipLaunchKernelGGL((k_gemm_gateup_nvfp4<true, false>), grid, block, 0, s, GU_ARGS);

@@ -43,6 +43,7 @@ typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) v4u_t g_v4u;
 typedef __attribute__((address_space(1))) v2u_t g_v2u;
 typedef __attribute__((address_space(1))) uint16_t g_u16;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
   const v4u_t t = __builtin_nontemporal_load((const g_v4u*)(uintptr_t)p);
   return make_uint4(t.x, t.y, t.z, t.w);
@@ -51,12 +52,16 @@ __device__ __forceinline__ uint2 ld8(const uint8_t* p) {
   const v2u_t t = __builtin_nontemporal_load((const g_v2u*)(uintptr_t)p);
   return make_uint2(t.x, t.y);
 }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) {
+  return __builtin_nontemporal_load((const g_u32*)(uintptr_t)p);
+}
 __device__ __forceinline__ uint16_t ld2(const uint8_t* p) {
   return __builtin_nontemporal_load((const g_u16*)(uintptr_t)p);
 }
 #else
 __device__ uint4 ld16(const uint8_t* p);
 __device__ uint2 ld8(const uint8_t* p);
+__device__ uint32_t ld4(const uint8_t* p);
 __device__ uint16_t ld2(const uint8_t* p);
 #endif
 

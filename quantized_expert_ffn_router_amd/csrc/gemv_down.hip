@@ -10,6 +10,9 @@
 //   IQ3G (IQ3-style codebook, own grid, iq3g.h): per 4 elements an 8-bit index
 //     into a grid of odd magnitudes m <= 9, a sign bit per element, an odd
 //     multiplier 2 s + 1 per 32 and fp16 d per 256: w = d * (2 s + 1) * +-m.
+//   IQ1G (IQ1-style codebook, own grid, iq1g.h): per 8 elements a 10-bit index
+//     into a grid of ternary vectors v in {-1, 0, +1}^8, an odd multiplier
+//     2 s + 1 per 32 and fp16 d per 256: w = d * (2 s + 1) * v.
 // Weights are decoded exactly to bf16 (E2M1 has 2 significant bits, q - 32 is
 // a 6-bit integer, an int8 code has at most 8) and meet h (bf16, from the gate/up kernel) in
 // v_dot2_f32_bf16 with fp32 accumulation.  Each 16-element block sum is scaled
@@ -59,10 +62,17 @@ struct Group<MOE_FMT_IQ3G> {
   uint2 sc;    // d fp16 and the superblock's 8 nibble multipliers
 };
 
+template <>
+struct Group<MOE_FMT_IQ1G> {
+  uint4 q;      // low bytes of the 16 grid indices (8 elements each)
+  uint32_t qh;  // their 2-bit high parts
+  uint2 sc;     // d fp16 and the superblock's 8 nibble multipliers
+};
+
 struct Planes {
-  const uint8_t* a;  // NVFP4 codes | Q6_K ql | Q8_0 codes | IQ3G indices
-  const uint8_t* b;  // NVFP4 scales | Q6_K qh | Q8_0 scales | IQ3G signs
-  const uint8_t* c;  // Q6_K sc | IQ3G d and multipliers
+  const uint8_t* a;  // NVFP4 codes | Q6_K ql | Q8_0 codes | IQ3G indices | IQ1G index low bytes
+  const uint8_t* b;  // NVFP4 scales | Q6_K qh | Q8_0 scales | IQ3G signs | IQ1G index high bits
+  const uint8_t* c;  // Q6_K sc | IQ3G, IQ1G d and multipliers
   const uint8_t* d;  // Q6_K d
 };
 
@@ -96,6 +106,13 @@ __device__ __forceinline__ void load_group(Group<MOE_FMT_IQ3G>& r, const Planes&
 #pragma unroll
   for (int q = 0; q < 2; ++q) r.q[q] = ld16(P.a + (((size_t)(2 * g + q)) * H + nc) * 16);
   r.sg = ld16(P.b + ((size_t)g * H + nc) * 16);
+  r.sc = ld8(P.c + ((size_t)(g >> 1) * H + nc) * 8);
+}
+
+__device__ __forceinline__ void load_group(Group<MOE_FMT_IQ1G>& r, const Planes& P, int H,
+                                           size_t nc, int g) {
+  r.q = ld16(P.a + ((size_t)g * H + nc) * 16);
+  r.qh = ld4(P.b + ((size_t)g * H + nc) * 4);
   r.sc = ld8(P.c + ((size_t)(g >> 1) * H + nc) * 8);
 }
 
@@ -204,6 +221,44 @@ __device__ __forceinline__ void decode_group_iq3g(const Group<MOE_FMT_IQ3G>& r, 
   }
 }
 
+// The IQ1G grid as bf16 pairs in LDS: entry e = the pairs (v0, v1) .. (v6, v7)
+// of values -1, 0, +1 (exact).
+__device__ __forceinline__ void iq1g_table_bf16(uint4* tab, int tid, int nthreads) {
+  for (int e = tid; e < 1024; e += nthreads) {
+    const uint32_t c = kIq1gGridDev.c[e];
+    auto pair = [c](int p) {  // values 2p, 2p + 1
+      const uint32_t lo = ((c >> (4 * p)) & 1u) * 0x3f80u | ((c >> (4 * p + 1)) & 1u) << 15;
+      const uint32_t hi = ((c >> (4 * p + 2)) & 1u) * 0x3f80u | ((c >> (4 * p + 3)) & 1u) << 15;
+      return lo | (hi << 16);
+    };
+    tab[e] = make_uint4(pair(0), pair(1), pair(2), pair(3));
+  }
+}
+
+// Exact bf16 pairs of a 128-element IQ1G group (half h = g & 1 of its
+// superblock) and the fp32 scales d * (2 s + 1) of its 8 blocks of 16.
+__device__ __forceinline__ void decode_group_iq1g(const Group<MOE_FMT_IQ1G>& r, int h,
+                                                  const uint4* tab, v2bf_t (*w)[8], float* sc) {
+  const float d = f16_to_f32((uint16_t)(r.sc.x & 0xffffu));
+  const uint32_t mul = (r.sc.x >> 16) | (r.sc.y << 16);  // nibble j: multiplier of sub-block j
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int j = 4 * h + (b >> 1);
+    sc[b] = d * (float)(2u * ((mul >> (4 * j)) & 15u) + 1u);
+    const uint32_t lo = word_of(r.q, b >> 1);  // index low bytes of groups 4(b/2) .. +3
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // the block's groups of 8: 2b, 2b + 1
+      const int gi = 2 * b + i;
+      const uint32_t idx = ((lo >> (8 * (gi & 3))) & 255u) | (((r.qh >> (2 * gi)) & 3u) << 8);
+      const uint4 v = tab[idx];
+      w[b][4 * i] = as_v2bf(v.x);
+      w[b][4 * i + 1] = as_v2bf(v.y);
+      w[b][4 * i + 2] = as_v2bf(v.z);
+      w[b][4 * i + 3] = as_v2bf(v.w);
+    }
+  }
+}
+
 // Issue the loads of the first D groups of a pass.
 template <int FMT, int GP, int D>
 __device__ __forceinline__ void dn_issue(Group<FMT> (&r)[GP], const Planes& P, int H, size_t nc,
@@ -224,7 +279,7 @@ template <int FMT, int GP, int D>
 __device__ __forceinline__ void dn_consume(Group<FMT> (&r)[GP], const uint16_t* __restrict__ h,
                                            int p0, int H, int I, size_t nc, const Planes& P,
                                            float ts, int gb, int mt, float* acc,
-                                           const uint2* tab) {
+                                           const uint2* tab, const uint4* tab1) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int gi = 0; gi < GP; ++gi) {
@@ -264,6 +319,7 @@ __device__ __forceinline__ void dn_consume(Group<FMT> (&r)[GP], const uint16_t* 
       v2bf_t w[8][8];
       float sc[8];
       if constexpr (FMT == MOE_FMT_IQ3G) decode_group_iq3g(r[gi], g & 1, tab, w, sc);
+      else if constexpr (FMT == MOE_FMT_IQ1G) decode_group_iq1g(r[gi], g & 1, tab1, w, sc);
       else decode_group(r[gi], ts, w, sc);
 #pragma unroll 1
       for (int t = 0; t < mt; ++t) {
@@ -291,7 +347,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const int32_t* __restrict__ n_active, void* __restrict__ y) {
   extern __shared__ __align__(16) float red[];  // [S][kDnMT][64]
-  __shared__ uint2 tab[FMT == MOE_FMT_IQ3G ? 256 : 1];  // IQ3G grid as bf16 pairs
+  __shared__ uint2 tab[FMT == MOE_FMT_IQ3G ? 256 : 1];    // IQ3G grid as bf16 pairs
+  __shared__ uint4 tab1[FMT == MOE_FMT_IQ1G ? 1024 : 1];  // IQ1G grid as bf16 pairs
 
   int e;
   moe_expert_ref ref;
@@ -331,6 +388,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
             __syncthreads();
           }
         }
+        if constexpr (FMT == MOE_FMT_IQ1G) {
+          if (c0 == 0) {
+            iq1g_table_bf16(tab1, tid, nthreads);
+            __syncthreads();
+          }
+        }
       }
       {  // the pass's h values of the first 4 tokens (4 lines per group)
         uint32_t tch = 0;
@@ -342,7 +405,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
                                        64 * (gb + sg));
         keep_scalar(tch);
       }
-      dn_consume<FMT, GP, D>(r, h, base + c0, H, I, nc, P, ts, gb + sg, mt, acc, tab);
+      dn_consume<FMT, GP, D>(r, h, base + c0, H, I, nc, P, ts, gb + sg, mt, acc, tab, tab1);
     }
     __syncthreads();
     for (int o = tid; o < mt * 64; o += nthreads) {
@@ -365,7 +428,7 @@ hipError_t down_t(const moe_layer_desc* L, const uint16_t* h, const moe_buckets*
   Planes P;
   if (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_Q8_0) {
     P = {(const uint8_t*)lay.down_q, (const uint8_t*)lay.down_s, nullptr, nullptr};
-  } else if (FMT == MOE_FMT_IQ3G) {
+  } else if (FMT == MOE_FMT_IQ3G || FMT == MOE_FMT_IQ1G) {
     P = {(const uint8_t*)lay.down_q, (const uint8_t*)lay.down_s, (const uint8_t*)lay.down_sc,
          nullptr};
   } else {
@@ -418,6 +481,7 @@ hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const mo
   if (L->fmt_down == MOE_FMT_Q6K) return down_fmt<MOE_FMT_Q6K>(L, h, b, max_slots, y, y_dtype, s);
   if (L->fmt_down == MOE_FMT_Q8_0) return down_fmt<MOE_FMT_Q8_0>(L, h, b, max_slots, y, y_dtype, s);
   if (L->fmt_down == MOE_FMT_IQ3G) return down_fmt<MOE_FMT_IQ3G>(L, h, b, max_slots, y, y_dtype, s);
+  if (L->fmt_down == MOE_FMT_IQ1G) return down_fmt<MOE_FMT_IQ1G>(L, h, b, max_slots, y, y_dtype, s);
   return down_fmt<MOE_FMT_NVFP4>(L, h, b, max_slots, y, y_dtype, s);
 }
 

@@ -1,4 +1,4 @@
-// pack.hip -- re-arrange canonical NVFP4 / Q6_K-style / Q8_0 / IQ3G expert bytes into the
+// pack.hip -- re-arrange canonical NVFP4 / Q6_K-style / Q8_0 / IQ3G / IQ1G expert bytes into the
 // device blob (16-byte granules transposed from [row][granule] to
 // [granule][row], see common.h).  A one-time byte permutation at load.
 #include "common.h"
@@ -44,7 +44,9 @@ __global__ void k_pack_granules(const uint8_t* __restrict__ src, size_t src_expe
 //          with M = max |d * sc|, M * 2^s < 2^5 keeps the fp16 factor below
 //          2^15 and |w| * 2^s below 2^10;
 //   IQ3G:  w * 2^s = (m * (2 s_j + 1)) * (d * 2^s), m * (2 s_j + 1) <= 279:
-//          with M = max |d|, M * 2^s < 2^6 keeps |w| * 2^s below 2^15.
+//          with M = max |d|, M * 2^s < 2^6 keeps |w| * 2^s below 2^15;
+//   IQ1G:  w * 2^s = (v * (2 s_j + 1)) * (d * 2^s), |v * (2 s_j + 1)| <= 31:
+//          with M = max |d|, M * 2^s < 2^9 keeps |w| * 2^s below 2^14.
 // s = P - e for M = f * 2^e (f in [0.5, 1)) is the largest such s; all-zero
 // scales give s = 0.  Clamped to [-64, 64].
 __global__ __launch_bounds__(256) void k_down_exponent(const uint8_t* __restrict__ src,
@@ -55,8 +57,11 @@ __global__ __launch_bounds__(256) void k_down_exponent(const uint8_t* __restrict
   const uint8_t* s = src + (size_t)blockIdx.x * src_expert_stride;
   float m = 0.0f;
   for (int64_t b = threadIdx.x; b < nblocks; b += blockDim.x) {
-    if (fmt == MOE_FMT_Q8_0 || fmt == MOE_FMT_IQ3G) {  // d leads both blocks
-      const uint8_t* blk = s + (size_t)b * (fmt == MOE_FMT_Q8_0 ? 34 : kIq3gBlockBytes);
+    if (fmt == MOE_FMT_Q8_0 || fmt == MOE_FMT_IQ3G || fmt == MOE_FMT_IQ1G) {  // d leads
+      const uint8_t* blk =
+          s + (size_t)b * (fmt == MOE_FMT_Q8_0 ? 34
+                                               : (fmt == MOE_FMT_IQ3G ? kIq3gBlockBytes
+                                                                      : kIq1gBlockBytes));
       m = fmaxf(m, fabsf(f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)))));
     } else {
       const uint8_t* blk = s + (size_t)b * 210;
@@ -75,7 +80,10 @@ __global__ __launch_bounds__(256) void k_down_exponent(const uint8_t* __restrict
     const float M = red[0];
     int e = 0;
     (void)frexpf(M, &e);
-    const int P = (fmt == MOE_FMT_Q8_0) ? 8 : (fmt == MOE_FMT_IQ3G ? 6 : 5);
+    const int P = (fmt == MOE_FMT_Q8_0)   ? 8
+                  : (fmt == MOE_FMT_IQ3G) ? 6
+                  : (fmt == MOE_FMT_IQ1G) ? 9
+                                          : 5;
     int sx = (M > 0.0f && M <= 3.0e38f) ? P - e : 0;
     sx = sx < -64 ? -64 : (sx > 64 ? 64 : sx);
     *reinterpret_cast<int32_t*>(meta + (size_t)blockIdx.x * dst_expert_stride) = sx;
@@ -87,7 +95,10 @@ __global__ __launch_bounds__(256) void k_down_exponent(const uint8_t* __restrict
 hipError_t launch_down_exponent(const uint8_t* down_q, int E, int64_t H, int64_t I, int fmt,
                                 uint8_t* meta, size_t dst_expert_stride, hipStream_t s) {
   const int64_t per_row = (fmt == MOE_FMT_Q8_0) ? I / 32 : I / 256;
-  const size_t bsz = (fmt == MOE_FMT_Q8_0) ? 34 : (fmt == MOE_FMT_IQ3G ? kIq3gBlockBytes : 210);
+  const size_t bsz = (fmt == MOE_FMT_Q8_0)   ? 34
+                     : (fmt == MOE_FMT_IQ3G) ? kIq3gBlockBytes
+                     : (fmt == MOE_FMT_IQ1G) ? kIq1gBlockBytes
+                                             : 210;
   const int64_t nblocks = H * per_row;
   hipLaunchKernelGGL(k_down_exponent, dim3((unsigned)E), dim3(256), 0, s, down_q,
                      (size_t)nblocks * bsz, nblocks, fmt, meta, dst_expert_stride);

@@ -122,7 +122,7 @@ def test_zero_tokens_is_a_noop_and_null_checks():
 
 def test_blob_bytes_per_down_format():
     """Sections start on 256-byte boundaries: gate and up (NVFP4 codes and
-    scales), then the down projection's planes; Q6_K, Q8_0 and IQ3G blobs end
+    scales), then the down projection's planes; Q6_K, Q8_0, IQ3G and IQ1G blobs end
     with a 256-byte section for the grouped GEMM's per-expert weight
     exponent."""
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
@@ -140,6 +140,12 @@ def test_blob_bytes_per_down_format():
     assert q.moe_expert_blob_bytes(H, I, 1, 4) == gu + al(H * I // 4) + al(H * I // 8) + \
         al(H * I // 32) + 256
     assert q.moe_expert_blob_bytes(H, 384, 1, 4) == 0
+    # IQ1G: index low bytes (I/8 per row), 2-bit high parts (I/32), d and
+    # multipliers (8 bytes per 256), exponent section
+    assert q.moe_expert_blob_bytes(H, I, 1, 5) == gu + al(H * I // 8) + al(H * I // 32) + \
+        al(H * I // 32) + 256
+    assert q.moe_expert_blob_bytes(H, 384, 1, 5) == 0
+    assert "IQ1G" in q.last_error()
 
 
 def test_workspace_bytes_cover_hidden_buffers():
@@ -212,3 +218,30 @@ def test_library_grid_equals_oracle_grid():
     m = np.array([int(v) for v in out], np.uint32)
     lib_grid = np.stack([(m >> (8 * c)) & 255 for c in range(4)], axis=1).astype(np.uint8)
     np.testing.assert_array_equal(lib_grid, oracle.iq3g_grid())
+
+
+def test_library_iq1g_grid_equals_oracle_grid():
+    """The library builds the IQ1G grid at compile time (csrc/iq1g.h, a
+    counting sort on the nonzero count, 2 bits per value); compiled on the
+    host here, its 1024 entries equal the oracle's (which walks the counts)."""
+    import os
+    import subprocess
+    import tempfile
+    import oracle
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hdr = os.path.join(root, "quantized_expert_ffn_router_amd", "csrc", "iq1g.h")
+    src = ('#include "%s"\n#include <cstdio>\nint main() {\n'
+           '  constexpr moe::Iq1gGrid g = moe::make_iq1g_grid();\n'
+           '  for (int e = 0; e < 1024; ++e) printf("%%u\\n", (unsigned)g.c[e]);\n}\n') % hdr
+    with tempfile.TemporaryDirectory() as d:
+        with open(os.path.join(d, "g.cpp"), "w") as f:
+            f.write(src)
+        subprocess.check_call(["g++", "-std=c++17", "-O1", os.path.join(d, "g.cpp"), "-o",
+                               os.path.join(d, "g")])
+        out = subprocess.check_output([os.path.join(d, "g")], text=True).split()
+    c = np.array([int(v) for v in out], np.uint32)
+    nz = np.stack([(c >> (2 * i)) & 1 for i in range(8)], axis=1)
+    neg = np.stack([(c >> (2 * i + 1)) & 1 for i in range(8)], axis=1)
+    assert not (neg & (1 - nz)).any()  # a negative flag only on a nonzero value
+    lib_grid = (nz * np.where(neg > 0, -1, 1)).astype(np.int8)
+    np.testing.assert_array_equal(lib_grid, oracle.iq1g_grid())

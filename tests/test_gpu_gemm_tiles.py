@@ -27,7 +27,7 @@ def _layer(fmt_down):
 
 
 @pytest.mark.parametrize("fmt_down", [moegen.FMT_NVFP4, moegen.FMT_Q6K, moegen.FMT_Q8_0,
-                                      moegen.FMT_IQ3G])
+                                      moegen.FMT_IQ3G, moegen.FMT_IQ1G])
 @pytest.mark.parametrize("y_dtype", [0, 1])
 def test_grouped_gemm_multi_tile_every_assignment(fmt_down, y_dtype):
     w, L = _layer(fmt_down)

@@ -238,13 +238,16 @@ def test_q8_0_prefill_sampled():
     (3e5, 0.02, 4),   # the same with IQ3G
     (1e-3, 0.02, 4),
     (1.0, 4.0, 4),
+    (3e5, 0.02, 5),   # the same with IQ1G
+    (1e-3, 0.02, 5),
+    (1.0, 4.0, 5),
 ])
 def test_gemm_activation_magnitudes(x_std, w_std, fmt_down):
     """The grouped GEMM multiplies fp16 operands; the token rows and h carry
     per-row power-of-two scales and an h overflow redoes the FFN with bf16 h.
     Results stay within the relative bars at any activation magnitude (the
     absolute bar of the other tests is for unit-scale activations)."""
-    I = 384 if fmt_down in (1, 3) else 512  # Q6_K and IQ3G need I % 256 == 0
+    I = 384 if fmt_down in (1, 3) else 512  # Q6_K, IQ3G and IQ1G need I % 256 == 0
     w, L = layer("gemm_mag", E=16, k=4, H=512, I=I, T=300, x_std=x_std, w_std=w_std,
                  fmt_down=fmt_down)
     x = moegen.make_tokens(w, w.T)
@@ -303,13 +306,14 @@ def test_graph_replay_matches_eager():
 
 
 def _scale_down_block_scales(L, exp2):
-    """Copy of layer L whose Q6_K / Q8_0 / IQ3G down block scales d (fp16)
+    """Copy of layer L whose Q6_K / Q8_0 / IQ3G / IQ1G down block scales d (fp16)
     are multiplied by 2^exp2 (rounded to fp16 where the result is subnormal;
     the oracle reads the same bytes)."""
     import dataclasses
     dq = L.down_q.copy()
     flat = dq.reshape(-1)
-    bsz, off = {moegen.FMT_Q8_0: (34, 0), moegen.FMT_IQ3G: (102, 0)}.get(L.fmt_down, (210, 208))
+    bsz, off = {moegen.FMT_Q8_0: (34, 0), moegen.FMT_IQ3G: (102, 0),
+                moegen.FMT_IQ1G: (46, 0)}.get(L.fmt_down, (210, 208))
     at = np.arange(flat.size // bsz) * bsz + off
     d = (flat[at].astype(np.uint16) | (flat[at + 1].astype(np.uint16) << 8)).view(np.float16)
     d2 = (d.astype(np.float64) * 2.0 ** exp2).astype(np.float16)
@@ -320,13 +324,15 @@ def _scale_down_block_scales(L, exp2):
     return dataclasses.replace(L, down_q=dq)
 
 
-@pytest.mark.parametrize("fmt_down,exp2", [(3, 18), (3, -10), (2, 16), (2, -8), (4, 16), (4, -10)])
+@pytest.mark.parametrize("fmt_down,exp2", [(3, 18), (3, -10), (2, 16), (2, -8), (4, 16), (4, -10),
+                                           (5, 20), (5, -10)])
 def test_gemm_down_weights_at_any_scale(fmt_down, exp2):
     """The grouped GEMM's fp16 down weights carry a per-expert power of two
     fixed at pack time from the expert's largest block scale: Q8_0 weights
     up to 16K (beyond the plain fp16 product q * d * 16) and Q6_K d * sc up to
     ~100 (beyond d * sc * 2^10 in fp16), IQ3G superblock scales d near 20
-    (weights up to ~5K), and block scales pushed into fp16's subnormal range,
+    (weights up to ~5K), IQ1G superblock scales d near 2,000 (weights up to ~60K), and
+    block scales pushed into fp16's subnormal range,
     all match the oracle at the relative bars."""
     I = 384 if fmt_down == 3 else 512
     w, L0 = layer("gemm_scale", E=16, k=4, H=512, I=I, T=300, fmt_down=fmt_down)
@@ -379,3 +385,37 @@ def test_iq3g_prefill_sampled():
     g, _ = check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
     (r, worst), n = check_block_edges(g, L, x)
     print(f"iq3g prefill block edges: {n} rows, rel L2 {r:.2e}, worst row {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_iq1g_decode_parity(B):
+    """The decode layer with the IQ1-style ternary-grid down projection (own
+    grid): dequant-fused GEMV with the grid in LDS as bf16 pairs."""
+    w, L = layer("iq1")
+    x = moegen.make_tokens(w, B, step=B + 4)
+    print("iq1g decode B", B, flush=True)
+    check_layer(L, x)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_iq1g_both_ffn_families_ragged(mode):
+    # 600 tokens x top-8 over 64 experts, I = 512 (4 groups of 128, 2
+    # superblocks, 4 K steps of the GEMM): GEMV (mode 1) and grouped GEMM
+    # (mode 2) against the oracle.
+    w, L = layer("iq1_many", E=64, k=8, H=256, I=512, T=600, fmt_down=moegen.FMT_IQ1G)
+    x = moegen.make_tokens(w, w.T, step=9)
+    res = moegen.make_residual(w, w.T)
+    print("iq1g ragged mode", mode, flush=True)
+    check_layer(L, x, residual=res, tokens=list(range(0, 600, 5)), ffn_mode=mode,
+                y_rel=GEMM_Y_REL)
+
+
+def test_iq1g_prefill_sampled():
+    """4096-token prefill of the IQ1G layer on the grouped GEMM path, with
+    the first and last row of every 128-row block."""
+    w, L = layer("iq1")
+    x = moegen.make_tokens(w, 4096, step=5)
+    print("iq1g prefill", flush=True)
+    g, _ = check_layer(L, x, tokens=list(range(0, 4096, 128)), y_dtype=1, y_rel=GEMM_Y_REL)
+    (r, worst), n = check_block_edges(g, L, x)
+    print(f"iq1g prefill block edges: {n} rows, rel L2 {r:.2e}, worst row {worst:.2e}", flush=True)
