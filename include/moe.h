@@ -323,6 +323,20 @@ moe_status moe_expert_ffn_noalloc(const moe_layer_desc* L, const uint16_t* x, in
                                   const moe_buckets* b, void* y, int32_t y_dtype,
                                   hipStream_t stream);
 
+/* moe_route_bucket followed by moe_expert_ffn (the layer's routing and its
+ * routed experts: basalt.jgulfo.com, "Expert tiers"), with the same arguments
+ * and the same outputs bit for bit (logits, top-k, buckets, histogram, y).  For
+ * batches of up to 4 tokens (with E <= 256, the GEMV family, NVFP4 gate/up
+ * with H <= 2048) it takes one launch fewer: every
+ * workgroup of the gate/up kernel repeats the batch's top-k and bucketing
+ * in its own LDS from the router logits and finds its expert there, and one
+ * of them writes the gating outputs.  Otherwise it makes the two calls.
+ * ws: at least moe_workspace_bytes(L, T) bytes (serves both steps). */
+moe_status moe_route_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T, float* logits,
+                         int32_t* topk_idx, float* topk_w, const moe_buckets* b, uint32_t* hist,
+                         int32_t decay_shift, int32_t unit_shift, void* y, int32_t y_dtype,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Gate-weighted combine: each token's output is its selected experts'
  * outputs weighted by the gates (the mixture the pages' model computes from
  * the few experts a token uses: basalt.jgulfo.com, "Expert tiers"), written

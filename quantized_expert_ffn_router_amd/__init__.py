@@ -102,6 +102,8 @@ SIGNATURES = {
     "moe_expert_ffn_noalloc": (ctypes.c_int, [_LP, _vp, _i64, _BP, _vp, _i32, _vp]),
     "moe_combine": (ctypes.c_int, [_LP, _vp, _i32, _BP, _vp, _i64, _vp, _vp, _vp]),
     "moe_expert_hist": (ctypes.c_int, [_LP, _BP, _vp, _i32, _i32, _vp]),
+    "moe_route_ffn": (ctypes.c_int, [_LP, _vp, _i64, _vp, _vp, _vp, _BP, _vp, _i32, _i32, _vp,
+                                      _i32, _vp, _sz, _vp]),
     "moe_route_bucket": (ctypes.c_int, [_LP, _vp, _i64, _vp, _vp, _vp, _BP, _vp, _sz, _vp, _i32,
                                          _i32, _vp]),
     "moe_tier_create": (ctypes.c_int, [ctypes.POINTER(TierDesc), ctypes.POINTER(ctypes.c_void_p)]),
@@ -225,6 +227,13 @@ def moe_route_bucket(desc, x, T, logits, topk_idx, topk_w, buckets, ws, ws_bytes
                                   _ptr(hist), decay_shift, unit_shift, _stream(stream)))
 
 
+def moe_route_ffn(desc, x, T, logits, topk_idx, topk_w, buckets, hist, decay_shift, unit_shift,
+                  y, y_dtype, ws, ws_bytes, stream=None):
+    _check(lib().moe_route_ffn(ctypes.byref(desc), _ptr(x), T, _ptr(logits), _ptr(topk_idx),
+                               _ptr(topk_w), ctypes.byref(buckets), _ptr(hist), decay_shift,
+                               unit_shift, _ptr(y), y_dtype, _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def moe_tier_create(desc: TierDesc) -> int:
     h = ctypes.c_void_p()
     _check(lib().moe_tier_create(ctypes.byref(desc), ctypes.byref(h)))
@@ -345,18 +354,19 @@ class StepBuffers:
 def layer_forward(layer: DeviceLayer, buf: StepBuffers, x, T: int, residual=None,
                   hist_shifts=(5, 10), stream=None, fused_gating=True):
     """One pass of the layer: route, bucket, expert FFN, combine, histogram.
-    fused_gating: one moe_route_bucket call (which also updates the
-    histogram) in place of moe_route + moe_bucket + moe_expert_hist."""
+    fused_gating: one moe_route_ffn call (routing, gating, buckets, histogram
+    and the expert FFN) in place of moe_route + moe_bucket + moe_expert_ffn +
+    moe_expert_hist."""
     d = layer.desc
     if fused_gating:
         h = None if hist_shifts is None else buf.hist
         ds, us = (0, 0) if hist_shifts is None else hist_shifts
-        moe_route_bucket(d, x, T, buf.logits, buf.idx, buf.w, buf.buckets, buf.ws, buf.ws_bytes,
-                         h, ds, us, stream)
+        moe_route_ffn(d, x, T, buf.logits, buf.idx, buf.w, buf.buckets, h, ds, us, buf.y,
+                      buf.y_dtype, buf.ws, buf.ws_bytes, stream)
     else:
         moe_route(d, x, T, buf.logits, buf.idx, buf.w, stream)
         moe_bucket(d, buf.idx, T, buf.buckets, buf.ws, buf.ws_bytes, stream)
-    moe_expert_ffn(d, x, T, buf.buckets, buf.y, buf.y_dtype, buf.ws, buf.ws_bytes, stream)
+        moe_expert_ffn(d, x, T, buf.buckets, buf.y, buf.y_dtype, buf.ws, buf.ws_bytes, stream)
     moe_combine(d, buf.y, buf.y_dtype, buf.buckets, buf.w, T, residual, buf.out, stream)
     if hist_shifts is not None and not fused_gating:
         moe_expert_hist(d, buf.buckets, buf.hist, hist_shifts[0], hist_shifts[1], stream)

@@ -433,6 +433,37 @@ moe_status moe_route_bucket(const moe_layer_desc* L, const uint16_t* x, int64_t 
   return hip_status(W, e);
 }
 
+moe_status moe_route_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T, float* logits,
+                         int32_t* topk_idx, float* topk_w, const moe_buckets* b, uint32_t* hist,
+                         int32_t decay_shift, int32_t unit_shift, void* y, int32_t y_dtype,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* W = "moe_route_ffn";
+  moe_status st = ffn_check(W, L, x, T, b, y, y_dtype);
+  if (st != MOE_OK) return st;
+  if (hist && (decay_shift < 0 || decay_shift > 31 || unit_shift < 0 || unit_shift > 31))
+    return fail(MOE_ERR_INVALID_ARG, "%s: shifts (%d, %d) must be in [0, 31]", W, decay_shift,
+                unit_shift);
+  if (T == 0) return MOE_OK;
+  CHECK_PTR(logits, W); CHECK_PTR(topk_idx, W); CHECK_PTR(topk_w, W); CHECK_PTR(ws, W);
+  CHECK_PTR(L->w_router, W);
+  const size_t need = ffn_ws(L, T);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
+  if (use_gemm(L, T) || !moe::gemv_gate_gateup32_fits(L, T)) {  // the two calls
+    st = moe_route_bucket(L, x, T, logits, topk_idx, topk_w, b, ws, ws_bytes, hist, decay_shift,
+                          unit_shift, stream);
+    if (st != MOE_OK) return st;
+    return ffn_launch(W, L, x, T, b, y, y_dtype, ws, stream);
+  }
+  const int max_slots = (int)((T * L->k < L->E) ? T * L->k : L->E);
+  uint16_t* h = (uint16_t*)ws;  // bf16 [T*k][I], sorted order
+  hipError_t e = moe::launch_router(x, T, L->H, L->w_router, L->router_bias, L->E, logits, stream);
+  if (e == hipSuccess)
+    e = moe::launch_gemv_gate_gateup32(L, x, T, logits, topk_idx, topk_w, b, hist, decay_shift,
+                                       unit_shift, max_slots, h, stream);
+  if (e == hipSuccess) e = moe::launch_gemv_down(L, h, b, max_slots, y, y_dtype, stream);
+  return hip_status(W, e);
+}
+
 moe_status moe_expert_hist(const moe_layer_desc* L, const moe_buckets* b, uint32_t* hist,
                            int32_t decay_shift, int32_t unit_shift, hipStream_t stream) {
   const char* W = "moe_expert_hist";

@@ -229,6 +229,14 @@ hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const mo
 bool gemv_gateup32_fits(const moe_layer_desc* L);
 hipError_t launch_gemv_gateup32(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
                                 int max_slots, uint16_t* h, hipStream_t s);
+// The decode gating (as launch_gate_fused: top-k, buckets, histogram, from
+// the router logits) and then the 32-row gate/up, in one launch; for the
+// layers and batches gemv_gate_gateup32_fits accepts.
+bool gemv_gate_gateup32_fits(const moe_layer_desc* L, int64_t T);
+hipError_t launch_gemv_gate_gateup32(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                                     const float* logits, int32_t* idx, float* w,
+                                     const moe_buckets* b, uint32_t* hist, int ds, int us,
+                                     int max_slots, uint16_t* h, hipStream_t s);
 
 
 }  // namespace moe

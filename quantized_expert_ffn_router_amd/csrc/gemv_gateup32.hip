@@ -26,6 +26,14 @@
 // Workgroup order: 4 consecutive slices of an expert run on one XCD one
 // after another (block ids 8 apart), sharing that XCD's L2 for the expert's
 // token rows.
+//
+// k_gemv_gate_gateup32 starts with the decode gating (gate_common.h) from the
+// router logits: each workgroup runs the top-k and bucketing of the whole
+// batch into its LDS, finds its slot's expert there and goes on as above;
+// workgroup 0 also writes the gating outputs (top-k, buckets, histogram).
+// One launch fewer per layer step than gating and gate/up apart, the same
+// results bit for bit.
+#include "gate_common.h"
 #include "gemv_gateup.h"
 
 namespace moe {
@@ -201,6 +209,71 @@ k_gemv_gateup32_nvfp4(const uint16_t* __restrict__ x, int H, int I, int ktop, in
   } while (c0 < cnt);
 }
 
+// The gating of the batch (all T tokens) by every workgroup, then its slice
+// of gate/up as in k_gemv_gateup32_nvfp4 (T <= kGateGemvMaxT: one pass of
+// tokens).
+template <int NP, int NV>
+__global__ __launch_bounds__(kG32Threads) __attribute__((amdgpu_waves_per_eu(4))) void
+k_gemv_gate_gateup32(const uint16_t* __restrict__ x, int H, int I, int ktop, int NS,
+                     int max_slots, int nparts, const moe_expert_ref* __restrict__ experts,
+                     size_t off_gq, size_t off_gs, size_t off_uq, size_t off_us,
+                     const float* __restrict__ logits, int T, int E, int renorm, GateOut out,
+                     uint16_t* __restrict__ hout) {
+  __shared__ float red[kG32Waves][kGuMT][64];  // [wave][token][lane] partial sums
+  __shared__ GateLds gl;
+  __shared__ int s_tok[kGuMT];  // the expert's tokens, ascending
+
+  int slot, j;
+  if (!g32_item(NS, max_slots, &slot, &j)) return;  // block 0 has slot 0
+  const int tid = threadIdx.x, lane = tid & 63;
+  gate_block<NV>(gl, logits, T, E, ktop, renorm, out, blockIdx.x == 0, tid, kG32Threads);
+  if (slot >= gl.n_active) return;
+  const int e = gl.active[slot];
+  const moe_expert_ref ref = experts[e];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool up = lane >= 32;
+  const uint32_t n = (uint32_t)j * 32u + (uint32_t)(lane & 31);  // row of the slice
+  const uint8_t* blob = (const uint8_t*)ref.blob;  // wave-uniform
+  const uint32_t aq = (uint32_t)(up ? off_uq : off_gq) + n * 16u;
+  const uint32_t as = (uint32_t)(up ? off_us : off_gs) + n * 8u;
+  const bool part = wave < nparts;
+
+  G32A<NP> ra;
+  if (part) g32_load<NP>(ra, blob, aq, as, I, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned long long m = gl.tmask[e];
+  const int cnt = __popcll(m), base = gl.off[e];
+  if (tid < T && ((m >> tid) & 1ull)) s_tok[__popcll(m & ((1ull << tid) - 1ull))] = tid;
+  __syncthreads();
+  if (part) {
+    // the first 4 tokens' activation lines, while the weights are in flight
+    uint32_t tch = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < cnt) {
+        const uint32_t* xp = reinterpret_cast<const uint32_t*>(x + (size_t)s_tok[t] * H);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) tch ^= xp[16 * (wave + kG32Waves * i)];
+      }
+    }
+    keep_scalar(tch);
+#pragma unroll 1
+    for (int t = 0; t < cnt; ++t)
+      red[wave][t][lane] = g32_token<NP>(ra, x, (uint32_t)s_tok[t] * (uint32_t)H, wave);
+  }
+  __syncthreads();
+  for (int o = tid; o < cnt * 32; o += kG32Threads) {
+    const int t = o >> 5, r = o & 31;
+    float g = 0.0f, u = 0.0f;
+    for (int w = 0; w < nparts; ++w) {
+      g += red[w][t][r];
+      u += red[w][t][32 + r];
+    }
+    hout[(size_t)(base + t) * I + j * 32 + r] =
+        f32_to_bf16_rne(swiglu(g * ref.ts_gate, u * ref.ts_up));
+  }
+}
+
 }  // namespace
 
 bool gemv_gateup32_fits(const moe_layer_desc* L) {
@@ -241,6 +314,56 @@ hipError_t launch_gemv_gateup32(const moe_layer_desc* L, const uint16_t* x, cons
     default: G32(8); break;
   }
 #undef G32
+  return hipGetLastError();
+}
+
+// Every workgroup repeats the batch's gating before it knows its expert: at
+// batch 8 that put about 3 us more in front of each workgroup's weight loads
+// than the separate gating launch costs (step 44.4 against 41.6 us), while up
+// to 4 tokens it saves 0.8-1.0 us per step.
+constexpr int kGateGemvMaxT = 4;
+
+bool gemv_gate_gateup32_fits(const moe_layer_desc* L, int64_t T) {
+  return gemv_gateup32_fits(L) && gate_fused_fits(T, L->E, L->k) && T <= kGateGemvMaxT;
+}
+
+hipError_t launch_gemv_gate_gateup32(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                                     const float* logits, int32_t* idx, float* w,
+                                     const moe_buckets* b, uint32_t* hist, int ds, int us,
+                                     int max_slots, uint16_t* h, hipStream_t s) {
+  const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
+  const int NS = L->I / 32;
+  const int ngran = L->H / 32;
+  const int nparts = ngran < kG32Waves ? ngran : kG32Waves;
+  const int NP = ngran / nparts;
+  const int groups = max_slots * (NS / 4);
+  const unsigned nblocks = (unsigned)(((groups + 7) / 8) * 32);
+  const GateOut out = {idx, w, b->counts, b->offsets, b->active, b->n_active, b->sorted_asg,
+                       b->asg_pos, hist, ds, us};
+#define GG(P, V)                                                                                \
+  hipLaunchKernelGGL((k_gemv_gate_gateup32<P, V>), dim3(nblocks), dim3(kG32Threads), 0, s, x,   \
+                     L->H, L->I, L->k, NS, max_slots, nparts, L->experts, lay.gate_q, lay.gate_s, \
+                     lay.up_q, lay.up_s, logits, (int)T, L->E, L->renormalize, out, h)
+#define GG_NP(V)                 \
+  switch (NP) {                  \
+    case 1: GG(1, V); break;     \
+    case 2: GG(2, V); break;     \
+    case 3: GG(3, V); break;     \
+    case 4: GG(4, V); break;     \
+    case 5: GG(5, V); break;     \
+    case 6: GG(6, V); break;     \
+    case 7: GG(7, V); break;     \
+    default: GG(8, V); break;    \
+  }
+  if (L->E <= 64) {
+    GG_NP(1);
+  } else if (L->E <= 128) {
+    GG_NP(2);
+  } else {
+    GG_NP(4);
+  }
+#undef GG_NP
+#undef GG
   return hipGetLastError();
 }
 
