@@ -67,8 +67,9 @@ def parse():
                    help="steps of the graph-captured tiered run (0: skip)")
     p.add_argument("--no-tiered-check", action="store_true",
                    help="skip the all-resident run the tiered outputs are compared with")
-    p.add_argument("--cpu-sample-steps", type=int, default=12,
-                   help="decode steps of the oracle on all host cores (single-threaded: a quarter)")
+    p.add_argument("--cpu-sample-steps", type=int, default=192,
+                   help="decode steps of the oracle on all host cores (about 10 s; "
+                        "single-threaded: a sixteenth)")
     p.add_argument("--cpu-prefill-tokens", type=int, default=1024,
                    help="tokens of the prefill slice the oracle runs (extrapolated to 16384)")
     p.add_argument("--profile-steps", type=int, default=0,
@@ -769,7 +770,7 @@ def cpu_baseline(W, L, B, n_steps, prefill_tokens):
         oracle.layer(moegen.make_tokens(W, B, step=10_000 + s), L, parallel=True)
     dt_all = time.time() - t
     progress(f"cpu baseline: {n_steps} decode steps on all cores in {dt_all:.1f} s")
-    n_single = max(1, n_steps // 4)
+    n_single = max(1, n_steps // 16)
     t = time.time()
     for s in range(n_single):
         oracle.layer(moegen.make_tokens(W, B, step=20_000 + s), L)
