@@ -44,6 +44,10 @@ def parse():
     p.add_argument("--batches", type=str, default="1,2,4,8,16,32",
                    help="decode batch sizes; 16 and 32 are verification-sized batches "
                         "(a few slots with draft tokens)")
+    p.add_argument("--keep-y", action="store_true",
+                   help="decode steps write the expert outputs y and combine them in a "
+                        "separate launch (default: moe_layer_forward, which fuses the down "
+                        "projection with the combine for batches of 2 to 8)")
     p.add_argument("--head-batch", type=int, default=8,
                    help="the batch the headline value is reported for (largest if absent)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -211,7 +215,8 @@ def main():
               for s in range(X_POOL)]
 
         def step(i):
-            return q.layer_forward(layers[i % N_LAYERS], buf, xs[i % X_POOL], B, stream=stream)
+            return q.layer_forward(layers[i % N_LAYERS], buf, xs[i % X_POOL], B, stream=stream,
+                                   keep_y=args.keep_y)
 
         # cold: the first step of this batch size, before any warm-up (eager
         # launches; the first batch's also pays the library's first launches)

@@ -337,6 +337,22 @@ moe_status moe_route_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T, 
                          int32_t decay_shift, int32_t unit_shift, void* y, int32_t y_dtype,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The whole layer step: moe_route_ffn then moe_combine (same arguments,
+ * routing outputs, buckets and histogram bit for bit; out within the bf16
+ * rounding of the combine).  For decode batches of 2 to 8 tokens on the
+ * GEMV family the down projection and the combine run as one kernel that
+ * writes out straight from h: y is then not written (the caller still
+ * passes it, for the other sizes), and out sums each token's k gate-weighted
+ * expert rows in a fixed order (slots j = w mod 8 for each w, then w
+ * ascending) -- the mixture of the experts a token uses (basalt.jgulfo.com,
+ * "Expert tiers").  residual: bf16 [T][H] or NULL; out: bf16 [T][H] (may
+ * alias residual).  ws: at least moe_workspace_bytes(L, T) bytes. */
+moe_status moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                             const uint16_t* residual, uint16_t* out, float* logits,
+                             int32_t* topk_idx, float* topk_w, const moe_buckets* b,
+                             uint32_t* hist, int32_t decay_shift, int32_t unit_shift, void* y,
+                             int32_t y_dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Gate-weighted combine: each token's output is its selected experts'
  * outputs weighted by the gates (the mixture the pages' model computes from
  * the few experts a token uses: basalt.jgulfo.com, "Expert tiers"), written

@@ -104,6 +104,8 @@ SIGNATURES = {
     "moe_expert_hist": (ctypes.c_int, [_LP, _BP, _vp, _i32, _i32, _vp]),
     "moe_route_ffn": (ctypes.c_int, [_LP, _vp, _i64, _vp, _vp, _vp, _BP, _vp, _i32, _i32, _vp,
                                       _i32, _vp, _sz, _vp]),
+    "moe_layer_forward": (ctypes.c_int, [_LP, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _BP, _vp, _i32,
+                                          _i32, _vp, _i32, _vp, _sz, _vp]),
     "moe_route_bucket": (ctypes.c_int, [_LP, _vp, _i64, _vp, _vp, _vp, _BP, _vp, _sz, _vp, _i32,
                                          _i32, _vp]),
     "moe_tier_create": (ctypes.c_int, [ctypes.POINTER(TierDesc), ctypes.POINTER(ctypes.c_void_p)]),
@@ -234,6 +236,14 @@ def moe_route_ffn(desc, x, T, logits, topk_idx, topk_w, buckets, hist, decay_shi
                                unit_shift, _ptr(y), y_dtype, _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def moe_layer_forward(desc, x, T, residual, out, logits, topk_idx, topk_w, buckets, hist,
+                      decay_shift, unit_shift, y, y_dtype, ws, ws_bytes, stream=None):
+    _check(lib().moe_layer_forward(ctypes.byref(desc), _ptr(x), T, _ptr(residual), _ptr(out),
+                                   _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                   ctypes.byref(buckets), _ptr(hist), decay_shift, unit_shift,
+                                   _ptr(y), y_dtype, _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def moe_tier_create(desc: TierDesc) -> int:
     h = ctypes.c_void_p()
     _check(lib().moe_tier_create(ctypes.byref(desc), ctypes.byref(h)))
@@ -352,12 +362,20 @@ class StepBuffers:
 
 
 def layer_forward(layer: DeviceLayer, buf: StepBuffers, x, T: int, residual=None,
-                  hist_shifts=(5, 10), stream=None, fused_gating=True):
+                  hist_shifts=(5, 10), stream=None, fused_gating=True, keep_y=True):
     """One pass of the layer: route, bucket, expert FFN, combine, histogram.
     fused_gating: one moe_route_ffn call (routing, gating, buckets, histogram
     and the expert FFN) in place of moe_route + moe_bucket + moe_expert_ffn +
-    moe_expert_hist."""
+    moe_expert_hist.  keep_y=False (with fused_gating): one moe_layer_forward
+    call, which for decode batches fuses the down projection with the
+    combine and leaves buf.y unwritten."""
     d = layer.desc
+    if fused_gating and not keep_y:
+        h = None if hist_shifts is None else buf.hist
+        ds, us = (0, 0) if hist_shifts is None else hist_shifts
+        moe_layer_forward(d, x, T, residual, buf.out, buf.logits, buf.idx, buf.w, buf.buckets, h,
+                          ds, us, buf.y, buf.y_dtype, buf.ws, buf.ws_bytes, stream)
+        return buf.out
     if fused_gating:
         h = None if hist_shifts is None else buf.hist
         ds, us = (0, 0) if hist_shifts is None else hist_shifts

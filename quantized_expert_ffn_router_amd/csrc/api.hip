@@ -119,6 +119,13 @@ bool gemm_fits(const moe_layer_desc* L, int64_t T) {
 
 // Grouped GEMM once experts average >= 16 tokens (and the batch is not a
 // decode step); dequant-fused GEMV otherwise.
+// Batches of 2 to 8 tokens run the down projection and the combine as one
+// kernel in moe_layer_forward (graph-replayed steps: batch 8 39.0 against
+// 41.8 us, batch 4 27.7 against 29.5; at batch 1 its 32 workgroups pull
+// each CU's 221 KB of expert rows too slowly, 20.0 against 19.2 us, and at
+// batch 16 the experts that several tokens share are read once per token).
+constexpr int64_t kDownCombineMinT = 2, kDownCombineMaxT = 8;
+
 bool use_gemm(const moe_layer_desc* L, int64_t T) {
   if (L->ffn_mode == MOE_FFN_GEMV) return false;
   if (L->ffn_mode == MOE_FFN_GEMM) return true;
@@ -305,6 +312,17 @@ moe_status ffn_check(const char* W, const moe_layer_desc* L, const uint16_t* x, 
   return MOE_OK;
 }
 
+// The GEMV family's gate/up into h (bf16 [T*k][I], sorted order): 32-row
+// slices for up to 16 tokens (it redoes the weight decode per token, which
+// costs more than it saves once experts hold many tokens), else 64-row blocks.
+hipError_t gemv_gateup_launch(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                              const moe_buckets* b, int max_slots, uint16_t* h,
+                              hipStream_t stream) {
+  return (T <= 16 && moe::gemv_gateup32_fits(L))
+             ? moe::launch_gemv_gateup32(L, x, b, max_slots, h, stream)
+             : moe::launch_gemv_gateup(L, x, b, max_slots, h, stream);
+}
+
 // The FFN's launches (checks done, T > 0, ws holds ffn_ws(L, T) bytes).
 moe_status ffn_launch(const char* W, const moe_layer_desc* L, const uint16_t* x, int64_t T,
                       const moe_buckets* b, void* y, int32_t y_dtype, void* ws,
@@ -319,11 +337,7 @@ moe_status ffn_launch(const char* W, const moe_layer_desc* L, const uint16_t* x,
   // Worst-case number of active experts; workgroups past n_active exit.
   const int max_slots = (int)((T * L->k < L->E) ? T * L->k : L->E);
   uint16_t* h = (uint16_t*)ws;  // bf16 [T*k][I], sorted order
-  // Gate/up in 32-row slices for up to 16 tokens (it redoes the weight decode
-  // per token, which costs more than it saves once experts hold many tokens).
-  hipError_t e = (T <= 16 && moe::gemv_gateup32_fits(L))
-                    ? moe::launch_gemv_gateup32(L, x, b, max_slots, h, stream)
-                    : moe::launch_gemv_gateup(L, x, b, max_slots, h, stream);
+  hipError_t e = gemv_gateup_launch(L, x, T, b, max_slots, h, stream);
   if (e == hipSuccess) e = moe::launch_gemv_down(L, h, b, max_slots, y, y_dtype, stream);
   return hip_status(W, e);
 }
@@ -461,6 +475,48 @@ moe_status moe_route_ffn(const moe_layer_desc* L, const uint16_t* x, int64_t T, 
     e = moe::launch_gemv_gate_gateup32(L, x, T, logits, topk_idx, topk_w, b, hist, decay_shift,
                                        unit_shift, max_slots, h, stream);
   if (e == hipSuccess) e = moe::launch_gemv_down(L, h, b, max_slots, y, y_dtype, stream);
+  return hip_status(W, e);
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                             const uint16_t* residual, uint16_t* out, float* logits,
+                             int32_t* topk_idx, float* topk_w, const moe_buckets* b,
+                             uint32_t* hist, int32_t decay_shift, int32_t unit_shift, void* y,
+                             int32_t y_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* W = "moe_layer_forward";
+  moe_status st = ffn_check(W, L, x, T, b, y, y_dtype);
+  if (st != MOE_OK) return st;
+  if (hist && (decay_shift < 0 || decay_shift > 31 || unit_shift < 0 || unit_shift > 31))
+    return fail(MOE_ERR_INVALID_ARG, "%s: shifts (%d, %d) must be in [0, 31]", W, decay_shift,
+                unit_shift);
+  if (T == 0) return MOE_OK;
+  CHECK_PTR(out, W); CHECK_PTR(logits, W); CHECK_PTR(topk_idx, W); CHECK_PTR(topk_w, W);
+  CHECK_PTR(ws, W); CHECK_PTR(L->w_router, W);
+  const size_t need = ffn_ws(L, T);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu", W, ws_bytes, need);
+  if (use_gemm(L, T) || T < kDownCombineMinT || T > kDownCombineMaxT) {  // the two calls
+    st = moe_route_ffn(L, x, T, logits, topk_idx, topk_w, b, hist, decay_shift, unit_shift, y,
+                       y_dtype, ws, ws_bytes, stream);
+    if (st != MOE_OK) return st;
+    return moe_combine(L, y, y_dtype, b, topk_w, T, residual, out, stream);
+  }
+  const int max_slots = (int)((T * L->k < L->E) ? T * L->k : L->E);
+  uint16_t* h = (uint16_t*)ws;  // bf16 [T*k][I], sorted order
+  hipError_t e;
+  if (moe::gemv_gate_gateup32_fits(L, T)) {
+    e = moe::launch_router(x, T, L->H, L->w_router, L->router_bias, L->E, logits, stream);
+    if (e == hipSuccess)
+      e = moe::launch_gemv_gate_gateup32(L, x, T, logits, topk_idx, topk_w, b, hist, decay_shift,
+                                         unit_shift, max_slots, h, stream);
+  } else {
+    st = moe_route_bucket(L, x, T, logits, topk_idx, topk_w, b, ws, ws_bytes, hist, decay_shift,
+                          unit_shift, stream);
+    if (st != MOE_OK) return st;
+    e = gemv_gateup_launch(L, x, T, b, max_slots, h, stream);
+  }
+  if (e == hipSuccess)
+    e = moe::launch_gemv_down_combine(L, h, T, topk_idx, b->asg_pos, topk_w, residual, out,
+                                      stream);
   return hip_status(W, e);
 }
 

@@ -224,6 +224,12 @@ hipError_t launch_gemv_gateup(const moe_layer_desc* L, const uint16_t* x, const 
                               int max_slots, uint16_t* h, hipStream_t s);
 hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const moe_buckets* b,
                             int max_slots, void* y, int y_dtype, hipStream_t s);
+// Down projection fused with the gate-weighted combine for decode batches
+// (gemv_down.hip): out bf16 [T][H] straight from h, no y.
+hipError_t launch_gemv_down_combine(const moe_layer_desc* L, const uint16_t* h, int64_t T,
+                                   const int32_t* idx, const int32_t* asg_pos,
+                                   const float* topk_w, const uint16_t* residual, uint16_t* out,
+                                   hipStream_t s);
 // Gate/up in 32-row slices (gemv_gateup32.hip), for the layers it fits; the
 // same h as launch_gemv_gateup.
 bool gemv_gateup32_fits(const moe_layer_desc* L);

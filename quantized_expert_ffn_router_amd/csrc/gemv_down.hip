@@ -474,6 +474,115 @@ hipError_t down_fmt(const moe_layer_desc* L, const uint16_t* h, const moe_bucket
   }
 }
 
+// Down projection and gate-weighted combine in one kernel, for decode
+// batches: a workgroup owns 64 rows of one token's output and has one wave
+// per expert slot j < NJ = min(k, 8) (slots j, j + 8, ... when k > 8).  A
+// wave takes its experts' 64 rows of Wd over the whole of K (the same group
+// decode and pass schedule as k_gemv_down, one token), multiplies each
+// expert's sum by its gate weight in slot order, and the waves' sums are
+// added in wave order, then the residual:
+//   out[t][n] = bf16_rne( residual[t][n] + sum_w sum_{j = w mod NJ, j < k} w_tj y_tj[n] ).
+// A fixed order, so the result does not depend on scheduling; y never goes
+// to memory.  Workgroups of one row block sit 32 or more ids apart per
+// token, on one XCD, so an expert that several tokens picked is read once
+// into that XCD's L2.
+template <int FMT, int GP, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_down_combine(
+    const uint16_t* __restrict__ h, int H, int I, int NG, Planes P0,
+    const moe_expert_ref* __restrict__ experts, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ asg_pos, const float* __restrict__ topk_w, int k, int NJ,
+    const uint16_t* __restrict__ residual, uint16_t* __restrict__ out) {
+  __shared__ float acc_s[8][64];   // a wave's running dot products of the current expert
+  __shared__ float part_s[8][64];  // the waves' gate-weighted sums
+  __shared__ uint2 tab[FMT == MOE_FMT_IQ3G ? 256 : 1];
+  __shared__ uint4 tab1[FMT == MOE_FMT_IQ1G ? 1024 : 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = blockIdx.y;
+  const int n = blockIdx.x * 64 + lane;
+  const size_t nc = (n < H) ? (size_t)n : 0;  // rows past the end read row 0, never stored
+  if constexpr (FMT == MOE_FMT_IQ3G) iq3g_table_bf16(tab, tid, 64 * NJ);
+  if constexpr (FMT == MOE_FMT_IQ1G) iq1g_table_bf16(tab1, tid, 64 * NJ);
+  if constexpr (FMT == MOE_FMT_IQ3G || FMT == MOE_FMT_IQ1G) __syncthreads();
+  float* acc = &acc_s[wave][0];
+  float part = 0.0f;
+  for (int j = wave; j < k; j += NJ) {
+    const size_t a = (size_t)t * k + j;
+    const int e = idx[a], p = asg_pos[a];
+    const float wj = topk_w[a];
+    const moe_expert_ref ref = experts[e];
+    const uintptr_t blob = (uintptr_t)ref.blob;
+    const Planes P = {(const uint8_t*)(blob + (uintptr_t)P0.a), (const uint8_t*)(blob + (uintptr_t)P0.b),
+                      (const uint8_t*)(blob + (uintptr_t)P0.c), (const uint8_t*)(blob + (uintptr_t)P0.d)};
+    const float ts = (FMT == MOE_FMT_NVFP4) ? ref.ts_down : 1.0f;
+    acc[lane] = 0.0f;
+    for (int sg = 0; sg < NG; sg += GP) {
+      Group<FMT> r[GP];
+      dn_issue<FMT, GP, D>(r, P, H, nc, sg);
+      __builtin_amdgcn_sched_barrier(0);
+      keep_scalar(touch_lines<4 * GP>(reinterpret_cast<const uint32_t*>(h + (size_t)p * I) +
+                                      64 * sg));
+      dn_consume<FMT, GP, D>(r, h, p, H, I, nc, P, ts, sg, 1, acc, tab, tab1);
+    }
+    part = fmaf(wj, acc[lane], part);
+  }
+  part_s[wave][lane] = part;
+  __syncthreads();
+  if (wave != 0 || n >= H) return;
+  float sum = part_s[0][lane];
+  for (int w = 1; w < NJ; ++w) sum += part_s[w][lane];
+  if (residual) sum = bf16_to_f32(residual[(size_t)t * H + n]) + sum;
+  out[(size_t)t * H + n] = f32_to_bf16_rne(sum);
+}
+
+template <int FMT, int GP>
+hipError_t down_combine_t(const moe_layer_desc* L, const uint16_t* h, int64_t T,
+                          const int32_t* idx, const int32_t* asg_pos, const float* topk_w,
+                          const uint16_t* residual, uint16_t* out, hipStream_t s) {
+  constexpr int D = GP < 2 ? GP : 2;
+  const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
+  Planes P;
+  if (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_Q8_0) {
+    P = {(const uint8_t*)lay.down_q, (const uint8_t*)lay.down_s, nullptr, nullptr};
+  } else if (FMT == MOE_FMT_IQ3G || FMT == MOE_FMT_IQ1G) {
+    P = {(const uint8_t*)lay.down_q, (const uint8_t*)lay.down_s, (const uint8_t*)lay.down_sc,
+         nullptr};
+  } else {
+    P = {(const uint8_t*)lay.down_ql, (const uint8_t*)lay.down_qh, (const uint8_t*)lay.down_sc,
+         (const uint8_t*)lay.down_d};
+  }
+  const int NJ = L->k < 8 ? L->k : 8;
+  dim3 grid((unsigned)((L->H + 63) / 64), (unsigned)T);
+  hipLaunchKernelGGL((k_gemv_down_combine<FMT, GP, D>), grid, dim3(64 * NJ), 0, s, h, L->H, L->I,
+                     L->I / 128, P, L->experts, idx, asg_pos, topk_w, L->k, NJ, residual, out);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t down_combine_fmt(const moe_layer_desc* L, const uint16_t* h, int64_t T,
+                            const int32_t* idx, const int32_t* asg_pos, const float* topk_w,
+                            const uint16_t* residual, uint16_t* out, hipStream_t s) {
+  // One wave runs all of K: passes of GP groups (the register budgets of
+  // k_gemv_down), the largest that divides the group count.  (Splitting K
+  // over two waves per expert, 16 waves per workgroup, measured no faster.)
+  const int NG = L->I / 128;
+  const int gp_max = (FMT == MOE_FMT_NVFP4) ? 4 : 2;
+  int GP = NG > gp_max ? gp_max : NG;
+  while (NG % GP) --GP;
+#define DC(G) down_combine_t<FMT, G>(L, h, T, idx, asg_pos, topk_w, residual, out, s)
+  if (GP == 1) return DC(1);
+  if constexpr (FMT != MOE_FMT_NVFP4) {
+    return DC(2);
+  } else {
+    switch (GP) {
+      case 2: return DC(2);
+      case 3: return DC(3);
+      default: return DC(4);
+    }
+  }
+#undef DC
+}
+
 }  // namespace
 
 hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const moe_buckets* b,
@@ -483,6 +592,19 @@ hipError_t launch_gemv_down(const moe_layer_desc* L, const uint16_t* h, const mo
   if (L->fmt_down == MOE_FMT_IQ3G) return down_fmt<MOE_FMT_IQ3G>(L, h, b, max_slots, y, y_dtype, s);
   if (L->fmt_down == MOE_FMT_IQ1G) return down_fmt<MOE_FMT_IQ1G>(L, h, b, max_slots, y, y_dtype, s);
   return down_fmt<MOE_FMT_NVFP4>(L, h, b, max_slots, y, y_dtype, s);
+}
+
+hipError_t launch_gemv_down_combine(const moe_layer_desc* L, const uint16_t* h, int64_t T,
+                                   const int32_t* idx, const int32_t* asg_pos,
+                                   const float* topk_w, const uint16_t* residual, uint16_t* out,
+                                   hipStream_t s) {
+  switch (L->fmt_down) {
+    case MOE_FMT_Q6K: return down_combine_fmt<MOE_FMT_Q6K>(L, h, T, idx, asg_pos, topk_w, residual, out, s);
+    case MOE_FMT_Q8_0: return down_combine_fmt<MOE_FMT_Q8_0>(L, h, T, idx, asg_pos, topk_w, residual, out, s);
+    case MOE_FMT_IQ3G: return down_combine_fmt<MOE_FMT_IQ3G>(L, h, T, idx, asg_pos, topk_w, residual, out, s);
+    case MOE_FMT_IQ1G: return down_combine_fmt<MOE_FMT_IQ1G>(L, h, T, idx, asg_pos, topk_w, residual, out, s);
+    default: return down_combine_fmt<MOE_FMT_NVFP4>(L, h, T, idx, asg_pos, topk_w, residual, out, s);
+  }
 }
 
 }  // namespace moe
