@@ -228,6 +228,32 @@ def test_route_ffn_checks_before_launch():
              None) == q.MOE_ERR_WORKSPACE
 
 
+def test_layer_forward_checks_before_launch():
+    """moe_layer_forward validates on the host first, like moe_route_ffn,
+    and also needs the output buffer."""
+    d = _desc()
+    lib = q.lib()
+    n = q.moe_buckets_bytes(8, 4, 2)
+    buf = np.zeros(n + 256, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    b = q.moe_buckets_carve(base, n, 8, 4, 2)
+    f = lib.moe_layer_forward
+    B = ctypes.byref(b)
+    big = 1 << 20
+    assert f(ctypes.byref(d), None, 0, None, None, None, None, None, B, None, 0, 0, None, 0,
+             None, 0, None) == q.MOE_OK
+    assert f(ctypes.byref(d), 0x10, 4, None, None, 0x20, 0x30, 0x40, B, None, 0, 0, 0x60, 0,
+             0x70, big, None) == q.MOE_ERR_INVALID_ARG
+    assert "out is NULL" in q.last_error()
+    assert f(ctypes.byref(d), 0x10, 4, None, 0x80, 0x20, 0x30, 0x40, B, 0x50, 32, 0, 0x60, 0,
+             0x70, big, None) == q.MOE_ERR_INVALID_ARG
+    assert "shifts" in q.last_error()
+    assert f(ctypes.byref(d), 0x10, 4, None, 0x80, 0x20, 0x30, 0x40, B, None, 0, 0, 0x60, 0,
+             0x70, 16, None) == q.MOE_ERR_WORKSPACE
+    assert f(ctypes.byref(d), 0x10, 5, None, 0x80, 0x20, 0x30, 0x40, B, None, 0, 0, 0x60, 0,
+             0x70, big, None) == q.MOE_ERR_WORKSPACE
+
+
 def test_library_grid_equals_oracle_grid():
     """The library builds the IQ3G grid at compile time (csrc/iq3g.h, a
     counting sort on the squared norm); compiled on the host here, its 256
