@@ -269,38 +269,9 @@ def main():
         ffn_bytes = na * expert_bytes
         ffn_gbs = float(ffn_bytes.sum() / (ffn_ms.sum() * 1e-3) / 1e9)
 
-        # (1b) the same FFN calls back to back from a HIP graph (the buckets of
-        #      the 16 (layer, input) pairs that i % N_LAYERS, i % X_POOL walk
-        #      through, made beforehand): the kernels' time per call without
-        #      the host's launch gaps between eager calls.
-        combos = 16
-        gbufs = [q.StepBuffers(layers[0], B) for _ in range(combos)]
-        with torch.cuda.stream(stream):
-            for c, gb in enumerate(gbufs):
-                d = layers[c % N_LAYERS].desc
-                q.moe_route(d, xs[c % X_POOL], B, gb.logits, gb.idx, gb.w, stream)
-                q.moe_bucket(d, gb.idx, B, gb.buckets, gb.ws, gb.ws_bytes, stream)
-        torch.cuda.synchronize()
-        na_g = np.array([gb.bucket_view(W.E, B, W.k)["n_active"] for gb in gbufs], np.float64)
-        g_reps, g_calls = 4, 8 * combos
-        ffn_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(ffn_graph, stream=stream):
-            for r in range(g_calls):
-                c = r % combos
-                q.moe_expert_ffn(layers[c % N_LAYERS].desc, xs[c % X_POOL], B, gbufs[c].buckets,
-                                 buf.y, buf.y_dtype, buf.ws, buf.ws_bytes, stream)
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            ffn_graph.replay()
-            g0.record(stream)
-            for _ in range(g_reps):
-                ffn_graph.replay()
-            g1.record(stream)
-        torch.cuda.synchronize()
-        ffn_graph_us = g0.elapsed_time(g1) * 1e3 / (g_reps * g_calls)
-        ffn_graph_gbs = float(na_g.mean() * expert_bytes / (ffn_graph_us * 1e-6) / 1e9)
-        del ffn_graph, gbufs
+        # (1b) the same FFN calls back to back from a HIP graph
+        ffn_graph_us, ffn_graph_gbs = ffn_graph_rate(q, torch, layers, xs, B, buf, stream,
+                                                     expert_bytes)
 
         # (2) whole-step throughput: exactly args.steps steps, replayed from
         # HIP graphs (one of X_POOL steps, replayed steps // X_POOL times, and
@@ -478,14 +449,53 @@ FORMAT_LAYERS = {
 }
 
 
+def ffn_graph_rate(q, torch, layers, xs, B, buf, stream, expert_bytes, combos=16, reps=4):
+    """moe_expert_ffn calls back to back, replayed from a HIP graph: the
+    buckets of the `combos` (layer, input) pairs that i % len(layers),
+    i % len(xs) walk through are made beforehand, the graph holds 8 rounds of
+    them, and HIP events bracket `reps` replays after a warm one.  Returns
+    (us per call, GB/s over the active experts' bytes): the FFN's time as a
+    graph-replayed step runs it, without the host's launch gaps between
+    eager calls."""
+    nl, nx = len(layers), len(xs)
+    L0 = layers[0]
+    gbufs = [q.StepBuffers(L0, B) for _ in range(combos)]
+    with torch.cuda.stream(stream):
+        for c, gb in enumerate(gbufs):
+            d = layers[c % nl].desc
+            q.moe_route(d, xs[c % nx], B, gb.logits, gb.idx, gb.w, stream)
+            q.moe_bucket(d, gb.idx, B, gb.buckets, gb.ws, gb.ws_bytes, stream)
+    torch.cuda.synchronize()
+    na = np.array([gb.bucket_view(L0.E, B, L0.k)["n_active"] for gb in gbufs], np.float64)
+    calls = 8 * combos
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for r in range(calls):
+            c = r % combos
+            q.moe_expert_ffn(layers[c % nl].desc, xs[c % nx], B, gbufs[c].buckets, buf.y,
+                             buf.y_dtype, buf.ws, buf.ws_bytes, stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+    del graph, gbufs
+    return us, float(na.mean() * expert_bytes / (us * 1e-6) / 1e9)
+
+
 def measure_format(args, q, moegen, torch, dev, name):
     """A layer with another down-projection format (the mixed layer: 256
     experts, top-8, hidden 2048, intermediate 512, Q6_K-style down; the Q8_0,
     IQ3G and IQ1G layers: the decode layer's shape with that down format): decode
-    batch 8 expert FFN
-    (GB/s over the active experts' bytes, four layer copies cycled so the
-    Infinity Cache cannot hold them) and the 4096-token prefill FFN (TFLOP/s),
-    HIP events on the launch stream around moe_expert_ffn."""
+    batch 8 expert FFN (GB/s over the active experts' bytes, four layer copies
+    cycled so the Infinity Cache cannot hold them; eager calls and graph
+    replays, see ffn_graph_rate) and the 4096-token prefill FFN (TFLOP/s), HIP
+    events on the launch stream around moe_expert_ffn."""
     W = moegen.WORKLOADS[name]
     n_layers = 4
     layers = [q.DeviceLayer(moegen.make_layer(W, layer=200 + l)) for l in range(n_layers)]
@@ -524,9 +534,12 @@ def measure_format(args, q, moegen, torch, dev, name):
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     na = nact.cpu().numpy().astype(np.float64)
     gbs = float((na * expert_bytes).sum() / (ms.sum() * 1e-3) / 1e9)
+    g_us, g_gbs = ffn_graph_rate(q, torch, layers, xs, B, buf, stream, expert_bytes)
     out["decode_b8"] = {"ffn_us": round(float(ms.mean() * 1e3), 3),
                         "active_experts": round(float(na.mean()), 2),
-                        "ffn_GBps": round(gbs, 1), "ffn_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+                        "ffn_GBps": round(gbs, 1), "ffn_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "ffn_graph_us": round(g_us, 3), "ffn_graph_GBps": round(g_gbs, 1),
+                        "ffn_graph_hbm_frac": round(g_gbs / HBM_PEAK_GBS, 4)}
     del buf
     return measure_format_prefill(args, q, moegen, torch, dev, W, layers[0], stream, out, 10)
 
