@@ -264,16 +264,18 @@ def test_gemm_activation_magnitudes(x_std, w_std, fmt_down):
     assert rel_l2(got, ref) <= 5e-3, rel_l2(got, ref)
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("B,keep_y", [(8, True), (1, False), (4, False), (8, False)])
+def test_graph_replay_matches_eager(B, keep_y):
     """The bench times decode steps replayed from a HIP graph: each replay of
     a captured step equals the eager step bit for bit (output, indices, gate
     weights), with eager steps on other inputs and synchronizations between
-    the replays."""
+    the replays; for the step through moe_route_ffn + moe_combine (keep_y) and
+    through moe_layer_forward (gating inside gate/up at batch 1, down and
+    combine in one kernel at batches 4 and 8)."""
     import torch
     import quantized_expert_ffn_router_amd as q
     w, L = layer("decode")
     dl = q.DeviceLayer(L)
-    B = 8
     buf = q.StepBuffers(dl, B)
     xa = torch.from_numpy(moegen.make_tokens(w, B, step=11).view(np.int16).copy()).cuda()
     xb = torch.from_numpy(moegen.make_tokens(w, B, step=12).view(np.int16).copy()).cuda()
@@ -283,16 +285,16 @@ def test_graph_replay_matches_eager():
         return (buf.out[:B].clone(), buf.idx[:B].clone(), buf.w[:B].clone())
 
     with torch.cuda.stream(s):
-        q.layer_forward(dl, buf, xa, B, stream=s, hist_shifts=None)
+        q.layer_forward(dl, buf, xa, B, stream=s, hist_shifts=None, keep_y=keep_y)
     torch.cuda.synchronize()
     ref = snap()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        q.layer_forward(dl, buf, xa, B, stream=s, hist_shifts=None)
+        q.layer_forward(dl, buf, xa, B, stream=s, hist_shifts=None, keep_y=keep_y)
     torch.cuda.synchronize()
     for rep in range(4):
         with torch.cuda.stream(s):
-            q.layer_forward(dl, buf, xb, B, stream=s, hist_shifts=None)
+            q.layer_forward(dl, buf, xb, B, stream=s, hist_shifts=None, keep_y=keep_y)
         torch.cuda.synchronize()
         other = snap()
         assert not torch.equal(other[0], ref[0])  # the buffers now hold another step
