@@ -354,7 +354,7 @@ def main():
             "weights": "nvfp4", "layers_cycled": N_LAYERS, "hip_graph": True,
         },
         "roofline": {
-            "kernel": "expert FFN (k_gemv_gateup32_nvfp4<8> + k_gemv_down<1, 2, 2, false>, NVFP4)",
+            "kernel": "expert FFN (k_gemv_gateup32_nvfp4<8, 32> + k_gemv_down<1, 2, 2, false>, NVFP4)",
             "bound": "hbm",
             "achieved": round(head["ffn_graph_GBps"], 1),
             "peak": HBM_PEAK_GBS,

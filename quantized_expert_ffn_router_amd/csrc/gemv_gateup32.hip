@@ -33,6 +33,8 @@
 // workgroup 0 also writes the gating outputs (top-k, buckets, histogram).
 // One launch fewer per layer step than gating and gate/up apart, the same
 // results bit for bit.
+#include <mutex>
+
 #include "gate_common.h"
 #include "gemv_gateup.h"
 
@@ -131,7 +133,7 @@ __device__ __forceinline__ float g32_token(const G32A<NP>& r, const uint16_t* __
   return acc;
 }
 
-template <int NP>
+template <int NP, int R>
 __global__ __launch_bounds__(kG32Threads) __attribute__((amdgpu_waves_per_eu(4))) void
 k_gemv_gateup32_nvfp4(const uint16_t* __restrict__ x, int H, int I, int ktop, int kshift, int NS,
                       int max_slots, int nparts, const moe_expert_ref* __restrict__ experts,
@@ -151,7 +153,9 @@ k_gemv_gateup32_nvfp4(const uint16_t* __restrict__ x, int H, int I, int ktop, in
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool up = lane >= 32;
-  const uint32_t n = (uint32_t)j * 32u + (uint32_t)(lane & 31);  // row of the slice
+  // row of the slice (R rows: lanes past R in each half repeat row R - 1's
+  // loads, in bounds, and their sums are never stored)
+  const uint32_t n = (uint32_t)j * (uint32_t)R + (uint32_t)min(lane & 31, R - 1);
   const uint8_t* blob = (const uint8_t*)ref.blob;  // wave-uniform
   const uint32_t aq = (uint32_t)(up ? off_uq : off_gq) + n * 16u;
   const uint32_t as = (uint32_t)(up ? off_us : off_gs) + n * 8u;
@@ -197,12 +201,13 @@ k_gemv_gateup32_nvfp4(const uint16_t* __restrict__ x, int H, int I, int ktop, in
     __syncthreads();
     for (int o = tid; o < mt * 32; o += kG32Threads) {
       const int t = o >> 5, r = o & 31;
+      if (r >= R) continue;
       float g = 0.0f, u = 0.0f;
       for (int w = 0; w < nparts; ++w) {
         g += red[w][t][r];
         u += red[w][t][32 + r];
       }
-      hout[(size_t)(base + c0 + t) * I + j * 32 + r] =
+      hout[(size_t)(base + c0 + t) * I + j * R + r] =
           f32_to_bf16_rne(swiglu(g * ref.ts_gate, u * ref.ts_up));
     }
     c0 += kGuMT;
@@ -212,7 +217,7 @@ k_gemv_gateup32_nvfp4(const uint16_t* __restrict__ x, int H, int I, int ktop, in
 // The gating of the batch (all T tokens) by every workgroup, then its slice
 // of gate/up as in k_gemv_gateup32_nvfp4 (T <= kGateGemvMaxT: one pass of
 // tokens).
-template <int NP, int NV>
+template <int NP, int NV, int R>
 __global__ __launch_bounds__(kG32Threads) __attribute__((amdgpu_waves_per_eu(4))) void
 k_gemv_gate_gateup32(const uint16_t* __restrict__ x, int H, int I, int ktop, int NS,
                      int max_slots, int nparts, const moe_expert_ref* __restrict__ experts,
@@ -232,7 +237,8 @@ k_gemv_gate_gateup32(const uint16_t* __restrict__ x, int H, int I, int ktop, int
   const moe_expert_ref ref = experts[e];
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool up = lane >= 32;
-  const uint32_t n = (uint32_t)j * 32u + (uint32_t)(lane & 31);  // row of the slice
+  // row of the slice (as in k_gemv_gateup32_nvfp4)
+  const uint32_t n = (uint32_t)j * (uint32_t)R + (uint32_t)min(lane & 31, R - 1);
   const uint8_t* blob = (const uint8_t*)ref.blob;  // wave-uniform
   const uint32_t aq = (uint32_t)(up ? off_uq : off_gq) + n * 16u;
   const uint32_t as = (uint32_t)(up ? off_us : off_gs) + n * 8u;
@@ -264,14 +270,48 @@ k_gemv_gate_gateup32(const uint16_t* __restrict__ x, int H, int I, int ktop, int
   __syncthreads();
   for (int o = tid; o < cnt * 32; o += kG32Threads) {
     const int t = o >> 5, r = o & 31;
+    if (r >= R) continue;
     float g = 0.0f, u = 0.0f;
     for (int w = 0; w < nparts; ++w) {
       g += red[w][t][r];
       u += red[w][t][32 + r];
     }
-    hout[(size_t)(base + t) * I + j * 32 + r] =
+    hout[(size_t)(base + t) * I + j * R + r] =
         f32_to_bf16_rne(swiglu(g * ref.ts_gate, u * ref.ts_up));
   }
+}
+
+}  // namespace
+
+namespace {
+
+// CUs of the current device, looked up once per device (0 if unknown).
+constexpr int kG32MaxDevices = 64;
+std::once_flag g_g32_cu_once[kG32MaxDevices];
+int g_g32_cus[kG32MaxDevices];
+
+int g32_device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kG32MaxDevices) return 0;
+  std::call_once(g_g32_cu_once[dev], [dev] {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 0;
+    g_g32_cus[dev] = c;
+  });
+  return g_g32_cus[dev];
+}
+
+// Rows per slice: 32, or 24 when the 32-row grid would give the CUs at most
+// 1.5 workgroups each (decode batches of 1 and 2 tokens at I = 768: 192 and
+// 384 workgroups on 256 CUs) and I splits into groups of 4 such slices.  A
+// workgroup then carries 3/4 of the bytes, the busiest CU pulls fewer of
+// them (batch 1: 256 workgroups of 55 KB instead of 192 of 74 KB), and the
+// idle lanes (8 of each 32) cost nothing that is not already waiting on
+// memory at these batch sizes.
+int g32_rows(const moe_layer_desc* L, int max_slots) {
+  if (L->I % 96 != 0) return 32;
+  const int cus = g32_device_cus();
+  return (cus > 0 && 2 * (int64_t)max_slots * (L->I / 32) <= 3 * (int64_t)cus) ? 24 : 32;
 }
 
 }  // namespace
@@ -287,7 +327,8 @@ bool gemv_gateup32_fits(const moe_layer_desc* L) {
 hipError_t launch_gemv_gateup32(const moe_layer_desc* L, const uint16_t* x, const moe_buckets* b,
                                 int max_slots, uint16_t* h, hipStream_t s) {
   const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
-  const int NS = L->I / 32;
+  const int R = g32_rows(L, max_slots);
+  const int NS = L->I / R;
   // K parts: one per wave (H/32 granules over at most 8 waves), NP <= 8 each
   const int ngran = L->H / 32;
   const int nparts = ngran < kG32Waves ? ngran : kG32Waves;
@@ -298,11 +339,16 @@ hipError_t launch_gemv_gateup32(const moe_layer_desc* L, const uint16_t* x, cons
   // 4-slice groups: max_slots * NS / 4 of them, 8 XCD lanes x 4 slices each
   const int groups = max_slots * (NS / 4);
   const unsigned nblocks = (unsigned)(((groups + 7) / 8) * 32);
-#define G32(P)                                                                                  \
-  hipLaunchKernelGGL(k_gemv_gateup32_nvfp4<P>, dim3(nblocks), dim3(kG32Threads), 0, s, x, L->H, \
-                     L->I, L->k, kshift, NS, max_slots, nparts, L->experts, lay.gate_q,         \
+#define G32R(P, RR)                                                                            \
+  hipLaunchKernelGGL((k_gemv_gateup32_nvfp4<P, RR>), dim3(nblocks), dim3(kG32Threads), 0, s, x, \
+                     L->H, L->I, L->k, kshift, NS, max_slots, nparts, L->experts, lay.gate_q,   \
                      lay.gate_s, lay.up_q, lay.up_s, b->counts, b->offsets, b->sorted_asg,      \
                      b->active, b->n_active, h)
+#define G32(P)        \
+  if (R == 24)        \
+    G32R(P, 24);      \
+  else                \
+    G32R(P, 32)
   switch (NP) {
     case 1: G32(1); break;
     case 2: G32(2); break;
@@ -314,6 +360,7 @@ hipError_t launch_gemv_gateup32(const moe_layer_desc* L, const uint16_t* x, cons
     default: G32(8); break;
   }
 #undef G32
+#undef G32R
   return hipGetLastError();
 }
 
@@ -332,7 +379,8 @@ hipError_t launch_gemv_gate_gateup32(const moe_layer_desc* L, const uint16_t* x,
                                      const moe_buckets* b, uint32_t* hist, int ds, int us,
                                      int max_slots, uint16_t* h, hipStream_t s) {
   const BlobLayout lay = blob_layout(L->H, L->I, L->fmt_down);
-  const int NS = L->I / 32;
+  const int R = g32_rows(L, max_slots);
+  const int NS = L->I / R;
   const int ngran = L->H / 32;
   const int nparts = ngran < kG32Waves ? ngran : kG32Waves;
   const int NP = ngran / nparts;
@@ -340,10 +388,15 @@ hipError_t launch_gemv_gate_gateup32(const moe_layer_desc* L, const uint16_t* x,
   const unsigned nblocks = (unsigned)(((groups + 7) / 8) * 32);
   const GateOut out = {idx, w, b->counts, b->offsets, b->active, b->n_active, b->sorted_asg,
                        b->asg_pos, hist, ds, us};
-#define GG(P, V)                                                                                \
-  hipLaunchKernelGGL((k_gemv_gate_gateup32<P, V>), dim3(nblocks), dim3(kG32Threads), 0, s, x,   \
-                     L->H, L->I, L->k, NS, max_slots, nparts, L->experts, lay.gate_q, lay.gate_s, \
-                     lay.up_q, lay.up_s, logits, (int)T, L->E, L->renormalize, out, h)
+#define GGR(P, V, RR)                                                                           \
+  hipLaunchKernelGGL((k_gemv_gate_gateup32<P, V, RR>), dim3(nblocks), dim3(kG32Threads), 0, s,  \
+                     x, L->H, L->I, L->k, NS, max_slots, nparts, L->experts, lay.gate_q,        \
+                     lay.gate_s, lay.up_q, lay.up_s, logits, (int)T, L->E, L->renormalize, out, h)
+#define GG(P, V)         \
+  if (R == 24)           \
+    GGR(P, V, 24);       \
+  else                   \
+    GGR(P, V, 32)
 #define GG_NP(V)                 \
   switch (NP) {                  \
     case 1: GG(1, V); break;     \
@@ -364,6 +417,7 @@ hipError_t launch_gemv_gate_gateup32(const moe_layer_desc* L, const uint16_t* x,
   }
 #undef GG_NP
 #undef GG
+#undef GGR
   return hipGetLastError();
 }
 

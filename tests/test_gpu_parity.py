@@ -45,6 +45,32 @@ def test_decode_layer_parity(B):
     check_layer(L, x)
 
 
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_decode_gate_up_in_24_row_slices(B):
+    """Small decode batches whose 32-row gate/up grid would give the CUs at
+    most 1.5 workgroups each run gate/up in 24-row slices when I is a multiple
+    of 96: here I = 384 (16 slices of 24 rows), H = 1024 (4 granules per
+    lane), 48 experts, top-6, with a residual.  The decode layer (I = 768) at
+    batches 1 and 2 takes the same path in test_decode_layer_parity."""
+    import torch
+    import quantized_expert_ffn_router_amd as q
+    w, L = layer("rows24", E=48, k=6, H=1024, I=384, T=B)
+    x = moegen.make_tokens(w, B, step=B)
+    print("rows24 B", B, flush=True)
+    check_layer(L, x, residual=moegen.make_residual(w, B))
+    # the gate/up kernel that also gates (moe_route_ffn) and the plain one
+    # (moe_expert_ffn after moe_route and moe_bucket) give the same y
+    dl = q.DeviceLayer(L)
+    xd = torch.from_numpy(x.view(np.int16).copy()).cuda()
+    ys = []
+    for fused in (True, False):
+        buf = q.StepBuffers(dl, B, 0)
+        q.layer_forward(dl, buf, xd, B, None, fused_gating=fused)
+        torch.cuda.synchronize()
+        ys.append(buf.y[:B * L.k].float().cpu().numpy())
+    assert np.array_equal(ys[0], ys[1])
+
+
 def test_ragged_mid_layer_parity():
     # 37 tokens (ragged), 3 K-groups of 128 in the down projection over 2 waves
     w, L = layer("mid", E=32, k=4, H=512, I=384, T=37)
