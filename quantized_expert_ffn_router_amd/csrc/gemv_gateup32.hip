@@ -1,12 +1,14 @@
 // gemv_gateup32.hip -- decode-size gate/up projections of the routed experts
-// in 32-row slices, all of a workgroup's weight loads issued when it starts.
+// in 32-row (or, for the smallest batches, 24-row) slices, all of a
+// workgroup's weight loads issued when it starts.
 //
-// A workgroup (8 waves) owns one active expert and one slice of 32
-// consecutive rows of its intermediate dimension (slice j: rows 32j..32j+31),
-// and computes h = silu(g * ts_g) * (u * ts_u) for those rows and the
-// expert's tokens:
+// A workgroup (8 waves) owns one active expert and one slice of R = 32 (or
+// 24, see g32_rows) consecutive rows of its intermediate dimension (slice j:
+// rows Rj..Rj+R-1), and computes h = silu(g * ts_g) * (u * ts_u) for those
+// rows and the expert's tokens:
 //   - in every wave lanes 0..31 are the gate rows and lanes 32..63 the same
-//     up rows, and wave w takes K granules (32 elements) w, w + 8, w + 16,
+//     up rows (with R = 24, lanes 24..31 and 56..63 repeat the last row and
+//     are not stored), and wave w takes K granules (32 elements) w, w + 8, w + 16,
 //     ...: all lanes of a wave use the same activations, which are read with
 //     wave-uniform addresses (scalar loads, SGPR operands of v_dot2);
 //   - each lane's granules (8 of 16 bytes for H = 2048, with their E4M3 scale
